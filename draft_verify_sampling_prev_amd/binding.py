@@ -1,0 +1,232 @@
+"""ctypes binding of libdspark (C ABI declared in include/dspark.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs and the workspace are allocated with torch, and raw
+device pointers plus torch's current HIP stream are passed to the library.
+Every step of the path runs in the library's kernels; there is no CPU
+fallback, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+DSPARK_F32 = 0
+DSPARK_BF16 = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libdspark.so")
+
+# Kernel ids for dspark_profile_query.
+KERNELS = ("draft_tiles", "draft_locate", "schedule", "target_partials", "accept", "resid_tiles",
+           "bonus_partials", "final")
+
+
+class DsparkError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def load_library():
+    """Load libdspark.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise DsparkError(f"{_LIB_PATH} is missing: build it with draft_verify_sampling_prev_amd.build.build() "
+                          "(or __graft_entry__.build())")
+    L = ctypes.CDLL(_LIB_PATH)
+    L.dspark_version.restype = ctypes.c_char_p
+    L.dspark_version.argtypes = []
+    L.dspark_last_error.restype = ctypes.c_char_p
+    L.dspark_last_error.argtypes = []
+    L.dspark_workspace_size.restype = ctypes.c_size_t
+    L.dspark_workspace_size.argtypes = [_I, _I, _I, _I]
+    L.dspark_markov_draft.restype = _I
+    L.dspark_markov_draft.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P,
+                                      ctypes.c_size_t, _P]
+    L.dspark_schedule.restype = _I
+    L.dspark_schedule.argtypes = [_P, _P, _I, _I, ctypes.c_int64, _P, _P, _P]
+    L.dspark_verify.restype = _I
+    L.dspark_verify.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P,
+                                _P, _P, ctypes.c_size_t, _P]
+    L.dspark_profile_start.restype = _I
+    L.dspark_profile_start.argtypes = [_I, ctypes.c_uint]
+    L.dspark_profile_stop.restype = _I
+    L.dspark_profile_stop.argtypes = []
+    L.dspark_profile_query.restype = _I
+    L.dspark_profile_query.argtypes = [_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    _lib = L
+    return L
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().dspark_last_error().decode()
+        raise DsparkError(f"{what} failed ({rc}): {msg}")
+
+
+def dspark_version() -> str:
+    return load_library().dspark_version().decode()
+
+
+def dspark_workspace_size(B: int, gamma: int, V: int, r: int) -> int:
+    return int(load_library().dspark_workspace_size(B, gamma, V, r))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSPARK_BF16
+    if t.dtype == torch.float32:
+        return DSPARK_F32
+    raise DsparkError(f"unsupported logits dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, device, dtype=None, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise DsparkError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise DsparkError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise DsparkError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise DsparkError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise DsparkError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise DsparkError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace(B: int, gamma: int, V: int, r: int, device) -> torch.Tensor:
+    n = dspark_workspace_size(B, gamma, V, r)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def dspark_markov_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor, seed: int,
+                        ws: Optional[torch.Tensor] = None, out: Optional[Tuple] = None,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Draft gamma tokens per request.  Returns (draft_tok int32 [B][g], draft_p f32 [B][g], draft_lse f64 [B][g])."""
+    dev = L.device
+    _dev(L, "L", None)
+    B, gamma, V = L.shape
+    r = A.shape[1]
+    _dev(A, "A", dev, L.dtype, (V, r))
+    _dev(Bm, "Bm", dev, L.dtype, (r, V))
+    _dev(x0, "x0", dev, torch.int32, (B,))
+    if out is None:
+        tok = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+        p = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, gamma), dtype=torch.float64, device=dev)
+    else:
+        tok, p, lse = out
+    if ws is None:
+        ws = workspace(B, gamma, V, r, dev)
+    rc = load_library().dspark_markov_draft(_dtype_code(L), _ptr(L), _ptr(A), _ptr(Bm), _ptr(x0), B, gamma, V, r,
+                                            ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(tok), _ptr(p),
+                                            _ptr(lse), _ptr(ws), ws.numel(), _stream(dev, stream))
+    _check(rc, "dspark_markov_draft")
+    return tok, p, lse
+
+
+def dspark_schedule(z: Optional[torch.Tensor], temps: Optional[torch.Tensor], budget: int,
+                    survival: Optional[torch.Tensor] = None, out_len: Optional[torch.Tensor] = None,
+                    B: Optional[int] = None, gamma: Optional[int] = None,
+                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Survival product and budget selection.  With z=None, `survival` is the input Theta.
+    Returns (survival f32 [B][g], verify_len int32 [B])."""
+    ref = z if z is not None else survival
+    if ref is None:
+        raise DsparkError("either z or survival must be given")
+    dev = ref.device
+    if B is None or gamma is None:
+        B, gamma = ref.shape
+    if z is not None:
+        _dev(z, "z", dev, torch.float32, (B, gamma))
+        _dev(temps, "temps", dev, torch.float32, (gamma,))
+        if survival is None:
+            survival = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    _dev(survival, "survival", dev, torch.float32, (B, gamma))
+    if out_len is None:
+        out_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = load_library().dspark_schedule(_ptr(z), _ptr(temps), B, gamma, ctypes.c_int64(int(budget)), _ptr(survival),
+                                        _ptr(out_len), _stream(dev, stream))
+    _check(rc, "dspark_schedule")
+    return survival, out_len
+
+
+def dspark_verify(Tgt: torch.Tensor, L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor,
+                  draft_tok: torch.Tensor, draft_p: torch.Tensor, draft_lse: torch.Tensor, verify_len: torch.Tensor,
+                  seed: int, ws: Optional[torch.Tensor] = None, out: Optional[Tuple] = None, want_target_p: bool = True,
+                  stream=None):
+    """Rejection-sampling verification.
+    Returns (accepted int32 [B], out_tok int32 [B][g+1], n_out int32 [B], target_p f32 [B][g] or None)."""
+    dev = L.device
+    _dev(L, "L", None)
+    B, gamma, V = L.shape
+    r = A.shape[1]
+    _dev(Tgt, "Tgt", dev, L.dtype, (B, gamma + 1, V))
+    _dev(A, "A", dev, L.dtype, (V, r))
+    _dev(Bm, "Bm", dev, L.dtype, (r, V))
+    _dev(x0, "x0", dev, torch.int32, (B,))
+    _dev(draft_tok, "draft_tok", dev, torch.int32, (B, gamma))
+    _dev(draft_p, "draft_p", dev, torch.float32, (B, gamma))
+    _dev(draft_lse, "draft_lse", dev, torch.float64, (B, gamma))
+    _dev(verify_len, "verify_len", dev, torch.int32, (B,))
+    if out is None:
+        acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        out_tok = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+        n_out = torch.empty((B,), dtype=torch.int32, device=dev)
+        tp = torch.empty((B, gamma), dtype=torch.float32, device=dev) if want_target_p else None
+    else:
+        acc, out_tok, n_out, tp = out
+    if ws is None:
+        ws = workspace(B, gamma, V, r, dev)
+    rc = load_library().dspark_verify(_dtype_code(L), _ptr(Tgt), _ptr(L), _ptr(A), _ptr(Bm), _ptr(x0), _ptr(draft_tok),
+                                      _ptr(draft_p), _ptr(draft_lse), _ptr(verify_len), B, gamma, V, r,
+                                      ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(acc), _ptr(out_tok),
+                                      _ptr(n_out), _ptr(tp), _ptr(ws), ws.numel(), _stream(dev, stream))
+    _check(rc, "dspark_verify")
+    return acc, out_tok, n_out, tp
+
+
+# ----------------------------------------------------------------------------- timing (measurement tools)
+def profile_start(max_launches: int = 100000, kernels=KERNELS):
+    """Start timing the named kernels (default: all)."""
+    mask = 0
+    for k in kernels:
+        mask |= 1 << KERNELS.index(k)
+    _check(load_library().dspark_profile_start(max_launches, mask), "dspark_profile_start")
+
+
+def profile_stop():
+    _check(load_library().dspark_profile_stop(), "dspark_profile_stop")
+
+
+def profile_query(kernel: str):
+    """Returns (total_ms, launches) of one kernel since profile_start."""
+    kid = KERNELS.index(kernel)
+    ms = ctypes.c_double()
+    n = ctypes.c_int()
+    _check(load_library().dspark_profile_query(kid, ctypes.byref(ms), ctypes.byref(n)), "dspark_profile_query")
+    return ms.value, n.value

@@ -1,0 +1,252 @@
+// dspark_api.hip -- the C ABI of libdspark: argument validation, workspace
+// layout, launch sequencing on the caller's stream, error reporting and
+// opt-in kernel timing.  No allocation happens inside the three calls.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "dspark.h"
+#include "dspark_internal.hpp"
+
+namespace dspark {
+
+static thread_local char g_err[512] = "";
+
+static int fail(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int B, int gamma, int V)
+{
+    WsLayout l;
+    const size_t nT = (size_t)n_tiles(V), nC = (size_t)n_chunks(V);
+    const size_t Bz = (size_t)(B > 0 ? B : 0), G = (size_t)gamma;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    l.draft_m = take(Bz * nT * 4);
+    l.draft_s = take(Bz * nT * 8);
+    l.tgt_m = take(Bz * G * nC * 4);
+    l.tgt_s = take(Bz * G * nC * 8);
+    l.lse_t = take(Bz * G * 8);
+    l.resid_idx = take(Bz * 4);
+    l.resid_list = take(Bz * 4);
+    l.resid_count = take(4);
+    l.res_w = take(Bz * nT * 8);
+    l.res_p = take(Bz * nT * 8);
+    l.bon_m = take(Bz * nC * 4);
+    l.bon_s = take(Bz * nC * 8);
+    l.total = o;
+    return l;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing.
+// ---------------------------------------------------------------------------
+struct ProfState {
+    bool on = false;
+    unsigned mask = 0u;                // bit i set: time kernel i
+    int capacity = 0;
+    std::vector<hipEvent_t> pool;
+    int used = 0;
+    int open_id = -1;
+    std::vector<int> ids;              // kernel id of each recorded pair
+    std::vector<int> starts, stops;    // indices into pool
+    bool overflow = false;
+};
+static ProfState g_prof;
+
+void prof_begin(int id, hipStream_t s)
+{
+    if (!g_prof.on || !(g_prof.mask & (1u << id))) return;
+    if (g_prof.used + 2 > g_prof.capacity) {
+        g_prof.overflow = true;
+        g_prof.open_id = -1;
+        return;
+    }
+    const int e = g_prof.used++;
+    (void)hipEventRecord(g_prof.pool[e], s);
+    g_prof.open_id = id;
+    g_prof.starts.push_back(e);
+}
+
+void prof_end(int id, hipStream_t s)
+{
+    if (!g_prof.on || g_prof.open_id != id) return;
+    const int e = g_prof.used++;
+    (void)hipEventRecord(g_prof.pool[e], s);
+    g_prof.ids.push_back(id);
+    g_prof.stops.push_back(e);
+    g_prof.open_id = -1;
+}
+
+static int check_common(int B, int gamma, int V, int r)
+{
+    if (B < 0) return fail(DSPARK_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    if (gamma < 1 || gamma > kMaxGamma) return fail(DSPARK_ERR_UNSUPPORTED, "gamma must be in [1, %d] (got %d)", kMaxGamma, gamma);
+    if (V < 8 || V % 8 != 0 || V > (1 << 24))
+        return fail(DSPARK_ERR_UNSUPPORTED, "V must be a multiple of 8 in [8, 2^24] (got %d)", V);
+    if (r < 8 || r > kMaxRank || r % 8 != 0)
+        return fail(DSPARK_ERR_UNSUPPORTED, "r must be a multiple of 8 in [8, %d] (got %d)", kMaxRank, r);
+    if ((long long)B * gamma > kMaxCandidates)
+        return fail(DSPARK_ERR_UNSUPPORTED, "B*gamma must be <= %d (got %lld)", kMaxCandidates, (long long)B * gamma);
+    return DSPARK_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int hip_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(DSPARK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return DSPARK_OK;
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" {
+
+const char* dspark_version(void) { return "dspark-mi355x 0.1.0 (gfx950)"; }
+
+const char* dspark_last_error(void) { return g_err; }
+
+size_t dspark_workspace_size(int B, int gamma, int V, int r)
+{
+    (void)r;
+    if (B < 0 || gamma < 1 || V < 1) return 0;
+    return ws_layout(B, gamma, V).total;
+}
+
+int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B, int gamma,
+                        int V, int r, uint64_t seed, int32_t* draft_tok, float* draft_p, double* draft_lse, void* ws,
+                        size_t ws_bytes, void* stream)
+{
+    g_err[0] = 0;
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    int rc = check_common(B, gamma, V, r);
+    if (rc) return rc;
+    if (B == 0) return DSPARK_OK;
+    if (!L || !A || !Bm || !x0 || !draft_tok || !draft_p || !draft_lse || !ws)
+        return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(L) || !aligned16(A) || !aligned16(Bm))
+        return fail(DSPARK_ERR_INVALID_ARG, "L, A and Bm must be 16-byte aligned");
+    const WsLayout lay = ws_layout(B, gamma, V);
+    if (ws_bytes < lay.total)
+        return fail(DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, lay.total);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int k = 1; k <= gamma; ++k) {
+        hipError_t e = launch_draft_step(dtype, L, A, Bm, x0, B, gamma, V, r, k, seed, draft_tok, draft_p, draft_lse,
+                                         ws, lay, s);
+        if (e != hipSuccess) return hip_status(e, "draft launch");
+    }
+    return DSPARK_OK;
+}
+
+int dspark_schedule(const float* z, const float* temps, int B, int gamma, int64_t budget, float* survival,
+                    int32_t* verify_len, void* stream)
+{
+    g_err[0] = 0;
+    if (B < 0) return fail(DSPARK_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    if (gamma < 1 || gamma > kMaxGamma) return fail(DSPARK_ERR_UNSUPPORTED, "gamma must be in [1, %d] (got %d)", kMaxGamma, gamma);
+    if ((long long)B * gamma > kMaxCandidates)
+        return fail(DSPARK_ERR_UNSUPPORTED, "B*gamma must be <= %d", kMaxCandidates);
+    if (budget < 0) return fail(DSPARK_ERR_INVALID_ARG, "budget must be >= 0 (got %lld)", (long long)budget);
+    if (B == 0) return DSPARK_OK;
+    if (!survival || !verify_len) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    if (z && !temps) return fail(DSPARK_ERR_INVALID_ARG, "temps must be given with z");
+    const int64_t n = (int64_t)B * gamma;
+    const int64_t admit = budget < n ? budget : n;
+    return hip_status(launch_schedule(z, temps, B, gamma, admit, survival, verify_len, static_cast<hipStream_t>(stream)),
+                      "schedule launch");
+}
+
+int dspark_verify(int dtype, const void* Tgt, const void* L, const void* A, const void* Bm, const int32_t* x0,
+                  const int32_t* draft_tok, const float* draft_p, const double* draft_lse, const int32_t* verify_len,
+                  int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok, int32_t* n_out,
+                  float* target_p, void* ws, size_t ws_bytes, void* stream)
+{
+    g_err[0] = 0;
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    int rc = check_common(B, gamma, V, r);
+    if (rc) return rc;
+    if (B == 0) return DSPARK_OK;
+    if (!Tgt || !L || !A || !Bm || !x0 || !draft_tok || !draft_p || !draft_lse || !verify_len || !accepted ||
+        !out_tok || !n_out || !ws)
+        return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(Tgt) || !aligned16(L) || !aligned16(A) || !aligned16(Bm))
+        return fail(DSPARK_ERR_INVALID_ARG, "Tgt, L, A and Bm must be 16-byte aligned");
+    const WsLayout lay = ws_layout(B, gamma, V);
+    if (ws_bytes < lay.total)
+        return fail(DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, lay.total);
+    return hip_status(launch_verify(dtype, Tgt, L, A, Bm, x0, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r,
+                                    seed, accepted, out_tok, n_out, target_p, ws, lay,
+                                    static_cast<hipStream_t>(stream)),
+                      "verify launch");
+}
+
+int dspark_profile_start(int max_launches, unsigned kernel_mask)
+{
+    g_err[0] = 0;
+    if (max_launches < 1) return fail(DSPARK_ERR_INVALID_ARG, "max_launches must be >= 1");
+    g_prof.mask = kernel_mask;
+    const int need = 2 * max_launches;
+    while ((int)g_prof.pool.size() < need) {
+        hipEvent_t e;
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return hip_status(err, "hipEventCreate");
+        g_prof.pool.push_back(e);
+    }
+    g_prof.capacity = need;
+    g_prof.used = 0;
+    g_prof.open_id = -1;
+    g_prof.ids.clear();
+    g_prof.starts.clear();
+    g_prof.stops.clear();
+    g_prof.overflow = false;
+    g_prof.on = true;
+    return DSPARK_OK;
+}
+
+int dspark_profile_stop(void)
+{
+    g_prof.on = false;
+    return DSPARK_OK;
+}
+
+int dspark_profile_query(int kernel, double* total_ms, int* launches)
+{
+    g_err[0] = 0;
+    if (kernel < 0 || kernel >= K_COUNT || !total_ms || !launches)
+        return fail(DSPARK_ERR_INVALID_ARG, "bad profile query");
+    if (g_prof.overflow) return fail(DSPARK_ERR_INVALID_ARG, "profile event capacity exceeded");
+    double tot = 0.0;
+    int n = 0;
+    for (size_t i = 0; i < g_prof.ids.size(); ++i) {
+        if (g_prof.ids[i] != kernel) continue;
+        hipError_t e = hipEventSynchronize(g_prof.pool[g_prof.stops[i]]);
+        if (e != hipSuccess) return hip_status(e, "hipEventSynchronize");
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, g_prof.pool[g_prof.starts[i]], g_prof.pool[g_prof.stops[i]]);
+        if (e != hipSuccess) return hip_status(e, "hipEventElapsedTime");
+        tot += ms;
+        ++n;
+    }
+    *total_ms = tot;
+    *launches = n;
+    return DSPARK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,248 @@
+// dspark_device.hpp -- device-side building blocks shared by the gfx950 kernels:
+// element traits, 128-bit loads, Philox-4x32-10 uniforms, exponentials and
+// wavefront / workgroup reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kThreads = 256;  // every kernel except the schedule uses 4 wave64s
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLog2eD = 1.4426950408889634074;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Element traits.  Logits, A and Bm share one element type per call.
+// ---------------------------------------------------------------------------
+struct Bf16 {
+    typedef uint16_t T;            // raw bfloat16 bits
+    static constexpr int kPerVec = 8;   // elements per 16-byte vector
+    __device__ static __forceinline__ float to_f32(T h) { return __uint_as_float((uint32_t)h << 16); }
+    // element j of a 16-byte vector
+    __device__ static __forceinline__ float get(const uint4& v, int j)
+    {
+        uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+        return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+};
+
+struct F32 {
+    typedef float T;
+    static constexpr int kPerVec = 4;
+    __device__ static __forceinline__ float to_f32(T h) { return h; }
+    __device__ static __forceinline__ float get(const uint4& v, int j)
+    {
+        uint32_t w = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+        return __uint_as_float(w);
+    }
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---------------------------------------------------------------------------
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
+// 4-word S-box with multipliers 0xD2511F53 / 0xCD9E8D57 and a key advanced by
+// the Weyl increments 0x9E3779B9 / 0xBB67AE85 after each round.  Counter
+// (k, b, draw, 0), key (lo32 seed, hi32 seed); the uniform is the top 24 bits
+// of output word 0 times 2^-24.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t b, uint32_t k, uint32_t draw)
+{
+    uint32_t w0 = k, w1 = b, w2 = draw, w3 = 0u;
+    uint32_t key_lo = (uint32_t)seed, key_hi = (uint32_t)(seed >> 32);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint32_t a0 = w0, a2 = w2;
+        const uint32_t lo_a = 0xD2511F53u * a0, hi_a = __umulhi(0xD2511F53u, a0);
+        const uint32_t lo_c = 0xCD9E8D57u * a2, hi_c = __umulhi(0xCD9E8D57u, a2);
+        w0 = hi_c ^ w1 ^ key_lo;
+        w2 = hi_a ^ w3 ^ key_hi;
+        w1 = lo_c;
+        w3 = lo_a;
+        key_lo += 0x9E3779B9u;
+        key_hi += 0xBB67AE85u;
+    }
+    return (float)(w0 >> 8) * 0x1p-24f;
+}
+
+// ---------------------------------------------------------------------------
+// Exponentials.
+//   exp_fast(x): e^x = 2^(x log2 e) with the hardware base-2 exponential;
+//     used for the un-normalised softmax weights exp(x - m) inside the vocab
+//     passes, where every weight is then summed in double.
+//   exp_to_double(y): e^y for a double argument y <= ~0, with the integer part
+//     of y log2 e applied exactly by ldexp and only the fraction in [0, 1)
+//     going through the single-precision base-2 exponential, so the relative
+//     error stays at the level of one float ulp for any y.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+__device__ __forceinline__ double exp_to_double(double y)
+{
+    double t = y * kLog2eD;
+    if (!(t > -1100.0)) return 0.0;  // also maps NaN / -inf to 0
+    double n = floor(t);
+    float fr = (float)(t - n);       // in [0, 1)
+    double e = (double)__builtin_amdgcn_exp2f(fr);
+    return ldexp(e, (int)n);
+}
+
+// ---------------------------------------------------------------------------
+// Reductions.  xor-shuffles within 16-lane groups (one MFMA output row group)
+// and within the 64-lane wavefront.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float max16(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 1, 16));
+    v = fmaxf(v, __shfl_xor(v, 2, 16));
+    v = fmaxf(v, __shfl_xor(v, 4, 16));
+    v = fmaxf(v, __shfl_xor(v, 8, 16));
+    return v;
+}
+
+__device__ __forceinline__ double sum16(double v)
+{
+    v += __shfl_xor(v, 1, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 8, 16);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_int(int v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Inclusive scan across the 64 lanes (fixed order, deterministic).
+__device__ __forceinline__ double wave_incl_scan(double v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        double n = __shfl_up(v, o, 64);
+        if (lane >= o) v += n;
+    }
+    return v;
+}
+
+// Workgroup (256 threads) reductions through a small LDS scratch.
+struct BlockScratch {
+    float f[kThreads / 64];
+    double d[kThreads / 64];
+    int i[kThreads / 64];
+};
+
+__device__ __forceinline__ float block_max(float v, BlockScratch& s)
+{
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s.f[w] = v;
+    __syncthreads();
+    float r = s.f[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, s.f[i]);
+    return r;
+}
+
+// Sum in a fixed order: lanes by xor tree, then waves 0..3 in order.
+__device__ __forceinline__ double block_sum(double v, BlockScratch& s)
+{
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s.d[w] = v;
+    __syncthreads();
+    double r = s.d[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r += s.d[i];
+    return r;
+}
+
+__device__ __forceinline__ int block_min_int(int v, BlockScratch& s)
+{
+    v = wave_min_int(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s.i[w] = v;
+    __syncthreads();
+    int r = s.i[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r = min(r, s.i[i]);
+    return r;
+}
+
+__device__ __forceinline__ int block_max_int(int v, BlockScratch& s)
+{
+    v = wave_max_int(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s.i[w] = v;
+    __syncthreads();
+    int r = s.i[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r = max(r, s.i[i]);
+    return r;
+}
+
+// Exclusive scan of one double per thread over the workgroup, in thread order.
+// Returns the exclusive prefix; *total receives the sum of all threads.
+__device__ __forceinline__ double block_excl_scan(double v, BlockScratch& s, double* total)
+{
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    double inc = wave_incl_scan(v);
+    double exc = __shfl_up(inc, 1, 64);
+    if (lane == 0) exc = 0.0;
+    __syncthreads();
+    if (lane == 63) s.d[w] = inc;
+    __syncthreads();
+    double off = 0.0;
+    for (int i = 0; i < w; ++i) off += s.d[i];
+    double tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) tot += s.d[i];
+    *total = tot;
+    return off + exc;
+}
+
+// Map a linear workgroup id to a logical id so that workgroups that run on
+// the same XCD (hardware dispatches ids round-robin over the 8 XCDs) receive
+// consecutive logical ids.  Ids past the last multiple of 8 keep their value.
+__device__ __forceinline__ int xcd_logical_id(int id, int count)
+{
+    const int full = (count / 8) * 8;
+    if (id >= full) return id;
+    return (id % 8) * (count / 8) + id / 8;
+}
+
+}  // namespace dspark

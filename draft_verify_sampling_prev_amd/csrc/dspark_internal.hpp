@@ -1,0 +1,63 @@
+// dspark_internal.hpp -- host-side pieces shared by the C-ABI layer and the
+// kernel launchers: workspace layout, launcher declarations, kernel timing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+constexpr int kMaxGamma = 16;
+constexpr int kMaxRank = 256;
+constexpr int kMaxCandidates = 16384;  // B * gamma handled by the one-workgroup selection
+constexpr int kChunkElems = 8192;       // vocabulary elements per workgroup in the row passes
+constexpr int kVocabTile = 128;         // vocabulary columns per Markov tile
+
+inline int n_tiles(int V) { return (V + kVocabTile - 1) / kVocabTile; }
+inline int n_chunks(int V) { return (V + kChunkElems - 1) / kChunkElems; }
+
+// Byte offsets into the caller's workspace (each 256-byte aligned).
+struct WsLayout {
+    size_t draft_m, draft_s;      // [B][nT] f32 / f64 : draft tile max and sum of exp
+    size_t tgt_m, tgt_s;          // [B*gamma][nC] f32 / f64 : target chunk max and sum of exp
+    size_t lse_t;                 // [B][gamma] f64 : target log-normalisers of verified rows
+    size_t resid_idx;             // [B] i32 : compact residual index of request b, or -1
+    size_t resid_list;            // [B] i32 : requests with a rejection, ascending
+    size_t resid_count;           // [1] i32
+    size_t res_w, res_p;          // [B][nT] f64 : per tile sum of max(0, p_t - p_d) and of p_t
+    size_t bon_m, bon_s;          // [B][nC] f32 / f64 : bonus-row chunk max and sum of exp
+    size_t total;
+};
+
+WsLayout ws_layout(int B, int gamma, int V);
+
+// Kernel timing (opt-in, host-side hipEvents around launches; not thread-safe).
+enum KernelId {
+    K_DRAFT_TILES = 0,
+    K_DRAFT_LOCATE,
+    K_SCHEDULE,
+    K_TARGET_PARTIALS,
+    K_ACCEPT,
+    K_RESID_TILES,
+    K_BONUS_PARTIALS,
+    K_FINAL,
+    K_COUNT
+};
+void prof_begin(int id, hipStream_t s);
+void prof_end(int id, hipStream_t s);
+
+// Launchers (return hipGetLastError()).
+hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0,
+                             int B, int gamma, int V, int r, int k, uint64_t seed, int32_t* tok, float* p,
+                             double* lse, void* ws, const WsLayout& lay, hipStream_t s);
+
+hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,
+                           int32_t* len, hipStream_t s);
+
+hipError_t launch_verify(int dtype, const void* Tg, const void* L, const void* A, const void* Bm, const int32_t* x0,
+                         const int32_t* tok, const float* pd, const double* lse_d, const int32_t* len, int B,
+                         int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok,
+                         int32_t* n_out, float* target_p, void* ws, const WsLayout& lay, hipStream_t s);
+
+}  // namespace dspark

@@ -1,0 +1,157 @@
+"""Teacher-forced parity checks of the GPU path against the oracle.
+
+Test infrastructure only (used by ``tests/``, ``__graft_entry__.smoke()``).
+Inputs are host numpy arrays: the synthetic inputs (widened to float32) and
+the GPU path's outputs copied back.  Every GPU decision is recomputed by the
+oracle from the GPU's own previous decisions (its previous draft token, its
+verify lengths, its accepted count), so one near-boundary flip does not
+cascade.  A disagreement is an *allowed flip* only when the oracle's own
+uniform lies within ``FLIP_TOL`` of the decision boundary:
+  accept test  |u - ratio| < 1e-5;
+  sampling     the GPU token y differs from the oracle's x and the oracle's
+               CDF boundary between them is within 1e-5 of u (in units of
+               the total mass).
+Anything else is a hard failure.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Iterable, List, Optional, Tuple
+
+import numpy as np
+
+from . import accept_scan, draft_row, final_token, select, survival, uniform
+
+FLIP_TOL = 1e-5
+P_RTOL = 1e-5       # probabilities, relative
+LSE_ATOL = 1e-5     # log-normalisers, absolute
+THETA_RTOL = 1e-5   # survivals, relative
+
+
+@dataclasses.dataclass
+class Report:
+    checked: int = 0
+    draft_flips: int = 0
+    accept_flips: int = 0
+    final_flips: int = 0
+    failures: List[str] = dataclasses.field(default_factory=list)
+
+    def fail(self, msg: str):
+        if len(self.failures) < 50:
+            self.failures.append(msg)
+
+    def ok(self) -> bool:
+        return not self.failures
+
+    def summary(self) -> str:
+        return (f"checked={self.checked} draft_flips={self.draft_flips} accept_flips={self.accept_flips} "
+                f"final_flips={self.final_flips} failures={len(self.failures)}"
+                + ("" if self.ok() else "\n  " + "\n  ".join(self.failures[:10])))
+
+
+def _sample_flip_allowed(o_tok: int, y: int, o: dict) -> bool:
+    """o: oracle row result queried at token y (cdf_before = C_{y-1}/S, cdf_through = C_y/S)."""
+    u = o["u"]
+    if y > o_tok:
+        return o["cdf_before"] - u < FLIP_TOL
+    return u - o["cdf_through"] < FLIP_TOL
+
+
+def check_draft(L, A, Bm, x0, seed, tok, p, lse, rep: Report, rows: Optional[Iterable[Tuple[int, int]]] = None):
+    """L [B][g][V] f32, tok/p/lse GPU outputs [B][g].  rows: (b, k) pairs with k 1-based; default all."""
+    B, gamma, V = L.shape
+    if rows is None:
+        rows = [(b, k) for b in range(B) for k in range(1, gamma + 1)]
+    for b, k in rows:
+        prev = int(x0[b]) if k == 1 else int(tok[b, k - 2])
+        y = int(tok[b, k - 1])
+        if not (0 <= y < V):
+            rep.fail(f"draft b={b} k={k}: token {y} out of range")
+            continue
+        u = uniform(seed, b, k, 0)
+        o = draft_row(L[b, k - 1], A, Bm, prev, u, query=y)
+        rep.checked += 1
+        if o["tok"] != y:
+            if _sample_flip_allowed(o["tok"], y, o):
+                rep.draft_flips += 1
+                continue
+            rep.fail(f"draft b={b} k={k}: gpu token {y} oracle {o['tok']} (u={u:.8f}, "
+                     f"C_before={o['cdf_before']:.8f}, C_through={o['cdf_through']:.8f})")
+            continue
+        if abs(float(p[b, k - 1]) - o["p"]) > P_RTOL * o["p"]:
+            rep.fail(f"draft b={b} k={k}: p_d gpu {float(p[b, k - 1]):.9g} oracle {o['p']:.9g}")
+        if abs(float(lse[b, k - 1]) - o["lse"]) > LSE_ATOL:
+            rep.fail(f"draft b={b} k={k}: lse gpu {float(lse[b, k - 1]):.9g} oracle {o['lse']:.9g}")
+
+
+def check_survival(z, temps, theta_gpu, rep: Report):
+    ref = survival(z, temps).astype(np.float64)
+    g = theta_gpu.astype(np.float64)
+    bad = np.abs(g - ref) > THETA_RTOL * np.abs(ref) + 1e-38
+    rep.checked += ref.size
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        rep.fail(f"survival mismatch at {tuple(i)}: gpu {g[tuple(i)]:.9g} oracle {ref[tuple(i)]:.9g}")
+
+
+def check_select(theta_gpu, budget, len_gpu, rep: Report):
+    """Bit-exact verify lengths given the GPU's own survivals."""
+    ref = select(theta_gpu, budget)
+    rep.checked += ref.size
+    if not np.array_equal(ref, len_gpu.astype(np.int32)):
+        i = int(np.argmax(ref != len_gpu))
+        rep.fail(f"verify length mismatch at b={i}: gpu {int(len_gpu[i])} oracle {int(ref[i])}")
+
+
+def check_verify(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_out, target_p, rep: Report,
+                 requests: Optional[Iterable[int]] = None):
+    """Teacher-forced on the GPU's draft outputs, verify lengths and accepted counts."""
+    B, gamma, V = L.shape
+    if requests is None:
+        requests = range(B)
+    for b in requests:
+        b = int(b)
+        l = int(ell[b])
+        a_g = int(acc[b])
+        rep.checked += 1
+        if not (0 <= a_g <= l):
+            rep.fail(f"verify b={b}: accepted {a_g} outside [0, {l}]")
+            continue
+        a_o, pt, ratio, us = accept_scan(T[b], tok[b], pd[b], l, seed, b)
+        if target_p is not None:
+            for k in range(l):
+                if abs(float(target_p[b, k]) - pt[k]) > P_RTOL * pt[k] + 1e-30:
+                    rep.fail(f"verify b={b} k={k + 1}: p_t gpu {float(target_p[b, k]):.9g} oracle {pt[k]:.9g}")
+            for k in range(l, gamma):
+                if float(target_p[b, k]) != 0.0:
+                    rep.fail(f"verify b={b} k={k + 1}: p_t beyond the verify length is {float(target_p[b, k])}")
+        # GPU decisions: accept at positions < a_g, reject at a_g (if a_g < l)
+        for k in range(min(a_g + 1, l)):
+            gpu_acc = k < a_g
+            orc_acc = bool(us[k] < np.float32(ratio[k]))
+            if gpu_acc != orc_acc:
+                if abs(float(us[k]) - ratio[k]) < FLIP_TOL:
+                    rep.accept_flips += 1
+                else:
+                    rep.fail(f"verify b={b} k={k + 1}: gpu {'accept' if gpu_acc else 'reject'} but "
+                             f"u={us[k]:.8f} ratio={ratio[k]:.8f}")
+        if int(n_out[b]) != a_g + 1:
+            rep.fail(f"verify b={b}: n_out {int(n_out[b])} != accepted + 1 = {a_g + 1}")
+        for k in range(a_g):
+            if int(out_tok[b, k]) != int(tok[b, k]):
+                rep.fail(f"verify b={b}: out_tok[{k}] {int(out_tok[b, k])} != draft token {int(tok[b, k])}")
+        for k in range(a_g + 1, gamma + 1):
+            if int(out_tok[b, k]) != -1:
+                rep.fail(f"verify b={b}: out_tok[{k}] = {int(out_tok[b, k])}, expected -1")
+        y = int(out_tok[b, a_g])
+        if not (0 <= y < V):
+            rep.fail(f"verify b={b}: final token {y} out of range")
+            continue
+        o = final_token(T[b], L[b], A, Bm, int(x0[b]), tok[b], l, a_g, seed, b, query=y)
+        if o["tok"] != y:
+            if _sample_flip_allowed(o["tok"], y, o):
+                rep.final_flips += 1
+            else:
+                kind = "residual" if a_g < l else "bonus"
+                rep.fail(f"verify b={b} ({kind}, a={a_g}, l={l}): gpu token {y} oracle {o['tok']} "
+                         f"(u={o['u']:.8f}, C_before={o['cdf_before']:.8f}, C_through={o['cdf_through']:.8f})")

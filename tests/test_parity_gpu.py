@@ -1,0 +1,99 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, teacher-forced.
+
+Bit-exact: verify lengths (given the GPU's own survivals), accepted counts and
+token ids, except counted near-boundary flips (|u - boundary| < 1e-5).
+Probabilities within 1e-5 relative, log-normalisers within 1e-5, survivals
+within 1e-5 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+from draft_verify_sampling_prev_amd import synth
+from gpu_util import check_step, run_step, structural_checks
+
+pytestmark = pytest.mark.gpu
+
+# Flips are rounding-level events; at these sizes more than a handful means a bug.
+MAX_FLIPS = 3
+
+
+def _run_and_check(wl, seed=None, draft_rows=None, requests=None, data_seed=None):
+    seed = wl.philox_seed if seed is None else seed
+    inp = synth.make_inputs(wl, seed=data_seed)
+    print(f"case {wl.describe()} seed={seed:#x}", flush=True)
+    out = run_step(inp, wl.budget, seed)
+    structural_checks(out, wl.gamma)
+    rep = check_step(inp, out, wl.budget, seed, draft_rows=draft_rows, requests=requests)
+    print("  ", rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep.draft_flips + rep.accept_flips + rep.final_flips <= MAX_FLIPS
+    return out, rep
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seed", [0x0123456789ABCDEF, 7, 2**63 + 12345])
+def test_tiny_full_parity(dtype, seed):
+    _run_and_check(synth.tiny(dtype=dtype), seed=seed)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_tiles_and_rank(dtype):
+    # V = 1000 is not a multiple of the 128-column tile nor of the 8192 chunk;
+    # r = 24 is not a multiple of the 32-wide k step; B = 300 spans two
+    # 256-row blocks, the second ragged.
+    wl = synth.tiny(B=300, gamma=3, V=1000, r=24, budget=450, dtype=dtype)
+    _run_and_check(wl)
+
+
+@pytest.mark.parametrize("B,gamma,budget", [(1, 1, 1), (1, 16, 7), (3, 16, 48), (17, 2, 0), (9, 4, 10**9)])
+def test_edge_shapes_and_budgets(B, gamma, budget):
+    wl = synth.tiny(B=B, gamma=gamma, V=256, r=8, budget=budget, dtype="bf16")
+    out, _ = _run_and_check(wl)
+    if budget == 0:
+        assert np.all(out["ell"] == 0) and np.all(out["n_out"] == 1)
+    if budget >= B * gamma:
+        assert np.all(out["ell"] == gamma)
+
+
+def test_many_vocab_chunks_and_row_blocks():
+    # B = 600 -> three 256-row blocks in the Markov tiles; V = 20000 -> 3 chunks, ragged.
+    wl = synth.tiny(B=600, gamma=4, V=20000, r=64, budget=1200, dtype="bf16")
+    rows = [(b, k) for b in range(0, 600, 37) for k in (1, 2, 3, 4)]
+    _run_and_check(wl, draft_rows=rows, requests=range(0, 600, 7))
+
+
+def test_zero_markov_factors_reduce_to_plain_softmax():
+    wl = synth.tiny(B=8, gamma=3, V=4096, r=32, budget=12, dtype="bf16")
+    inp = synth.make_inputs(wl)
+    inp.A.zero_()
+    inp.Bm.zero_()
+    out = run_step(inp, wl.budget, wl.philox_seed)
+    rep = check_step(inp, out, wl.budget, wl.philox_seed)
+    assert rep.ok(), rep.summary()
+
+
+def test_headline_shape_sampled():
+    """B=256, gamma=5, V=129280, r=256, bf16, budget 768: the benchmarked configuration."""
+    wl = synth.dsv4()
+    g = np.random.default_rng(5)
+    rows = [(int(b), int(k)) for b, k in zip(g.integers(0, wl.B, 40), g.integers(1, wl.gamma + 1, 40))]
+    rows += [(0, 1), (wl.B - 1, wl.gamma)]
+    reqs = sorted(set(int(b) for b in g.integers(0, wl.B, 40)) | {0, wl.B - 1})
+    _run_and_check(wl, draft_rows=rows, requests=reqs)
+
+
+def test_qwen_shape_sampled():
+    wl = synth.qwen3_4b()
+    g = np.random.default_rng(6)
+    rows = [(int(b), int(k)) for b, k in zip(g.integers(0, wl.B, 24), g.integers(1, wl.gamma + 1, 24))]
+    _run_and_check(wl, draft_rows=rows, requests=range(0, wl.B, 3))
+
+
+def test_run_to_run_determinism():
+    wl = synth.tiny(B=64, gamma=5, V=8192, r=64, budget=200, dtype="bf16")
+    inp = synth.make_inputs(wl)
+    a = run_step(inp, wl.budget, 11)
+    b = run_step(inp, wl.budget, 11)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
