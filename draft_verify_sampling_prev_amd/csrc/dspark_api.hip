@@ -28,7 +28,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 WsLayout ws_layout(int B, int gamma, int V)
 {
     WsLayout l;
-    const size_t nT = (size_t)n_tiles(V), nC = (size_t)n_chunks(V);
+    const size_t nT = (size_t)n_tiles(1, V), nC = (size_t)n_chunks(V);  // the larger tile count
     const size_t Bz = (size_t)(B > 0 ? B : 0), G = (size_t)gamma;
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -41,6 +41,7 @@ WsLayout ws_layout(int B, int gamma, int V)
     l.tgt_m = take(Bz * G * nC * 4);
     l.tgt_s = take(Bz * G * nC * 8);
     l.lse_t = take(Bz * G * 8);
+    l.pt = take(Bz * G * 8);
     l.resid_idx = take(Bz * 4);
     l.resid_list = take(Bz * 4);
     l.resid_count = take(4);
@@ -50,6 +51,20 @@ WsLayout ws_layout(int B, int gamma, int V)
     l.bon_s = take(Bz * nC * 8);
     l.total = o;
     return l;
+}
+
+static int g_cu_count[64];
+
+int cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (g_cu_count[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        g_cu_count[dev] = n;
+    }
+    return g_cu_count[dev];
 }
 
 // ---------------------------------------------------------------------------

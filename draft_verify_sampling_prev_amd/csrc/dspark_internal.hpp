@@ -12,9 +12,10 @@ constexpr int kMaxGamma = 16;
 constexpr int kMaxRank = 256;
 constexpr int kMaxCandidates = 16384;  // B * gamma handled by the one-workgroup selection
 constexpr int kChunkElems = 8192;       // vocabulary elements per workgroup in the row passes
-constexpr int kVocabTile = 128;         // vocabulary columns per Markov tile
-
-inline int n_tiles(int V) { return (V + kVocabTile - 1) / kVocabTile; }
+// Vocabulary columns per Markov tile (the granularity of the draft and
+// residual softmax partials): 64 for bf16, 128 for fp32.
+inline int tile_cols(int dtype) { return dtype == 1 ? 64 : 128; }
+inline int n_tiles(int dtype, int V) { return (V + tile_cols(dtype) - 1) / tile_cols(dtype); }
 inline int n_chunks(int V) { return (V + kChunkElems - 1) / kChunkElems; }
 
 // Byte offsets into the caller's workspace (each 256-byte aligned).
@@ -22,6 +23,7 @@ struct WsLayout {
     size_t draft_m, draft_s;      // [B][nT] f32 / f64 : draft tile max and sum of exp
     size_t tgt_m, tgt_s;          // [B*gamma][nC] f32 / f64 : target chunk max and sum of exp
     size_t lse_t;                 // [B][gamma] f64 : target log-normalisers of verified rows
+    size_t pt;                    // [B][gamma] f64 : p_t(x_k) of verified rows
     size_t resid_idx;             // [B] i32 : compact residual index of request b, or -1
     size_t resid_list;            // [B] i32 : requests with a rejection, ascending
     size_t resid_count;           // [1] i32
@@ -44,6 +46,9 @@ enum KernelId {
     K_FINAL,
     K_COUNT
 };
+// Compute units of the current device (cached per device).
+int cu_count();
+
 void prof_begin(int id, hipStream_t s);
 void prof_end(int id, hipStream_t s);
 

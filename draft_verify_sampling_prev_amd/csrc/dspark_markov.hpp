@@ -1,23 +1,23 @@
-// dspark_markov.hpp -- the Markov-head bias contraction on MFMA.
+// dspark_markov.hpp -- the Markov-head bias contraction on MFMA, fp32 path
+// (v_mfma_f32_16x16x4_f32; the bf16 path lives in dspark_tile.hpp).
 //
 // For a set of rows m (each row names a request whose conditioning token is
 // x_m and a backbone logit row L_m), one 128-column vocabulary tile
 // [n0, n0 + 128) of
 //     f[m][n] = L_m[n] + sum_i A[x_m][i] * Bm[i][n]
-// is computed by one wavefront per 16 * MB rows with 16x16 MFMA blocks
-// (bf16: v_mfma_f32_16x16x32_bf16; fp32: v_mfma_f32_16x16x4_f32), fp32
+// is computed by one wavefront per 16 * MB rows with 16x16 MFMA blocks, fp32
 // accumulation initialised with the backbone logit.  The bias term is the
 // low-rank Markov transition of the sequential head (paperlayer.ai summary of
 // arXiv 2607.05147, section 3.1; menfem.com note, Methodology: rank-256
 // factorisation; llm-wiki.hwlabs.dev explainer, Markov-head diagram).
 //
 // Data flow: A rows are gathered straight from global memory into MFMA
-// A-operand registers (each lane reads 8 consecutive k of its row: one
-// 16-byte load for bf16).  Bm is [r][V] row-major, so its k index is the
-// strided one; it is staged through LDS in 64-row (bf16) or 32-row (fp32) chunks, transposed on the
-// way in (4 rows x 8 (bf16) or 4 (fp32) columns per thread, re-packed in registers) so that the
-// B operand is again one 16-byte LDS read per lane (two for fp32).  Two LDS buffers
-// alternate so the global loads of chunk c+1 overlap the MFMAs of chunk c.
+// A-operand registers (each lane reads 8 consecutive k of its row).  Bm is
+// [r][V] row-major, so its k index is the strided one; it is staged through
+// LDS in 32-row chunks, transposed on the way in (4 rows x 4 columns per
+// thread, re-packed in registers) so that the B operand is two 16-byte LDS
+// reads per lane.  Two LDS buffers alternate so the global loads of chunk c+1
+// overlap the MFMAs of chunk c.
 //
 // Output layout (both dtypes): acc[mb][nb][i] holds row
 //   16*mb + 4*(lane>>4) + i  and column  n0 + 16*nb + (lane&15).
@@ -35,11 +35,6 @@ constexpr int kTileN = 128;  // vocabulary columns per wave tile
 // Bm rows per LDS chunk (kChunk), LDS pitch per column in elements, bytes per buffer.
 template <class DT> struct MarkovLds;
 
-template <> struct MarkovLds<Bf16> {
-    static constexpr int kChunk = 64;
-    static constexpr int kPitch = kChunk + 8;
-    static constexpr int kBufBytes = kTileN * kPitch * 2;            // 18432
-};
 template <> struct MarkovLds<F32> {
     static constexpr int kChunk = 32;
     static constexpr int kPitch = kChunk + 4;
@@ -55,45 +50,6 @@ template <class DT> constexpr int markov_lds_bytes() { return 2 * MarkovLds<DT>:
 // so the caller can keep the loads in flight.
 // ---------------------------------------------------------------------------
 template <class DT> struct BmStage;
-
-template <> struct BmStage<Bf16> {
-    // one item per thread: 4 consecutive k rows x 8 consecutive columns
-    uint4 v[4];
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ Bm, int V, int r, int n0, int k0)
-    {
-        const int t = threadIdx.x;
-        const int kq = t >> 4, ng = t & 15;
-        const int col = n0 + 8 * ng;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = k0 + 4 * kq + i;
-            if (k < r && col < V) v[i] = ld16(Bm + (size_t)k * V + col);
-            else v[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-    __device__ __forceinline__ void store(char* buf) const
-    {
-        const int t = threadIdx.x;
-        const int kq = t >> 4, ng = t & 15;
-        uint16_t* s = reinterpret_cast<uint16_t*>(buf);
-        const uint32_t a[4] = { v[0].x, v[0].y, v[0].z, v[0].w };
-        const uint32_t b[4] = { v[1].x, v[1].y, v[1].z, v[1].w };
-        const uint32_t c[4] = { v[2].x, v[2].y, v[2].z, v[2].w };
-        const uint32_t d[4] = { v[3].x, v[3].y, v[3].z, v[3].w };
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // column 8*ng + 2w takes the low halves, 8*ng + 2w + 1 the high halves
-            uint2 lo, hi;
-            lo.x = (a[w] & 0xFFFFu) | (b[w] << 16);
-            lo.y = (c[w] & 0xFFFFu) | (d[w] << 16);
-            hi.x = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
-            hi.y = (c[w] >> 16) | (d[w] & 0xFFFF0000u);
-            const int n = 8 * ng + 2 * w;
-            *reinterpret_cast<uint2*>(s + n * MarkovLds<Bf16>::kPitch + 4 * kq) = lo;
-            *reinterpret_cast<uint2*>(s + (n + 1) * MarkovLds<Bf16>::kPitch + 4 * kq) = hi;
-        }
-    }
-};
 
 template <> struct BmStage<F32> {
     // one item per thread: 4 consecutive k rows x 4 consecutive columns
@@ -132,25 +88,6 @@ template <> struct BmStage<F32> {
 // and B use the same k assignment, so the contraction is over all 32 k.
 // ---------------------------------------------------------------------------
 template <class DT> struct Frag;
-
-template <> struct Frag<Bf16> {
-    uint4 v;
-    __device__ __forceinline__ void load_a(const uint16_t* __restrict__ arow, int k, int r)
-    {
-        v = k < r ? ld16(arow + k) : make_uint4(0u, 0u, 0u, 0u);
-    }
-    __device__ __forceinline__ void load_b(const char* buf, int n, int kk)
-    {
-        const uint16_t* s = reinterpret_cast<const uint16_t*>(buf);
-        v = *reinterpret_cast<const uint4*>(s + n * MarkovLds<Bf16>::kPitch + kk);
-    }
-    __device__ __forceinline__ static floatx4 mma(const Frag& a, const Frag& b, floatx4 c)
-    {
-        bf16x8 av = __builtin_bit_cast(bf16x8, a.v);
-        bf16x8 bv = __builtin_bit_cast(bf16x8, b.v);
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
-    }
-};
 
 template <> struct Frag<F32> {
     uint4 v0, v1;

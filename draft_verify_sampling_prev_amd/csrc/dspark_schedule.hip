@@ -90,6 +90,10 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(const float* __restr
     }
 
     // Radix select of the admit-th largest key, most significant digit first.
+    // Per pass: histogram of the current digit among keys matching the prefix
+    // so far, then threads 0..255 scan the bins from the top digit down
+    // (thread t holds digit 255 - t) and the one whose running count first
+    // reaches the remaining rank selects its digit.
     if (t == 0) {
         sh_prefix = 0u;
         sh_rem = admit;
@@ -99,23 +103,33 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(const float* __restr
         for (int i = t; i < 256; i += kSchedThreads) hist[i] = 0u;
         __syncthreads();
         const uint32_t prefix = sh_prefix;
+        const long long rem = sh_rem;
         for (int i = t; i < N; i += kSchedThreads) {
             const uint32_t key = keys[i];
             if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (t == 0) {
-            long long rem = sh_rem, above = 0;
-            int sel = 0;
-            for (int d = 255; d >= 0; --d) {
-                if (above + (long long)hist[d] >= rem) {
-                    sel = d;
-                    break;
-                }
-                above += hist[d];
+        int cnt = 0, inc = 0;
+        if (t < 256) {
+            cnt = (int)hist[255 - t];
+            inc = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int n = __shfl_up(inc, o, 64);
+                if ((t & 63) >= o) inc += n;
             }
-            sh_rem = rem - above;
-            sh_prefix = prefix | ((uint32_t)sel << shift);
+            if ((t & 63) == 63) wsum[t >> 6] = inc;
+        }
+        __syncthreads();
+        if (t < 256) {
+            int off = 0;
+            for (int i = 0; i < (t >> 6); ++i) off += wsum[i];
+            const long long upto = (long long)(off + inc);  // keys with digit >= 255 - t
+            const long long above = upto - cnt;              // keys with digit >  255 - t
+            if (above < rem && rem <= upto) {
+                sh_rem = rem - above;
+                sh_prefix = prefix | ((uint32_t)(255 - t) << shift);
+            }
         }
         mask |= 255u << shift;
         __syncthreads();

@@ -13,9 +13,9 @@
 // device, so the sequence can be captured in a HIP graph):
 //   k_row_partials (target)  grid = chunks x (B*gamma): row (b,k) with
 //                            k <= ell_b -> chunk max and sum of exp (fp64).
-//   k_accept                 one workgroup: per request combine chunk
-//                            partials -> lse_t, p_t(x_k), ratio, accept
-//                            draws; compacts the requests with a rejection.
+//   k_target_lse             one wave per row: lse_t and p_t(x_k).
+//   k_accept                 one workgroup: accept draws per request; compacts
+//                            the requests with a rejection.
 //   k_resid_tiles            Markov MFMA tiles of the rejected draft rows
 //                            fused with the target row: per tile sums of
 //                            max(0, p_t - p_d) and of p_t.
@@ -25,8 +25,13 @@
 //                            the last token, write the emitted tokens.
 #include <limits.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "dspark_internal.hpp"
+#include "dspark_locate.hpp"
 #include "dspark_markov.hpp"
+#include "dspark_tile.hpp"
 
 namespace dspark {
 
@@ -37,6 +42,31 @@ __device__ __forceinline__ int cond_token_v(const int32_t* __restrict__ x0, cons
                                             int gamma, int k, int V)
 {
     return clamp_tok((k == 1) ? x0[b] : tok[b * gamma + (k - 2)], V);
+}
+
+// A log-normaliser split into two floats, hi + lo = lse to ~2^-48 relative.
+struct SplitLse {
+    float hi, lo;
+};
+__device__ __forceinline__ SplitLse split_lse(double v)
+{
+    SplitLse s;
+    s.hi = (float)v;
+    s.lo = (float)(v - (double)s.hi);
+    return s;
+}
+
+// Residual weight of one vocabulary entry: w = max(0, p_t - p_d) with
+// p = exp((x - hi) - lo) in fp32; *pt receives p_t.  The same expression is
+// used by the residual tile pass and by the final rescan, so the weights the
+// final sample scans are exactly those summed into the tile partials.
+__device__ __forceinline__ float resid_weight(float f, float t, SplitLse d, SplitLse tg, float* pt)
+{
+    const float ptv = exp_fast((t - tg.hi) - tg.lo);
+    const float pdv = exp_fast((f - d.hi) - d.lo);
+    *pt = ptv;
+    const float w = ptv - pdv;
+    return w > 0.0f ? w : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -104,9 +134,37 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T*
     }
 }
 
-__device__ __forceinline__ double part_mass(float m, double s, float M)
+// ---------------------------------------------------------------------------
+// Target log-normaliser and p_t(x_k) of every verified row: one wave per row.
+// ---------------------------------------------------------------------------
+template <class DT>
+__global__ __launch_bounds__(kThreads) void k_target_lse(const typename DT::T* __restrict__ Tg,
+                                                         const int32_t* __restrict__ tok,
+                                                         const int32_t* __restrict__ len,
+                                                         const float* __restrict__ tgm,
+                                                         const double* __restrict__ tgs, int B, int gamma, int V,
+                                                         int nC, double* __restrict__ lse_t, double* __restrict__ pt)
 {
-    return m == -INFINITY ? 0.0 : s * exp((double)m - (double)M);
+    const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= B * gamma) return;
+    const int b = row / gamma, kk = row - b * gamma;
+    if (kk >= clamp_len(len[b], gamma)) return;
+    const float* m = tgm + (size_t)row * nC;
+    const double* s = tgs + (size_t)row * nC;
+    float M = -INFINITY;
+    for (int c = lane; c < nC; c += 64) M = fmaxf(M, m[c]);
+    M = wave_max(M);
+    double S = 0.0;
+    for (int c = lane; c < nC; c += 64) S += tile_mass(m[c], s[c], M);
+    S = wave_sum(S);
+    if (lane == 0) {
+        const double lse = (double)M + log(S);
+        lse_t[row] = lse;
+        const int x = clamp_tok(tok[row], V);
+        const double tx = (double)DT::to_f32(Tg[((size_t)b * (gamma + 1) + kk) * V + x]);
+        pt[row] = exp(tx - lse);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -114,13 +172,13 @@ __device__ __forceinline__ double part_mass(float m, double s, float M)
 // ---------------------------------------------------------------------------
 constexpr int kAcceptThreads = 1024;
 
-template <class DT>
-__global__ __launch_bounds__(kAcceptThreads) void k_accept(
-    const typename DT::T* __restrict__ Tg, const int32_t* __restrict__ tok, const float* __restrict__ pd,
-    const int32_t* __restrict__ len, const float* __restrict__ tgm, const double* __restrict__ tgs, int B, int gamma,
-    int V, int nC, uint64_t seed, double* __restrict__ lse_t, int32_t* __restrict__ accepted,
-    int32_t* __restrict__ n_out, float* __restrict__ target_p, int32_t* __restrict__ resid_idx,
-    int32_t* __restrict__ resid_list, int32_t* __restrict__ resid_count)
+__global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restrict__ pd, const int32_t* __restrict__ len,
+                                                           const double* __restrict__ pt, int B, int gamma,
+                                                           uint64_t seed, int32_t* __restrict__ accepted,
+                                                           int32_t* __restrict__ n_out, float* __restrict__ target_p,
+                                                           int32_t* __restrict__ resid_idx,
+                                                           int32_t* __restrict__ resid_list,
+                                                           int32_t* __restrict__ resid_count)
 {
     __shared__ int wsum[kAcceptThreads / 64];
     __shared__ int base;
@@ -134,25 +192,15 @@ __global__ __launch_bounds__(kAcceptThreads) void k_accept(
             const int l = clamp_len(len[b], gamma);
             int a = l;
             for (int kk = 0; kk < gamma; ++kk) {
+                const size_t row = (size_t)b * gamma + kk;
                 if (kk < l) {
-                    const size_t row = (size_t)b * gamma + kk;
-                    const float* m = tgm + row * nC;
-                    const double* s = tgs + row * nC;
-                    float M = -INFINITY;
-                    for (int c = 0; c < nC; ++c) M = fmaxf(M, m[c]);
-                    double S = 0.0;
-                    for (int c = 0; c < nC; ++c) S += part_mass(m[c], s[c], M);
-                    const double lse = (double)M + log(S);
-                    lse_t[row] = lse;
-                    const int x = clamp_tok(tok[row], V);
-                    const double tx = (double)DT::to_f32(Tg[((size_t)b * (gamma + 1) + kk) * V + x]);
-                    const double pt = exp(tx - lse);
-                    const double ratio = pt / (double)pd[row];
+                    const double ptk = pt[row];
+                    const double ratio = ptk / (double)pd[row];
                     const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)(kk + 1), 1u);
                     if (a == l && !(u < (float)ratio)) a = kk;
-                    if (target_p) target_p[row] = (float)pt;
+                    if (target_p) target_p[row] = (float)ptk;
                 } else if (target_p) {
-                    target_p[(size_t)b * gamma + kk] = 0.0f;
+                    target_p[row] = 0.0f;
                 }
             }
             accepted[b] = a;
@@ -185,20 +233,30 @@ __global__ __launch_bounds__(kAcceptThreads) void k_accept(
     if (t == 0) *resid_count = base;
 }
 
+// Row m of the compacted residual list: request b at its first rejected position ks.
+struct ResidRow {
+    int b, ks;
+};
+__device__ __forceinline__ ResidRow resid_row(const int32_t* __restrict__ resid_list,
+                                              const int32_t* __restrict__ accepted, int m)
+{
+    ResidRow r;
+    r.b = resid_list[m];
+    r.ks = accepted[r.b] + 1;
+    return r;
+}
+
 // ---------------------------------------------------------------------------
-// Residual tiles: rows are the compacted requests with a rejection; row m is
-// request b = resid_list[m] at its first rejected position ks = a_b + 1.
+// Residual tiles, fp32: one 4-wave workgroup per (tile, 256-row block).
 // ---------------------------------------------------------------------------
-template <class DT>
-__global__ __launch_bounds__(kThreads) void k_resid_tiles(
-    const typename DT::T* __restrict__ Tg, const typename DT::T* __restrict__ L, const typename DT::T* __restrict__ A,
-    const typename DT::T* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
+__global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
+    const float* __restrict__ Tg, const float* __restrict__ L, const float* __restrict__ A,
+    const float* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int gamma, int V, int r, int nT,
     int nM, double* __restrict__ rw, double* __restrict__ rp)
 {
-    typedef typename DT::T T;
-    __shared__ __attribute__((aligned(16))) char lds[markov_lds_bytes<DT>()];
+    __shared__ __attribute__((aligned(16))) char lds[markov_lds_bytes<F32>()];
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int tile = lid / nM, mblk = lid % nM;
     const int cnt = *resid_count;
@@ -208,50 +266,43 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles(
     const int mw0 = mblk * 256 + wave * 64;
     const bool compute = mw0 < cnt;
 
-    const T* arow[4];
+    const float* arow[4];
     floatx4 acc[4][8];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-        const int ra = min(mw0 + 16 * mb + (lane & 15), cnt - 1);
-        const int ba = resid_list[ra];
-        arow[mb] = A + (size_t)cond_token_v(x0, tok, ba, gamma, accepted[ba] + 1, V) * r;
+        const ResidRow ra = resid_row(resid_list, accepted, min(mw0 + 16 * mb + (lane & 15), cnt - 1));
+        arow[mb] = A + (size_t)cond_token_v(x0, tok, ra.b, gamma, ra.ks, V) * r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = mw0 + 16 * mb + 4 * (lane >> 4) + i;
-            const int bb = resid_list[min(row, cnt - 1)];
-            const int ks = accepted[bb] + 1;
-            const T* lrow = L + ((size_t)bb * gamma + (ks - 1)) * V;
+            const ResidRow rr = resid_row(resid_list, accepted, min(row, cnt - 1));
+            const float* lrow = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 const int col = n0 + 16 * nb + (lane & 15);
-                acc[mb][nb][i] = (compute && row < cnt && col < V) ? DT::to_f32(lrow[col]) : 0.0f;
+                acc[mb][nb][i] = (compute && row < cnt && col < V) ? lrow[col] : 0.0f;
             }
         }
     }
-
-    markov_tile<DT, 4>(Bm, V, r, n0, arow, compute, lds, acc);
+    markov_tile<F32, 4>(Bm, V, r, n0, arow, compute, lds, acc);
     if (!compute) return;
-
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = mw0 + 16 * mb + 4 * (lane >> 4) + i;
-            const int bb = resid_list[min(row, cnt - 1)];
-            const int ks = accepted[bb] + 1;
-            const T* trow = Tg + ((size_t)bb * (gamma + 1) + (ks - 1)) * V;
-            const double ld = lse_d[(size_t)bb * gamma + ks - 1];
-            const double lt = lse_t[(size_t)bb * gamma + ks - 1];
+            const ResidRow rr = resid_row(resid_list, accepted, min(row, cnt - 1));
+            const float* trow = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
+            const SplitLse ld = split_lse(lse_d[(size_t)rr.b * gamma + rr.ks - 1]);
+            const SplitLse lt = split_lse(lse_t[(size_t)rr.b * gamma + rr.ks - 1]);
             double sw = 0.0, sp = 0.0;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 const int col = n0 + 16 * nb + (lane & 15);
                 if (col < V) {
-                    const double pdj = exp_to_double((double)acc[mb][nb][i] - ld);
-                    const double ptj = exp_to_double((double)DT::to_f32(trow[col]) - lt);
-                    const double dj = ptj - pdj;
-                    sw += dj > 0.0 ? dj : 0.0;
-                    sp += ptj;
+                    float ptv;
+                    sw += (double)resid_weight(acc[mb][nb][i], trow[col], ld, lt, &ptv);
+                    sp += (double)ptv;
                 }
             }
             sw = sum16(sw);
@@ -265,54 +316,121 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles(
 }
 
 // ---------------------------------------------------------------------------
-// Locate within a list of n non-negative masses (given by mass(i)) the first
-// index whose running sum exceeds tau (fallback: last index with positive
-// mass).  Returns the index and the running sum before it.  All threads.
+// Residual tiles, bf16: persistent workgroups of NW waves (dspark_tile.hpp)
+// over 64-column tiles; each LDS buffer holds the Bm tile, the rejected
+// rows' draft-logit tile and their target tile, all staged by DMA.
 // ---------------------------------------------------------------------------
-template <class MassFn>
-__device__ __forceinline__ int block_locate(int n, MassFn mass, double tau, double off, BlockScratch& bs,
-                                            double* sh_cprev, double* cprev_out)
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_resid_tiles_bf16(
+    const uint16_t* __restrict__ Tg, const uint16_t* __restrict__ L, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
+    const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ accepted,
+    const int32_t* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int gamma, int V, int r, int nT,
+    int nM, int S, double* __restrict__ rw, double* __restrict__ rp)
 {
-    const int t = threadIdx.x;
-    const int per = (n + kThreads - 1) / kThreads;
-    const int i0 = min(t * per, n), i1 = min(i0 + per, n);
-    int hit = INT_MAX, lastpos = -1;
-    double c = off, cph = 0.0, cpl = 0.0;
-    for (int i = i0; i < i1; ++i) {
-        const double mi = mass(i);
-        const double cb = c;
-        c += mi;
-        if (hit == INT_MAX && c > tau) {
-            hit = i;
-            cph = cb;
+    constexpr int R = 32 * NW;
+    constexpr int kRowBytes = R * kTrowBytes;
+    constexpr int kBuf = kBmTileBytes + 2 * kRowBytes;
+    __shared__ __attribute__((aligned(1024))) char lds[2 * kBuf];
+    __shared__ SplitLse sh_lse[R][2];
+
+    const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int mblk = lid % nM, slot = lid / nM;
+    const int cnt = *resid_count;
+    const int m0 = mblk * R;
+    if (m0 >= cnt || slot >= nT) return;  // uniform
+    const int w = wave_id(), lane = threadIdx.x & 63;
+    const int mw = m0 + 32 * w;
+    const bool active = mw < cnt;
+
+    uint4 a[2][8];
+    {
+        const uint16_t* arow[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const ResidRow ra = resid_row(resid_list, accepted, min(mw + 16 * mb + (lane & 15), cnt - 1));
+            arow[mb] = A + (size_t)cond_token_v(x0, tok, ra.b, gamma, ra.ks, V) * r;
         }
-        if (mi > 0.0) {
-            lastpos = i;
-            cpl = cb;
+        load_a_frags<2>(arow, r, a);
+    }
+    int lidx[4], tidx[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const ResidRow rr = resid_row(resid_list, accepted, min(m0 + dma_row_of<NW>(t), cnt - 1));
+        lidx[t] = rr.b * gamma + rr.ks - 1;
+        tidx[t] = rr.b * (gamma + 1) + rr.ks - 1;
+    }
+    for (int i = threadIdx.x; i < R; i += 64 * NW) {
+        const int m = m0 + i;
+        SplitLse d{ 0.f, 0.f }, t{ 0.f, 0.f };
+        if (m < cnt) {
+            const ResidRow rr = resid_row(resid_list, accepted, m);
+            d = split_lse(lse_d[(size_t)rr.b * gamma + rr.ks - 1]);
+            t = split_lse(lse_t[(size_t)rr.b * gamma + rr.ks - 1]);
+        }
+        sh_lse[i][0] = d;
+        sh_lse[i][1] = t;
+    }
+    const int nks = (r + 31) / 32;
+
+    auto issue = [&](int tile, char* buf) {
+        dma_bm_tile<NW>(Bm, V, r, tile * kTcols, 32 * nks, buf);
+        dma_row_tile<NW>(L, lidx, V, tile * kTcols, buf + kBmTileBytes);
+        dma_row_tile<NW>(Tg, tidx, V, tile * kTcols, buf + kBmTileBytes + kRowBytes);
+    };
+    issue(slot, lds);
+    int it = 0;
+    for (int tile = slot; tile < nT; tile += S, ++it) {
+        wait_all_mem();
+        __syncthreads();
+        const int next = tile + S;
+        if (next < nT) issue(next, lds + ((it + 1) & 1) * kBuf);
+        if (!active) continue;
+        const char* buf = lds + (it & 1) * kBuf;
+        floatx4 acc[2][4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
+        tile_mma64<2>(a, buf, nks, acc);
+        const int n0 = tile * kTcols;
+        const int nl = lane & 15;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            floatx4 tv[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                acc[mb][nb] += row_vals(buf + kBmTileBytes, 32 * w + 16 * mb, nb);
+                tv[nb] = row_vals(buf + kBmTileBytes + kRowBytes, 32 * w + 16 * mb, nb);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int lr = 32 * w + 16 * mb + 4 * (lane >> 4) + i;
+                const SplitLse ld = sh_lse[lr][0], ltg = sh_lse[lr][1];
+                double sw = 0.0, sp = 0.0;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    if (n0 + 16 * nb + nl < V) {
+                        float ptv;
+                        sw += (double)resid_weight(acc[mb][nb][i], tv[nb][i], ld, ltg, &ptv);
+                        sp += (double)ptv;
+                    }
+                }
+                sw = sum16(sw);
+                sp = sum16(sp);
+                const int row = m0 + lr;
+                if (nl == 0 && row < cnt) {
+                    rw[(size_t)row * nT + tile] = sw;
+                    rp[(size_t)row * nT + tile] = sp;
+                }
+            }
         }
     }
-    if (t == 0) *sh_cprev = 0.0;
-    const int th = block_min_int(hit, bs);
-    const int tl = block_max_int(lastpos, bs);
-    const bool use_hit = th != INT_MAX;
-    const int idx = use_hit ? th : max(tl, 0);
-    if (use_hit ? (hit == idx) : (lastpos == idx && tl >= 0)) *sh_cprev = use_hit ? cph : cpl;
-    __syncthreads();
-    *cprev_out = *sh_cprev;
-    return idx;
 }
 
-template <class MassFn>
-__device__ __forceinline__ double block_prefix_setup(int n, MassFn mass, BlockScratch& bs, double* total)
-{
-    const int t = threadIdx.x;
-    const int per = (n + kThreads - 1) / kThreads;
-    const int i0 = min(t * per, n), i1 = min(i0 + per, n);
-    double sloc = 0.0;
-    for (int i = i0; i < i1; ++i) sloc += mass(i);
-    return block_excl_scan(sloc, bs, total);
-}
-
+// ---------------------------------------------------------------------------
+// Final token of each request.
+// ---------------------------------------------------------------------------
 template <class DT>
 __global__ __launch_bounds__(kThreads) void k_final(
     const typename DT::T* __restrict__ Tg, const typename DT::T* __restrict__ L, const typename DT::T* __restrict__ A,
@@ -323,13 +441,14 @@ __global__ __launch_bounds__(kThreads) void k_final(
     int r, int nT, int nC, uint64_t seed, int32_t* __restrict__ out_tok)
 {
     typedef typename DT::T T;
-    __shared__ __attribute__((aligned(16))) char lds[markov_lds_bytes<DT>()];
+    typedef TileTraits<DT> TT;
+    __shared__ __attribute__((aligned(1024))) char lds[TT::kLdsBytes];
     __shared__ BlockScratch bs;
     __shared__ double sh_cprev;
     __shared__ int sh_tok;
 
     const int b = blockIdx.x;
-    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int t = threadIdx.x, lane = t & 63;
     const int l = clamp_len(len[b], gamma);
     const int a = accepted[b];
 
@@ -339,63 +458,40 @@ __global__ __launch_bounds__(kThreads) void k_final(
         const int m = resid_idx[b];
         const double* w = rw + (size_t)m * nT;
         const double* p = rp + (size_t)m * nT;
-        double Sw = 0.0;
-        double off = block_prefix_setup(nT, [&](int i) { return w[i]; }, bs, &Sw);
-        const bool degen = !(Sw > 0.0);
-        const double* src = degen ? p : w;
-        double S = Sw;
-        if (degen) off = block_prefix_setup(nT, [&](int i) { return p[i]; }, bs, &S);
-        const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)ks, 2u);
-        const double tau = (double)u * S;
-        double cprev;
-        const int tstar = block_locate(nT, [&](int i) { return src[i]; }, tau, off, bs, &sh_cprev, &cprev);
-
-        const int n0 = tstar * kTileN;
-        const T* arow[1] = { A + (size_t)cond_token_v(x0, tok, b, gamma, ks, V) * r };
-        const T* lrow = L + ((size_t)b * gamma + (ks - 1)) * V;
-        const T* trow = Tg + ((size_t)b * (gamma + 1) + (ks - 1)) * V;
-        floatx4 acc[1][8];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const int col = n0 + 16 * nb + (lane & 15);
-            const float v = col < V ? DT::to_f32(lrow[col]) : 0.0f;
-            acc[0][nb] = floatx4{ v, v, v, v };
+        // Total residual mass decides between the residual and its p_t fallback.
+        double sloc = 0.0;
+        {
+            const int per = (nT + kThreads - 1) / kThreads;
+            const int i0 = min(t * per, nT), i1 = min(i0 + per, nT);
+            for (int i = i0; i < i1; ++i) sloc += w[i];
         }
-        markov_tile<DT, 1>(Bm, V, r, n0, arow, wave == 0, lds, acc);
-        if (wave == 0) {
-            const double ld = lse_d[(size_t)b * gamma + ks - 1];
-            const double lt = lse_t[(size_t)b * gamma + ks - 1];
-            const int l16 = lane & 15;
-            double carry = 0.0;
-            int jhit = -1, jlast = -1;
+        const bool degen = !(block_sum(sloc, bs) > 0.0);
+        const double* src = degen ? p : w;
+        const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)ks, 2u);
+        const Located loc = locate(nT, [&](int i) { return src[i]; }, u, bs, &sh_cprev);
+
+        const int n0 = loc.idx * TT::kCols;
+        const T* trow = Tg + ((size_t)b * (gamma + 1) + (ks - 1)) * V;
+        float f[TT::kNB];
+        row_tile_f(L + ((size_t)b * gamma + (ks - 1)) * V, A, Bm, cond_token_v(x0, tok, b, gamma, ks, V), V, r, n0,
+                   lds, f);
+        if ((t >> 6) == 0) {
+            const SplitLse ld = split_lse(lse_d[(size_t)b * gamma + ks - 1]);
+            const SplitLse lt = split_lse(lse_t[(size_t)b * gamma + ks - 1]);
+            double wv[TT::kNB];
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const int col = n0 + 16 * nb + l16;
-                double wj = 0.0;
+            for (int nb = 0; nb < TT::kNB; ++nb) {
+                const int col = n0 + 16 * nb + (lane & 15);
+                wv[nb] = 0.0;
                 if (col < V) {
-                    const double ptj = exp_to_double((double)DT::to_f32(trow[col]) - lt);
-                    if (degen) {
-                        wj = ptj;
-                    } else {
-                        const double pdj = exp_to_double((double)acc[0][nb][0] - ld);
-                        const double dj = ptj - pdj;
-                        wj = dj > 0.0 ? dj : 0.0;
-                    }
+                    float ptv;
+                    const float wr = resid_weight(f[nb], DT::to_f32(trow[col]), ld, lt, &ptv);
+                    wv[nb] = (double)(degen ? ptv : wr);
                 }
-                double v = wj;
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    const double n = __shfl_up(v, o, 16);
-                    if (l16 >= o) v += n;
-                }
-                const double cum = carry + v;
-                carry = __shfl(cum, 15, 16);
-                const uint64_t mc = __ballot(cprev + cum > tau) & 0xFFFFull;
-                const uint64_t mp = __ballot(wj > 0.0) & 0xFFFFull;
-                if (jhit < 0 && mc) jhit = 16 * nb + __builtin_ctzll(mc);
-                if (mp) jlast = 16 * nb + (63 - __builtin_clzll(mp));
             }
-            if (lane == 0) sh_tok = clamp_tok(n0 + (jhit >= 0 ? jhit : max(jlast, 0)), V);
+            double wsel;
+            const int j = scan_tile_weights<TT::kNB>(wv, 1.0, loc.cprev, loc.tau, &wsel);
+            if (lane == 0) sh_tok = clamp_tok(n0 + j, V);
         }
     } else {
         // ---- bonus token from target row l (position l + 1) ----------------
@@ -406,20 +502,15 @@ __global__ __launch_bounds__(kThreads) void k_final(
         float mloc = -INFINITY;
         for (int c = c0; c < c1; ++c) mloc = fmaxf(mloc, pm[c]);
         const float M = block_max(mloc, bs);
-        double S = 0.0;
-        const double off = block_prefix_setup(nC, [&](int c) { return part_mass(pm[c], ps[c], M); }, bs, &S);
         const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)(l + 1), 3u);
-        const double tau = (double)u * S;
-        double cprev;
-        const int cstar =
-            block_locate(nC, [&](int c) { return part_mass(pm[c], ps[c], M); }, tau, off, bs, &sh_cprev, &cprev);
+        const Located loc = locate(nC, [&](int c) { return tile_mass(pm[c], ps[c], M); }, u, bs, &sh_cprev);
 
         // rescan the chunk in index order: 32 contiguous elements per thread
-        const float mc = pm[cstar];
-        const double scale = part_mass(mc, 1.0, M);
+        const float mc = pm[loc.idx];
+        const double scale = tile_mass(mc, 1.0, M);
         const T* x = Tg + ((size_t)b * (gamma + 1) + l) * V;
         constexpr int EPT = kChunkElems / kThreads;  // 32
-        const int e0 = cstar * kChunkElems + t * EPT;
+        const int e0 = loc.idx * kChunkElems + t * EPT;
         double wv[EPT];
         double tsum = 0.0;
 #pragma unroll
@@ -440,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void k_final(
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
             run += wv[j];
-            if (hit == INT_MAX && cprev + scale * run > tau) hit = e0 + j;
+            if (hit == INT_MAX && loc.cprev + scale * run > loc.tau) hit = e0 + j;
             if (wv[j] > 0.0) lastpos = e0 + j;
         }
         const int th = block_min_int(hit, bs);
@@ -468,6 +559,7 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     float* tgm = reinterpret_cast<float*>(w + lay.tgt_m);
     double* tgs = reinterpret_cast<double*>(w + lay.tgt_s);
     double* lse_t = reinterpret_cast<double*>(w + lay.lse_t);
+    double* ptw = reinterpret_cast<double*>(w + lay.pt);
     int32_t* ridx = reinterpret_cast<int32_t*>(w + lay.resid_idx);
     int32_t* rlist = reinterpret_cast<int32_t*>(w + lay.resid_list);
     int32_t* rcnt = reinterpret_cast<int32_t*>(w + lay.resid_count);
@@ -475,20 +567,34 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     double* rp = reinterpret_cast<double*>(w + lay.res_p);
     float* bm = reinterpret_cast<float*>(w + lay.bon_m);
     double* bsum = reinterpret_cast<double*>(w + lay.bon_s);
-    const int nT = n_tiles(V), nC = n_chunks(V);
-    const int nM = (B + 255) / 256;
+    const int nT = n_tiles(std::is_same<DT, Bf16>::value ? 1 : 0, V), nC = n_chunks(V);
 
     prof_begin(K_TARGET_PARTIALS, s);
     hipLaunchKernelGGL(k_row_partials<DT>, dim3(nC, B * gamma), dim3(kThreads), 0, s, Tg, len, accepted, B, gamma, V,
                        nC, 0, tgm, tgs);
+    hipLaunchKernelGGL(k_target_lse<DT>, dim3((B * gamma + 3) / 4), dim3(kThreads), 0, s, Tg, tok, len, tgm, tgs, B,
+                       gamma, V, nC, lse_t, ptw);
     prof_end(K_TARGET_PARTIALS, s);
     prof_begin(K_ACCEPT, s);
-    hipLaunchKernelGGL(k_accept<DT>, dim3(1), dim3(kAcceptThreads), 0, s, Tg, tok, pd, len, tgm, tgs, B, gamma, V, nC,
-                       seed, lse_t, accepted, n_out, target_p, ridx, rlist, rcnt);
+    hipLaunchKernelGGL(k_accept, dim3(1), dim3(kAcceptThreads), 0, s, pd, len, ptw, B, gamma, seed, accepted, n_out,
+                       target_p, ridx, rlist, rcnt);
     prof_end(K_ACCEPT, s);
     prof_begin(K_RESID_TILES, s);
-    hipLaunchKernelGGL(k_resid_tiles<DT>, dim3(nT * nM), dim3(kThreads), 0, s, Tg, L, A, Bm, x0, tok, lse_d, lse_t,
-                       accepted, rlist, rcnt, gamma, V, r, nT, nM, rw, rp);
+    if (std::is_same<DT, Bf16>::value) {
+        constexpr int NW = 4;
+        const int nM = (B + 32 * NW - 1) / (32 * NW);
+        const int S = std::min(nT, (cu_count() + nM - 1) / nM);
+        hipLaunchKernelGGL(k_resid_tiles_bf16<NW>, dim3(S * nM), dim3(64 * NW), 0, s,
+                           reinterpret_cast<const uint16_t*>(Tg), reinterpret_cast<const uint16_t*>(L),
+                           reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(Bm), x0, tok,
+                           lse_d, lse_t, accepted, rlist, rcnt, gamma, V, r, nT, nM, S, rw, rp);
+    } else {
+        const int nM = (B + 255) / 256;
+        hipLaunchKernelGGL(k_resid_tiles_f32, dim3(nT * nM), dim3(kThreads), 0, s,
+                           reinterpret_cast<const float*>(Tg), reinterpret_cast<const float*>(L),
+                           reinterpret_cast<const float*>(A), reinterpret_cast<const float*>(Bm), x0, tok, lse_d,
+                           lse_t, accepted, rlist, rcnt, gamma, V, r, nT, nM, rw, rp);
+    }
     prof_end(K_RESID_TILES, s);
     prof_begin(K_BONUS_PARTIALS, s);
     hipLaunchKernelGGL(k_row_partials<DT>, dim3(nC, B), dim3(kThreads), 0, s, Tg, len, accepted, B, gamma, V, nC, 1,
