@@ -18,7 +18,8 @@ DSPARK_F32 = 0
 DSPARK_BF16 = 1
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libdspark.so")
+# DSPARK_LIB may point at another build of the same library (for A/B timing).
+_LIB_PATH = os.environ.get("DSPARK_LIB") or os.path.join(_PKG, "libdspark.so")
 
 # Kernel ids for dspark_profile_query.
 KERNELS = ("draft_tiles", "draft_locate", "schedule", "target_partials", "accept", "resid_tiles",

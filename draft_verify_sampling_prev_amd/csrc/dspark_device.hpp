@@ -82,6 +82,16 @@ __device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t b, uint3
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
+// Softmax weight exp(x - m) as 2^(x log2 e - mlog2) with one FMA, where
+// mlog2 = m * log2 e rounded to float (m finite).  Every pass that sums the
+// weights of a row segment and every pass that rescans that segment uses this
+// expression with the same m, so they see the same weights bit for bit.
+// x = -inf gives 0.
+__device__ __forceinline__ float softmax_w(float x, float mlog2)
+{
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mlog2));
+}
+
 __device__ __forceinline__ double exp_to_double(double y)
 {
     double t = y * kLog2eD;
@@ -93,24 +103,64 @@ __device__ __forceinline__ double exp_to_double(double y)
 }
 
 // ---------------------------------------------------------------------------
-// Reductions.  xor-shuffles within 16-lane groups (one MFMA output row group)
-// and within the 64-lane wavefront.
+// Reductions.  Within a 16-lane row (one MFMA output row group) they use DPP
+// lane moves, which run on the VALU: a butterfly of quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror and row_mirror leaves the full
+// reduction in every lane of the row; an inclusive scan uses row_shr by
+// 1, 2, 4, 8 with zero fill.  Wave-wide reductions use xor-shuffles.
 // ---------------------------------------------------------------------------
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL> __device__ __forceinline__ double dpp_d(double v)
+{
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xFFFFFFFFll), CTRL, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, true);
+    return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
 __device__ __forceinline__ float max16(float v)
 {
-    v = fmaxf(v, __shfl_xor(v, 1, 16));
-    v = fmaxf(v, __shfl_xor(v, 2, 16));
-    v = fmaxf(v, __shfl_xor(v, 4, 16));
-    v = fmaxf(v, __shfl_xor(v, 8, 16));
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    return v;
+}
+
+__device__ __forceinline__ float sum16f(float v)
+{
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
     return v;
 }
 
 __device__ __forceinline__ double sum16(double v)
 {
-    v += __shfl_xor(v, 1, 16);
-    v += __shfl_xor(v, 2, 16);
-    v += __shfl_xor(v, 4, 16);
-    v += __shfl_xor(v, 8, 16);
+    v += dpp_d<kDppXor1>(v);
+    v += dpp_d<kDppXor2>(v);
+    v += dpp_d<kDppHalfMirror>(v);
+    v += dpp_d<kDppMirror>(v);
+    return v;
+}
+
+// Inclusive prefix sum over the 16 lanes of each row, in lane order.
+__device__ __forceinline__ double scan16(double v)
+{
+    v += dpp_d<kDppShr1>(v);
+    v += dpp_d<kDppShr2>(v);
+    v += dpp_d<kDppShr4>(v);
+    v += dpp_d<kDppShr8>(v);
     return v;
 }
 

@@ -39,31 +39,41 @@ __device__ __forceinline__ int cond_token(const int32_t* __restrict__ x0, const 
     return min(max(x, 0), V - 1);
 }
 
-// Tile max / sum of exp for the rows held in a wave's accumulators.
-//   f(mb, nb, i) gives the biased logit, valid(nb) whether the column exists.
-template <int MB, int NB, class FFn, class ValidFn, class OutFn>
-__device__ __forceinline__ void tile_partials_epilogue(FFn f, ValidFn valid, OutFn out)
+// Tile max m_t and s_t = sum exp(f - m_t) (fp32 within the tile) for the
+// rows held in a wave's accumulators: f[mb][nb][i] is row 16mb + 4g + i,
+// column 16nb + j of the tile (g = lane >> 4, j = lane & 15).  Columns at or
+// beyond ncols count as absent (only when `tail`).  The row results of block
+// mb are gathered so that lane (g, j < 4) holds row 4g + j in m[mb], s[mb].
+// A row without a finite logit gets m = -inf, s = 0.
+template <int MB, int NB>
+__device__ __forceinline__ void tile_row_partials(const floatx4 (&f)[MB][NB], bool tail, int ncols, float (&m)[MB],
+                                                  float (&s)[MB])
 {
-    const int lane = threadIdx.x & 63;
+    const int j = threadIdx.x & 15;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+        float mres = -INFINITY, sres = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float fv[NB];
             float mx = -INFINITY;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                fv[nb] = valid(nb) ? f(mb, nb, i) : -INFINITY;
+                fv[nb] = (tail && 16 * nb + j >= ncols) ? -INFINITY : f[mb][nb][i];
                 mx = fmaxf(mx, fv[nb]);
             }
             mx = max16(mx);
-            double s = 0.0;
+            const float ml = mx * kLog2e;
+            float sv = 0.0f;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                if (fv[nb] != -INFINITY) s += (double)exp_fast(fv[nb] - mx);
-            s = sum16(s);
-            if ((lane & 15) == 0) out(16 * mb + 4 * (lane >> 4) + i, mx, s);
+            for (int nb = 0; nb < NB; ++nb) sv += softmax_w(fv[nb], ml);
+            sv = sum16f(sv);
+            if (mx == -INFINITY) sv = 0.0f;
+            mres = j == i ? mx : mres;
+            sres = j == i ? sv : sres;
         }
+        m[mb] = mres;
+        s[mb] = sres;
     }
 }
 
@@ -104,15 +114,16 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
     }
     markov_tile<F32, 4>(Bm, V, r, n0, arow, compute, lds, acc);
     if (!compute) return;
-    tile_partials_epilogue<4, 8>([&](int mb, int nb, int i) { return acc[mb][nb][i]; },
-                              [&](int nb) { return n0 + 16 * nb + (lane & 15) < V; },
-                              [&](int lrow, float mx, double s) {
-                                  const int row = mw0 + lrow;
-                                  if (row < B) {
-                                      pm[(size_t)row * nT + tile] = mx;
-                                      ps[(size_t)row * nT + tile] = s;
-                                  }
-                              });
+    float m[4], sv[4];
+    tile_row_partials<4, 8>(acc, n0 + kTileN > V, V - n0, m, sv);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int row = mw0 + 16 * mb + 4 * (lane >> 4) + (lane & 15);
+        if ((lane & 15) < 4 && row < B) {
+            pm[(size_t)row * nT + tile] = m[mb];
+            ps[(size_t)row * nT + tile] = (double)sv[mb];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -121,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
 // holds two (Bm tile, L tile) buffers; the DMA of tile i+1 is issued before
 // the MFMAs of tile i.
 // ---------------------------------------------------------------------------
-template <int NW>
+template <int NW, int KS>
 __global__ __launch_bounds__(64 * NW) void k_draft_tiles_bf16(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
     const int32_t* __restrict__ x0, const int32_t* tok, int B, int gamma, int V, int r, int k, int nT, int nM, int S,
@@ -129,7 +140,8 @@ __global__ __launch_bounds__(64 * NW) void k_draft_tiles_bf16(
 {
     constexpr int R = 32 * NW;
     constexpr int kBuf = kBmTileBytes + R * kTrowBytes;
-    __shared__ __attribute__((aligned(1024))) char lds[2 * kBuf];
+    __shared__ __attribute__((aligned(1024))) char buf0[kBuf];
+    __shared__ __attribute__((aligned(1024))) char buf1[kBuf];
 
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int mblk = lid % nM, slot = lid / nM;
@@ -152,42 +164,64 @@ __global__ __launch_bounds__(64 * NW) void k_draft_tiles_bf16(
     int ridx[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) ridx[t] = min(m0 + dma_row_of<NW>(t), B - 1) * gamma + (k - 1);
-    const int nks = (r + 31) / 32;
+    const int nks = KS > 0 ? KS : (r + 31) / 32;
 
-    dma_bm_tile<NW>(Bm, V, r, slot * kTcols, 32 * nks, lds);
-    dma_row_tile<NW>(L, ridx, V, slot * kTcols, lds + kBmTileBytes);
-    int it = 0;
-    for (int tile = slot; tile < nT; tile += S, ++it) {
-        wait_all_mem();
-        __syncthreads();  // tile's DMA has landed; the other buffer is free
-        const int next = tile + S;
-        if (next < nT) {
-            char* nb_ = lds + ((it + 1) & 1) * kBuf;
-            dma_bm_tile<NW>(Bm, V, r, next * kTcols, 32 * nks, nb_);
-            dma_row_tile<NW>(L, ridx, V, next * kTcols, nb_ + kBmTileBytes);
+    // Software pipeline: the row partials of tile i (VALU) are computed while
+    // the MFMAs of tile i+1 run (fprev holds tile i's logits f = acc + L),
+    // and stored after the next loop-top barrier.
+    floatx4 fprev[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) fprev[mb][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
+    int prev = -1, done = -1;  // tile held in fprev; tile whose partials wait in pm_r / ps_r
+    float pm_r[2] = { 0.f, 0.f }, ps_r[2] = { 0.f, 0.f };
+    auto store = [&]() {
+        if (done < 0) return;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int row = mw + 16 * mb + 4 * (lane >> 4) + (lane & 15);
+            if ((lane & 15) < 4 && row < B) {
+                pm[(size_t)row * nT + done] = pm_r[mb];
+                ps[(size_t)row * nT + done] = (double)ps_r[mb];
+            }
         }
-        if (!active) continue;
-        const char* buf = lds + (it & 1) * kBuf;
-        floatx4 acc[2][4];
+        done = -1;
+    };
+    auto finish = [&]() {  // partials of tile `prev` from fprev into pm_r / ps_r
+        tile_row_partials<2, 4>(fprev, (prev + 1) * kTcols > V, V - prev * kTcols, pm_r, ps_r);
+        done = prev;
+    };
+    persistent_tiles(
+        slot, nT, S, buf0, buf1,
+        [&](int tile, char* buf) {
+            dma_bm_tile<NW>(Bm, V, r, tile * kTcols, 32 * nks, buf);
+            dma_row_tile<NW>(L, ridx, V, tile * kTcols, buf + kBmTileBytes);
+        },
+        [&](int tile, const char* buf) {
+            if (!active) return;
+            floatx4 acc[2][4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
-        tile_mma64<2>(a, buf, nks, acc);
-        const int n0 = tile * kTcols;
+                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
+            tile_mma64<2, KS>(a, buf, nks, acc);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) acc[mb][nb] += row_vals(buf + kBmTileBytes, 32 * w + 16 * mb, nb);
-        tile_partials_epilogue<2, 4>([&](int mb, int nb, int i) { return acc[mb][nb][i]; },
-                                     [&](int nb) { return n0 + 16 * nb + (lane & 15) < V; },
-                                     [&](int lrow, float mx, double s) {
-                                         const int row = mw + lrow;
-                                         if (row < B) {
-                                             pm[(size_t)row * nT + tile] = mx;
-                                             ps[(size_t)row * nT + tile] = s;
-                                         }
-                                     });
+                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] += row_vals(buf + kBmTileBytes, 32 * w + 16 * mb, nb);
+            finish();  // math of the previous tile; interleaves with the MFMAs above
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) fprev[mb][nb] = acc[mb][nb];
+            prev = tile;
+        },
+        [&]() { store(); });
+    if (active) {
+        store();
+        finish();
+        store();
     }
 }
 
@@ -228,11 +262,12 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
     const float mt = pmr[loc.idx];
     const double scale = tile_mass(mt, 1.0, M);
     const int l16 = threadIdx.x & 15;
+    const float ml = mt * kLog2e;
     double w[TT::kNB];
 #pragma unroll
     for (int nb = 0; nb < TT::kNB; ++nb) {
-        const bool ok = n0 + 16 * nb + l16 < V && f[nb] != -INFINITY && mt != -INFINITY;
-        w[nb] = ok ? (double)exp_fast(f[nb] - mt) : 0.0;
+        const bool ok = n0 + 16 * nb + l16 < V && mt != -INFINITY;
+        w[nb] = ok ? (double)softmax_w(f[nb], ml) : 0.0;
     }
     double wsel;
     const int j = scan_tile_weights<TT::kNB>(w, scale, loc.cprev, loc.tau, &wsel);
@@ -256,9 +291,10 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
         constexpr int NW = 8;
         const int nM = (B + 32 * NW - 1) / (32 * NW);
         const int S = std::min(nT, (cu_count() + nM - 1) / nM);
-        hipLaunchKernelGGL(k_draft_tiles_bf16<NW>, dim3(S * nM), dim3(64 * NW), 0, s,
-                           static_cast<const uint16_t*>(L), static_cast<const uint16_t*>(A),
-                           static_cast<const uint16_t*>(Bm), x0, tok, B, gamma, V, r, k, nT, nM, S, pm, ps);
+        auto kern = (r + 31) / 32 == 8 ? k_draft_tiles_bf16<NW, 8> : k_draft_tiles_bf16<NW, 0>;
+        hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * NW), 0, s, static_cast<const uint16_t*>(L),
+                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, B, gamma, V,
+                           r, k, nT, nM, S, pm, ps);
     } else {
         const int nM = (B + 255) / 256;
         hipLaunchKernelGGL(k_draft_tiles_f32, dim3(nT * nM), dim3(kThreads), 0, s, static_cast<const float*>(L),

@@ -21,7 +21,7 @@ namespace dspark {
 // partials without a finite value weigh 0.
 __device__ __forceinline__ double tile_mass(float m, double s, float M)
 {
-    return m == -INFINITY ? 0.0 : s * exp((double)m - (double)M);
+    return m == -INFINITY ? 0.0 : s * exp_to_double((double)m - (double)M);
 }
 
 struct Located {
@@ -83,13 +83,7 @@ __device__ __forceinline__ int scan_tile_weights(const double (&w)[NB], double s
     double whit = 0.0, wlast = 0.0;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        double v = w[nb];
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const double n = __shfl_up(v, o, 16);
-            if (l16 >= o) v += n;
-        }
-        const double cum = carry + v;
+        const double cum = carry + scan16(w[nb]);
         carry = __shfl(cum, 15, 16);
         const uint64_t mc = __ballot(cprev + scale * cum > tau) & 0xFFFFull;
         const uint64_t mp = __ballot(w[nb] > 0.0) & 0xFFFFull;
@@ -166,7 +160,8 @@ __device__ __forceinline__ void row_tile_f(const uint16_t* L_row, const uint16_t
         floatx4 acc[1][4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[0][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
-        tile_mma64<1>(a, lds, nks, acc);
+        if (nks == 8) tile_mma64<1, 8>(a, lds, nks, acc);
+        else tile_mma64<1, 0>(a, lds, nks, acc);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) f[nb] = acc[0][nb][0] + lv[nb];
     }

@@ -142,14 +142,17 @@ __device__ __forceinline__ void load_a_frags(const uint16_t* const (&arow)[MB], 
         }
 }
 
-// acc[mb][nb] += A block mb x Bm tile over k steps 0..nks-1 (B operand from LDS).
-template <int MB>
+// acc[mb][nb] += A block mb x Bm tile over k steps 0..nks-1 (B operand from
+// LDS).  KS > 0 fixes the number of k steps at compile time (straight-line
+// code, which also keeps the compiler's LDS-DMA alias tracking precise);
+// KS == 0 takes nks at run time.
+template <int MB, int KS>
 __device__ __forceinline__ void tile_mma64(const uint4 (&a)[MB][8], const char* bufB, int nks,
                                            floatx4 (&acc)[MB][4])
 {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        if (ks >= nks) break;
+        if (KS > 0 ? ks >= KS : ks >= nks) break;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             const bf16x8 b = b_frag(bufB, ks, nb);
@@ -163,5 +166,41 @@ __device__ __forceinline__ void tile_mma64(const uint4 (&a)[MB][8], const char* 
 
 // Wait for this wave's outstanding DMA / memory operations.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Persistent double-buffered tile loop: tiles first, first + S, ... < nT.
+// issue(tile, buf) starts the DMA of a tile into a buffer, compute(tile, buf)
+// consumes it.  b0 and b1 must be two distinct __shared__ arrays and the loop
+// is unrolled by two, so each compute statically reads one array while the
+// DMA into the other is in flight; the compiler can then see that they do
+// not alias and does not make the LDS reads wait for that DMA.
+//
+// flush() runs right after each loop-top barrier, before the next DMA is
+// issued: kernels use it to store results kept in registers from earlier
+// tiles, so those stores drain during a whole iteration instead of being
+// waited for at the next loop top.
+template <class IssueFn, class ComputeFn, class FlushFn>
+__device__ __forceinline__ void persistent_tiles(int first, int nT, int S, char* b0, char* b1, IssueFn issue,
+                                                 ComputeFn compute, FlushFn flush)
+{
+    int tile = first;
+    if (tile >= nT) return;
+    issue(tile, b0);
+    for (;;) {
+        wait_all_mem();
+        __syncthreads();  // this tile has landed in b0; every wave is done with b1
+        flush();
+        if (tile + S < nT) issue(tile + S, b1);
+        compute(tile, b0);
+        tile += S;
+        if (tile >= nT) break;
+        wait_all_mem();
+        __syncthreads();
+        flush();
+        if (tile + S < nT) issue(tile + S, b0);
+        compute(tile, b1);
+        tile += S;
+        if (tile >= nT) break;
+    }
+}
 
 }  // namespace dspark

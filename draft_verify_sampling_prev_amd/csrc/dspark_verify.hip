@@ -115,19 +115,20 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T*
         }
     }
     const float M = block_max(mloc, bs);
+    // exp(x - M) is 0 for x = -inf; each 16-byte vector is summed in fp32, vectors in fp64.
+    const float ml = M * kLog2e;
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = e0 + (i * kThreads + (int)threadIdx.x) * PV;
         if (e < V) {
+            float sv = 0.0f;
 #pragma unroll
-            for (int j = 0; j < PV; ++j) {
-                const float xv = DT::get(v[i], j);
-                if (xv != -INFINITY) s += (double)exp_fast(xv - M);
-            }
+            for (int j = 0; j < PV; ++j) sv += softmax_w(DT::get(v[i], j), ml);
+            s += (double)sv;
         }
     }
-    s = block_sum(s, bs);
+    s = block_sum(M == -INFINITY ? 0.0 : s, bs);
     if (threadIdx.x == 0) {
         om[(size_t)row * nC + c] = M;
         os[(size_t)row * nC + c] = s;
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
 // over 64-column tiles; each LDS buffer holds the Bm tile, the rejected
 // rows' draft-logit tile and their target tile, all staged by DMA.
 // ---------------------------------------------------------------------------
-template <int NW>
+template <int NW, int KS>
 __global__ __launch_bounds__(64 * NW) void k_resid_tiles_bf16(
     const uint16_t* __restrict__ Tg, const uint16_t* __restrict__ L, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
@@ -331,7 +332,8 @@ __global__ __launch_bounds__(64 * NW) void k_resid_tiles_bf16(
     constexpr int R = 32 * NW;
     constexpr int kRowBytes = R * kTrowBytes;
     constexpr int kBuf = kBmTileBytes + 2 * kRowBytes;
-    __shared__ __attribute__((aligned(1024))) char lds[2 * kBuf];
+    __shared__ __attribute__((aligned(1024))) char buf0[kBuf];
+    __shared__ __attribute__((aligned(1024))) char buf1[kBuf];
     __shared__ SplitLse sh_lse[R][2];
 
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -371,61 +373,58 @@ __global__ __launch_bounds__(64 * NW) void k_resid_tiles_bf16(
         sh_lse[i][0] = d;
         sh_lse[i][1] = t;
     }
-    const int nks = (r + 31) / 32;
+    const int nks = KS > 0 ? KS : (r + 31) / 32;
 
-    auto issue = [&](int tile, char* buf) {
-        dma_bm_tile<NW>(Bm, V, r, tile * kTcols, 32 * nks, buf);
-        dma_row_tile<NW>(L, lidx, V, tile * kTcols, buf + kBmTileBytes);
-        dma_row_tile<NW>(Tg, tidx, V, tile * kTcols, buf + kBmTileBytes + kRowBytes);
-    };
-    issue(slot, lds);
-    int it = 0;
-    for (int tile = slot; tile < nT; tile += S, ++it) {
-        wait_all_mem();
-        __syncthreads();
-        const int next = tile + S;
-        if (next < nT) issue(next, lds + ((it + 1) & 1) * kBuf);
-        if (!active) continue;
-        const char* buf = lds + (it & 1) * kBuf;
-        floatx4 acc[2][4];
+    persistent_tiles(
+        slot, nT, S, buf0, buf1,
+        [&](int tile, char* buf) {
+            dma_bm_tile<NW>(Bm, V, r, tile * kTcols, 32 * nks, buf);
+            dma_row_tile<NW>(L, lidx, V, tile * kTcols, buf + kBmTileBytes);
+            dma_row_tile<NW>(Tg, tidx, V, tile * kTcols, buf + kBmTileBytes + kRowBytes);
+        },
+        [&](int tile, const char* buf) {
+            if (!active) return;
+            floatx4 acc[2][4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
-        tile_mma64<2>(a, buf, nks, acc);
-        const int n0 = tile * kTcols;
-        const int nl = lane & 15;
+                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
+            tile_mma64<2, KS>(a, buf, nks, acc);
+            const int n0 = tile * kTcols;
+            const int nl = lane & 15;
+            const bool tail = n0 + kTcols > V;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            floatx4 tv[4];
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                acc[mb][nb] += row_vals(buf + kBmTileBytes, 32 * w + 16 * mb, nb);
-                tv[nb] = row_vals(buf + kBmTileBytes + kRowBytes, 32 * w + 16 * mb, nb);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int lr = 32 * w + 16 * mb + 4 * (lane >> 4) + i;
-                const SplitLse ld = sh_lse[lr][0], ltg = sh_lse[lr][1];
-                double sw = 0.0, sp = 0.0;
+            for (int mb = 0; mb < 2; ++mb) {
+                floatx4 tv[4];
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) {
-                    if (n0 + 16 * nb + nl < V) {
+                    acc[mb][nb] += row_vals(buf + kBmTileBytes, 32 * w + 16 * mb, nb);
+                    tv[nb] = row_vals(buf + kBmTileBytes + kRowBytes, 32 * w + 16 * mb, nb);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int lr = 32 * w + 16 * mb + 4 * (lane >> 4) + i;
+                    const SplitLse ld = sh_lse[lr][0], ltg = sh_lse[lr][1];
+                    double sw = 0.0, sp = 0.0;
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) {
                         float ptv;
-                        sw += (double)resid_weight(acc[mb][nb][i], tv[nb][i], ld, ltg, &ptv);
+                        float wr = resid_weight(acc[mb][nb][i], tv[nb][i], ld, ltg, &ptv);
+                        if (tail && n0 + 16 * nb + nl >= V) wr = ptv = 0.0f;
+                        sw += (double)wr;
                         sp += (double)ptv;
                     }
-                }
-                sw = sum16(sw);
-                sp = sum16(sp);
-                const int row = m0 + lr;
-                if (nl == 0 && row < cnt) {
-                    rw[(size_t)row * nT + tile] = sw;
-                    rp[(size_t)row * nT + tile] = sp;
+                    sw = sum16(sw);
+                    sp = sum16(sp);
+                    const int row = m0 + lr;
+                    if (nl == 0 && row < cnt) {
+                        rw[(size_t)row * nT + tile] = sw;
+                        rp[(size_t)row * nT + tile] = sp;
+                    }
                 }
             }
-        }
-    }
+        },
+        [&]() {});
 }
 
 // ---------------------------------------------------------------------------
@@ -507,6 +506,7 @@ __global__ __launch_bounds__(kThreads) void k_final(
 
         // rescan the chunk in index order: 32 contiguous elements per thread
         const float mc = pm[loc.idx];
+        const float mcl = mc * kLog2e;
         const double scale = tile_mass(mc, 1.0, M);
         const T* x = Tg + ((size_t)b * (gamma + 1) + l) * V;
         constexpr int EPT = kChunkElems / kThreads;  // 32
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void k_final(
             double wj = 0.0;
             if (e < V && mc != -INFINITY) {
                 const float xv = DT::to_f32(x[e]);
-                if (xv != -INFINITY) wj = (double)exp_fast(xv - mc);
+                wj = (double)softmax_w(xv, mcl);
             }
             wv[j] = wj;
             tsum += wj;
@@ -584,7 +584,8 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
         constexpr int NW = 4;
         const int nM = (B + 32 * NW - 1) / (32 * NW);
         const int S = std::min(nT, (cu_count() + nM - 1) / nM);
-        hipLaunchKernelGGL(k_resid_tiles_bf16<NW>, dim3(S * nM), dim3(64 * NW), 0, s,
+        auto kern = (r + 31) / 32 == 8 ? k_resid_tiles_bf16<NW, 8> : k_resid_tiles_bf16<NW, 0>;
+        hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * NW), 0, s,
                            reinterpret_cast<const uint16_t*>(Tg), reinterpret_cast<const uint16_t*>(L),
                            reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(Bm), x0, tok,
                            lse_d, lse_t, accepted, rlist, rcnt, gamma, V, r, nT, nM, S, rw, rp);
