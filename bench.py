@@ -46,10 +46,11 @@ def _workload(name: str):
 def draft_tiles_bytes_flops(wl) -> tuple:
     """Algorithmic bytes and flops of one launch of the draft Markov tile kernel:
     the step's L rows (B*V), Bm (r*V) and the gathered A rows (B*r), plus the
-    per-(row, tile) partials written (4 + 8 bytes) and the token reads."""
+    per-(row, tile) partials written (float max + float sum = 8 bytes) and the
+    token reads."""
     s = 2 if wl.dtype == "bf16" else 4
     nT = (wl.V + 63) // 64 if wl.dtype == "bf16" else (wl.V + 127) // 128
-    byts = s * (wl.B * wl.V + wl.r * wl.V + wl.B * wl.r) + wl.B * nT * 12 + wl.B * 4
+    byts = s * (wl.B * wl.V + wl.r * wl.V + wl.B * wl.r) + wl.B * nT * 8 + wl.B * 4
     flops = 2.0 * wl.B * wl.r * wl.V
     return byts, flops
 

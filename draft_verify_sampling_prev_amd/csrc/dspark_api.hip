@@ -36,8 +36,7 @@ WsLayout ws_layout(int B, int gamma, int V)
         o = align256(o + bytes);
         return at;
     };
-    l.draft_m = take(Bz * nT * 4);
-    l.draft_s = take(Bz * nT * 8);
+    l.draft_part = take(Bz * nT * 8);
     l.tgt_m = take(Bz * G * nC * 4);
     l.tgt_s = take(Bz * G * nC * 8);
     l.lse_t = take(Bz * G * 8);
@@ -45,8 +44,7 @@ WsLayout ws_layout(int B, int gamma, int V)
     l.resid_idx = take(Bz * 4);
     l.resid_list = take(Bz * 4);
     l.resid_count = take(4);
-    l.res_w = take(Bz * nT * 8);
-    l.res_p = take(Bz * nT * 8);
+    l.res_part = take(Bz * nT * 8);
     l.bon_m = take(Bz * nC * 4);
     l.bon_s = take(Bz * nC * 8);
     l.total = o;

@@ -75,10 +75,6 @@ __device__ __forceinline__ float philox_uniform(uint64_t seed, uint32_t b, uint3
 //   exp_fast(x): e^x = 2^(x log2 e) with the hardware base-2 exponential;
 //     used for the un-normalised softmax weights exp(x - m) inside the vocab
 //     passes, where every weight is then summed in double.
-//   exp_to_double(y): e^y for a double argument y <= ~0, with the integer part
-//     of y log2 e applied exactly by ldexp and only the fraction in [0, 1)
-//     going through the single-precision base-2 exponential, so the relative
-//     error stays at the level of one float ulp for any y.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
@@ -92,15 +88,10 @@ __device__ __forceinline__ float softmax_w(float x, float mlog2)
     return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mlog2));
 }
 
-__device__ __forceinline__ double exp_to_double(double y)
-{
-    double t = y * kLog2eD;
-    if (!(t > -1100.0)) return 0.0;  // also maps NaN / -inf to 0
-    double n = floor(t);
-    float fr = (float)(t - n);       // in [0, 1)
-    double e = (double)__builtin_amdgcn_exp2f(fr);
-    return ldexp(e, (int)n);
-}
+// Reference exponent of a row segment with max m for softmax_w: m log2 e, or
+// 0 when the segment has no finite value (every weight is then exp2(-inf) = 0).
+__device__ __forceinline__ float row_mlog2(float m) { return m == -INFINITY ? 0.0f : m * kLog2e; }
+
 
 // ---------------------------------------------------------------------------
 // Reductions.  Within a 16-lane row (one MFMA output row group) they use DPP
@@ -192,16 +183,41 @@ __device__ __forceinline__ int wave_max_int(int v)
     return v;
 }
 
-// Inclusive scan across the 64 lanes (fixed order, deterministic).
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
+
+// DPP move restricted to the rows in ROWS (others read 0).
+template <int CTRL, int ROWS> __device__ __forceinline__ double dpp_d_rows(double v)
+{
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xFFFFFFFFll), CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROWS, 0xF, false);
+    return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+// Inclusive scan across the 64 lanes in lane order (fixed order,
+// deterministic): row scans, then rows 1 and 3 add the last lane of rows 0
+// and 2, then rows 2 and 3 add lane 31.
 __device__ __forceinline__ double wave_incl_scan(double v)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        double n = __shfl_up(v, o, 64);
-        if (lane >= o) v += n;
-    }
+    v = scan16(v);
+    v += dpp_d_rows<kDppRowBcast15, 0xA>(v);
+    v += dpp_d_rows<kDppRowBcast31, 0xC>(v);
     return v;
+}
+
+constexpr int kDppWaveShr1 = 0x138;  // lane i <- lane i-1 across the wave (lane 0 reads 0)
+
+// Exclusive prefix from an inclusive scan: the inclusive value of the previous lane (0 in lane 0).
+__device__ __forceinline__ double wave_excl_from_incl(double inc) { return dpp_d<kDppWaveShr1>(inc); }
+
+// Value of lane 63 in every lane.
+__device__ __forceinline__ double wave_last(double v)
+{
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), 63);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+    return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
 }
 
 // Workgroup (256 threads) reductions through a small LDS scratch.

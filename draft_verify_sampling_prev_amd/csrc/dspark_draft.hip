@@ -7,12 +7,14 @@
 // diagram.  Each step is two launches:
 //
 //   k_draft_tiles   Markov MFMA tile fused with the vocabulary pass: per
-//                   (row, 128-column tile) it writes the tile max m_t (fp32)
-//                   and s_t = sum exp(f - m_t) (fp64).  The biased logits f
-//                   are never written to memory.  bf16: persistent kernel of
-//                   8-wave workgroups over 256-row x 128-column tiles
-//                   (dspark_tile.hpp), about one workgroup per CU; fp32:
-//                   one 4-wave workgroup per tile (dspark_markov.hpp).
+//                   (row, tile) it writes the tile max m_t and
+//                   s_t = sum exp(f - m_t) (both fp32, as one float2).  The
+//                   biased logits f are never written to memory.  bf16:
+//                   persistent kernel of 8-wave workgroups over 256-row x
+//                   64-column tiles in vocabulary-major MFMA form
+//                   (dspark_tile.hpp), one workgroup per CU, slots
+//                   interleaved over the tiles; fp32: one 4-wave workgroup
+//                   per 256-row x 128-column tile (dspark_markov.hpp).
 //   k_draft_locate  one workgroup per request.  Combines the tile partials in
 //                   tile order (fp64), draws u = U(seed, b, k, 0), finds the
 //                   tile where the running mass passes u*S, recomputes that
@@ -22,6 +24,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "dspark_internal.hpp"
 #include "dspark_locate.hpp"
@@ -63,12 +66,11 @@ __device__ __forceinline__ void tile_row_partials(const floatx4 (&f)[MB][NB], bo
                 mx = fmaxf(mx, fv[nb]);
             }
             mx = max16(mx);
-            const float ml = mx * kLog2e;
+            const float ml = row_mlog2(mx);
             float sv = 0.0f;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sv += softmax_w(fv[nb], ml);
             sv = sum16f(sv);
-            if (mx == -INFINITY) sv = 0.0f;
             mres = j == i ? mx : mres;
             sres = j == i ? sv : sres;
         }
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
                                                               const float* __restrict__ Bm,
                                                               const int32_t* __restrict__ x0, const int32_t* tok,
                                                               int B, int gamma, int V, int r, int k, int nT, int nM,
-                                                              float* __restrict__ pm, double* __restrict__ ps)
+                                                              float2* __restrict__ part)
 {
     __shared__ __attribute__((aligned(16))) char lds[markov_lds_bytes<F32>()];
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -119,109 +121,147 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
         const int row = mw0 + 16 * mb + 4 * (lane >> 4) + (lane & 15);
-        if ((lane & 15) < 4 && row < B) {
-            pm[(size_t)row * nT + tile] = m[mb];
-            ps[(size_t)row * nT + tile] = (double)sv[mb];
-        }
+        if ((lane & 15) < 4 && row < B) part[(size_t)row * nT + tile] = make_float2(m[mb], sv[mb]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// bf16: persistent.  Workgroup `lid` owns row block mblk = lid % nM (32*NW
-// rows) and the 64-column tiles slot, slot + S, ... (slot = lid / nM).  LDS
-// holds two (Bm tile, L tile) buffers; the DMA of tile i+1 is issued before
-// the MFMAs of tile i.
+// bf16: persistent.  Workgroup `lid` owns row block mblk = lid % nM (256
+// rows, 32 per wave) and the tiles of slot lid / nM (slot_tiles).
+//
+// Pipeline per tile i (one iteration; four LDS buffers s0..s3, the loop body
+// unrolled so every copy reads and fills fixed buffers):
+//   wait until Bm tile i has landed, barrier;
+//   load the L values of tile i+1 into registers, DMA Bm tile i+3;
+//   acc = L values of tile i, MFMAs over Bm tile i, and the epilogue (row
+//   max and sum of exp) of tile i-1 written to LDS staging -- in opposite
+//   orders in the two halves of the workgroup.
+// Every iteration issues the same number of loads (past the last tile they
+// are dummies reading one location), so the wait for Bm tile i is a constant
+// count of outstanding loads per wave (wait_stage).
+// Staged partials are written out once at the end (coalesced float2 runs per
+// row); keeping vector-memory stores out of the loop keeps the compiler's
+// waits on the register loads exact.
 // ---------------------------------------------------------------------------
-template <int NW, int KS>
-__global__ __launch_bounds__(64 * NW) void k_draft_tiles_bf16(
+constexpr int kPartTiles = 12;  // tiles per slot whose partials fit the LDS staging
+
+template <int KS>
+__global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
     const int32_t* __restrict__ x0, const int32_t* tok, int B, int gamma, int V, int r, int k, int nT, int nM, int S,
-    float* __restrict__ pm, double* __restrict__ ps)
+    float2* __restrict__ part)
 {
-    constexpr int R = 32 * NW;
-    constexpr int kBuf = kBmTileBytes + R * kTrowBytes;
-    __shared__ __attribute__((aligned(1024))) char buf0[kBuf];
-    __shared__ __attribute__((aligned(1024))) char buf1[kBuf];
+    constexpr int NW = kTileWaves, R = kTileRows;
+    __shared__ __attribute__((aligned(1024))) char s0[kBmTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s1[kBmTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s2[kBmTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s3[kBmTileBytes];
+    __shared__ unsigned long long stage[kPartTiles][R];  // float2 pairs, stored as one 64-bit word each
 
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int mblk = lid % nM, slot = lid / nM;
-    if (slot >= nT) return;
-    const int w = wave_id(), lane = threadIdx.x & 63;
+    int t0, ts, cnt;
+    slot_tiles(slot, S, nT, &t0, &ts, &cnt);
+    if (cnt <= 0) return;  // uniform
+    const int w = wave_id(), lane = threadIdx.x & 63, G = lane >> 4, c = lane & 15;
     const int m0 = mblk * R;
     const int mw = m0 + 32 * w;  // first row of this wave
     const bool active = mw < B;
 
     uint4 a[2][8];
+    const uint16_t* lrow[2];
     {
         const uint16_t* arow[2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int ra = min(mw + 16 * mb + (lane & 15), B - 1);
-            arow[mb] = A + (size_t)cond_token(x0, tok, ra, gamma, k, V) * r;
+        for (int bb = 0; bb < 2; ++bb) {
+            const int row = min(mw + 16 * bb + c, B - 1);
+            arow[bb] = A + (size_t)cond_token(x0, tok, row, gamma, k, V) * r;
+            lrow[bb] = L + ((size_t)row * gamma + (k - 1)) * V;
         }
         load_a_frags<2>(arow, r, a);
     }
-    int ridx[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) ridx[t] = min(m0 + dma_row_of<NW>(t), B - 1) * gamma + (k - 1);
     const int nks = KS > 0 ? KS : (r + 31) / 32;
 
-    // Software pipeline: the row partials of tile i (VALU) are computed while
-    // the MFMAs of tile i+1 run (fprev holds tile i's logits f = acc + L),
-    // and stored after the next loop-top barrier.
-    floatx4 fprev[2][4];
+    auto load_l = [&](int i, uint2 (&lv)[2][4]) {
+        const bool dummy = i >= cnt;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+        for (int bb = 0; bb < 2; ++bb) load_row16(lrow[bb], (t0 + i * ts) * kTcols, V, dummy, lv[bb]);
+    };
+    auto dma = [&](int i, char* buf) { dma_bm_tile<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf); };
+
+    floatx4 fprev[4][2];
+    int prev = -1;  // local index of the tile held in fprev
+    auto epilogue = [&]() {
+        if (prev < 0 || !active) return;
+        const int n0 = (t0 + prev * ts) * kTcols;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) fprev[mb][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
-    int prev = -1, done = -1;  // tile held in fprev; tile whose partials wait in pm_r / ps_r
-    float pm_r[2] = { 0.f, 0.f }, ps_r[2] = { 0.f, 0.f };
-    auto store = [&]() {
-        if (done < 0) return;
+        for (int bb = 0; bb < 2; ++bb) {
+            floatx4 v[4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int row = mw + 16 * mb + 4 * (lane >> 4) + (lane & 15);
-            if ((lane & 15) < 4 && row < B) {
-                pm[(size_t)row * nT + done] = pm_r[mb];
-                ps[(size_t)row * nT + done] = (double)ps_r[mb];
-            }
+            for (int vb = 0; vb < 4; ++vb) v[vb] = fprev[vb][bb];
+            float m, sum;
+            row64_max_sum(v, n0 + kTcols > V, V - n0, &m, &sum);
+            if (G == bb) stage[prev][32 * w + 16 * bb + c] = pack_f2(m, sum);
         }
-        done = -1;
     };
-    auto finish = [&]() {  // partials of tile `prev` from fprev into pm_r / ps_r
-        tile_row_partials<2, 4>(fprev, (prev + 1) * kTcols > V, V - prev * kTcols, pm_r, ps_r);
-        done = prev;
+    uint2 lc[2][4], ln[2][4];
+    auto body = [&](int i, const char* cur, char* nxt) {
+        wait_stage<2 * kRow16Loads, 32 / NW>(i);
+        barrier_lds();  // Bm tile i has landed in cur; every wave is done with nxt (tile i-1)
+        load_l(i + 1, ln);
+        dma(i + 3, nxt);
+        if (active) {
+            floatx4 acc[4][2];
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(lc[bb][vb]);
+            // The epilogue of the previous tile is independent of these
+            // MFMAs.  Waves 0-3 and 4-7 take the two phases in opposite
+            // order, so each SIMD (one wave of each half) has one wave on the
+            // matrix cores while the other runs the vector ALU.  (Only with a
+            // compile-time k-step count: the run-time variant has no
+            // registers to spare for the second code path.)
+            if (KS > 0 && (w & 4)) {
+                epilogue();
+                tile_mma_vm<2, KS>(a, cur, nks, acc);
+            } else {
+                tile_mma_vm<2, KS>(a, cur, nks, acc);
+                epilogue();
+            }
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) fprev[vb][bb] = acc[vb][bb];
+            prev = i;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb) lc[bb][vb] = ln[bb][vb];
     };
-    persistent_tiles(
-        slot, nT, S, buf0, buf1,
-        [&](int tile, char* buf) {
-            dma_bm_tile<NW>(Bm, V, r, tile * kTcols, 32 * nks, buf);
-            dma_row_tile<NW>(L, ridx, V, tile * kTcols, buf + kBmTileBytes);
-        },
-        [&](int tile, const char* buf) {
-            if (!active) return;
-            floatx4 acc[2][4];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
-            tile_mma64<2, KS>(a, buf, nks, acc);
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] += row_vals(buf + kBmTileBytes, 32 * w + 16 * mb, nb);
-            finish();  // math of the previous tile; interleaves with the MFMAs above
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) fprev[mb][nb] = acc[mb][nb];
-            prev = tile;
-        },
-        [&]() { store(); });
-    if (active) {
-        store();
-        finish();
-        store();
+
+    load_l(0, lc);
+    dma(0, s0);
+    dma(1, s1);
+    dma(2, s2);
+    for (int i = 0;;) {
+        body(i, s0, s3);
+        if (++i >= cnt) break;
+        body(i, s1, s0);
+        if (++i >= cnt) break;
+        body(i, s2, s1);
+        if (++i >= cnt) break;
+        body(i, s3, s2);
+        if (++i >= cnt) break;
+    }
+    epilogue();
+    wait_all_mem();  // the dummy loads past the last tile
+    __syncthreads();
+    // Write the staged partials (consecutive threads take consecutive tiles of a row).
+    for (int e = threadIdx.x; e < R * cnt; e += 64 * NW) {
+        const int row = e / cnt, i = e - row * cnt;
+        if (m0 + row < B) part[(size_t)(m0 + row) * nT + t0 + i * ts] = unpack_f2(stage[i][row]);
     }
 }
 
@@ -234,9 +274,8 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
                                                            const typename DT::T* __restrict__ Bm,
                                                            const int32_t* __restrict__ x0, int32_t* tok,
                                                            float* __restrict__ p_out, double* __restrict__ lse_out,
-                                                           const float* __restrict__ pm, const double* __restrict__ ps,
-                                                           int B, int gamma, int V, int r, int k, int nT,
-                                                           uint64_t seed)
+                                                           const float2* __restrict__ part, int B, int gamma, int V,
+                                                           int r, int k, int nT, uint64_t seed)
 {
     typedef TileTraits<DT> TT;
     __shared__ __attribute__((aligned(1024))) char lds[TT::kLdsBytes];
@@ -244,33 +283,47 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
     __shared__ double sh_cprev;
 
     const int b = blockIdx.x;
-    const float* pmr = pm + (size_t)b * nT;
-    const double* psr = ps + (size_t)b * nT;
+    const float2* pr = part + (size_t)b * nT;
     const int per = (nT + kThreads - 1) / kThreads;
     const int t0 = min((int)threadIdx.x * per, nT), t1 = min(t0 + per, nT);
     float mloc = -INFINITY;
-    for (int i = t0; i < t1; ++i) mloc = fmaxf(mloc, pmr[i]);
+    for (int i = t0; i < t1; ++i) mloc = fmaxf(mloc, pr[i].x);
     const float M = block_max(mloc, bs);
     const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)k, 0u);
-    const Located loc = locate(nT, [&](int i) { return tile_mass(pmr[i], psr[i], M); }, u, bs, &sh_cprev);
+    const Located loc = locate(
+        nT, [&](int i) { const float2 q = pr[i]; return tile_mass(q.x, (double)q.y, M); }, u, bs, &sh_cprev);
 
     const int n0 = loc.idx * TT::kCols;
     const int prev = cond_token(x0, tok, b, gamma, k, V);
-    float f[TT::kNB];
-    row_tile_f(L + ((size_t)b * gamma + (k - 1)) * V, A, Bm, prev, V, r, n0, lds, f);
-    if ((threadIdx.x >> 6) != 0) return;
-    const float mt = pmr[loc.idx];
+    const auto* lrow = L + ((size_t)b * gamma + (k - 1)) * V;
+    const float mt = pr[loc.idx].x;
     const double scale = tile_mass(mt, 1.0, M);
-    const int l16 = threadIdx.x & 15;
-    const float ml = mt * kLog2e;
-    double w[TT::kNB];
-#pragma unroll
-    for (int nb = 0; nb < TT::kNB; ++nb) {
-        const bool ok = n0 + 16 * nb + l16 < V && mt != -INFINITY;
-        w[nb] = ok ? (double)softmax_w(f[nb], ml) : 0.0;
-    }
+    const float ml = row_mlog2(mt);
     double wsel;
-    const int j = scan_tile_weights<TT::kNB>(w, scale, loc.cprev, loc.tau, &wsel);
+    int j;
+    if constexpr (std::is_same<DT, Bf16>::value) {
+        floatx4 f[4];
+        row_tile_vm(lrow, A, Bm, prev, V, r, n0, lds, f);
+        if ((threadIdx.x >> 6) != 0) return;
+        j = scan_vm_tile(
+            n0, b, scale, loc.cprev, loc.tau,
+            [&](int vb, int i, int col) {
+                return col < V && mt != -INFINITY ? (double)softmax_w(f[vb][i], ml) : 0.0;
+            },
+            &wsel);
+    } else {
+        float f[TT::kNB];
+        row_tile_f(lrow, A, Bm, prev, V, r, n0, lds, f);
+        if ((threadIdx.x >> 6) != 0) return;
+        const int l16 = threadIdx.x & 15;
+        double w[TT::kNB];
+#pragma unroll
+        for (int nb = 0; nb < TT::kNB; ++nb) {
+            const bool ok = n0 + 16 * nb + l16 < V && mt != -INFINITY;
+            w[nb] = ok ? (double)softmax_w(f[nb], ml) : 0.0;
+        }
+        j = scan_tile_weights<TT::kNB>(w, scale, loc.cprev, loc.tau, &wsel);
+    }
     if (threadIdx.x == 0) {
         tok[b * gamma + (k - 1)] = min(n0 + j, V - 1);
         p_out[b * gamma + (k - 1)] = (float)(scale * wsel / loc.S);
@@ -278,38 +331,116 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
     }
 }
 
+// bf16: one wave per request, for rows of at most 64*PER tiles.  The A
+// operand of the request's conditioning token is loaded first; lane l loads
+// its contiguous slice of the row's tile partials into registers with all
+// loads in flight at once; the partials are combined with wave scans (no
+// barriers, no LDS) by the same rule as locate(); the chosen tile is
+// recomputed by the wave alone from its own LDS copy of the Bm tile.
+template <int KS, int PER>
+__global__ __launch_bounds__(64) void k_draft_locate_bf16(const uint16_t* __restrict__ L,
+                                                          const uint16_t* __restrict__ A,
+                                                          const uint16_t* __restrict__ Bm,
+                                                          const int32_t* __restrict__ x0, int32_t* tok,
+                                                          float* __restrict__ p_out, double* __restrict__ lse_out,
+                                                          const float2* __restrict__ part, int B, int gamma, int V,
+                                                          int r, int k, int nT, uint64_t seed)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    // The partial loads go first: the A-operand loads wait for the token.
+    const float2* pr = part + (size_t)b * nT;
+    float2 q[PER];
+    int i0;
+    load_slices<PER>(pr, nT, make_float2(-INFINITY, 0.0f), q, &i0);
+    const int prev = cond_token(x0, tok, b, gamma, k, V);
+    uint4 a[1][8];
+    {
+        const uint16_t* arow[1] = { A + (size_t)prev * r };
+        load_a_frags<1>(arow, r, a);
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) mloc = fmaxf(mloc, q[j].x);
+    const float M = wave_max(mloc);
+    const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)k, 0u);
+    // Tile masses relative to the row max, kept when the registers allow.
+    constexpr bool kCache = PER <= 32;
+    double ms[kCache ? PER : 1];
+    if constexpr (kCache) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) ms[j] = tile_mass(q[j].x, (double)q[j].y, M);
+    }
+    const Located loc = wave_locate_slices<PER>(
+        i0,
+        [&](int j) {
+            if constexpr (kCache) return ms[j];
+            else return tile_mass(q[j].x, (double)q[j].y, M);
+        },
+        u);
+    const int idx = loc.idx;
+    const double cprev = loc.cprev, tau = loc.tau, S = loc.S;
+
+    const int n0 = idx * kTcols;
+    floatx4 f[4];
+    row_tile_vm_wave<KS>(L + ((size_t)b * gamma + (k - 1)) * V, a, Bm, V, r, n0, lds, f);
+    // Max of the chosen tile, from the registers of the lane whose slice holds it.
+    float mt_l = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < PER; ++jj)
+        if (i0 + jj == idx) mt_l = q[jj].x;
+    const float mt = __shfl(mt_l, min(idx / ((nT + 63) / 64), 63), 64);
+    const double scale = tile_mass(mt, 1.0, M);
+    const float ml = row_mlog2(mt);
+    double wsel;
+    const int j = scan_vm_tile(
+        n0, b, scale, cprev, tau,
+        [&](int vb, int i, int col) { return col < V && mt != -INFINITY ? (double)softmax_w(f[vb][i], ml) : 0.0; },
+        &wsel);
+    if (lane == 0) {
+        tok[b * gamma + (k - 1)] = min(n0 + j, V - 1);
+        p_out[b * gamma + (k - 1)] = (float)(scale * wsel / S);
+        lse_out[b * gamma + (k - 1)] = (double)M + log(S);
+    }
+}
+
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
                              int gamma, int V, int r, int k, uint64_t seed, int32_t* tok, float* p, double* lse,
                              void* ws, const WsLayout& lay, hipStream_t s)
 {
-    char* w = static_cast<char*>(ws);
-    float* pm = reinterpret_cast<float*>(w + lay.draft_m);
-    double* ps = reinterpret_cast<double*>(w + lay.draft_s);
+    float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.draft_part);
     const int nT = n_tiles(dtype, V);
     prof_begin(K_DRAFT_TILES, s);
     if (dtype == 1) {
-        constexpr int NW = 8;
-        const int nM = (B + 32 * NW - 1) / (32 * NW);
-        const int S = std::min(nT, (cu_count() + nM - 1) / nM);
-        auto kern = (r + 31) / 32 == 8 ? k_draft_tiles_bf16<NW, 8> : k_draft_tiles_bf16<NW, 0>;
-        hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * NW), 0, s, static_cast<const uint16_t*>(L),
+        const int nM = (B + kTileRows - 1) / kTileRows;
+        const int S = std::min(nT, std::max((cu_count() + nM - 1) / nM, (nT + kPartTiles - 1) / kPartTiles));
+        auto kern = (r + 31) / 32 == 8 ? k_draft_tiles_bf16<8> : k_draft_tiles_bf16<0>;
+        hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, B, gamma, V,
-                           r, k, nT, nM, S, pm, ps);
+                           r, k, nT, nM, S, part);
     } else {
         const int nM = (B + 255) / 256;
         hipLaunchKernelGGL(k_draft_tiles_f32, dim3(nT * nM), dim3(kThreads), 0, s, static_cast<const float*>(L),
                            static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, B, gamma, V, r, k,
-                           nT, nM, pm, ps);
+                           nT, nM, part);
     }
     prof_end(K_DRAFT_TILES, s);
     prof_begin(K_DRAFT_LOCATE, s);
-    if (dtype == 1)
-        hipLaunchKernelGGL(k_draft_locate<Bf16>, dim3(B), dim3(kThreads), 0, s, static_cast<const uint16_t*>(L),
-                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, pm, ps,
+    if (dtype == 1 && nT <= 64 * 64) {
+        const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32;
+        auto kern = small ? (k8 ? k_draft_locate_bf16<8, 32> : k_draft_locate_bf16<0, 32>)
+                          : (k8 ? k_draft_locate_bf16<8, 64> : k_draft_locate_bf16<0, 64>);
+        hipLaunchKernelGGL(kern, dim3(B), dim3(64), 0, s, static_cast<const uint16_t*>(L),
+                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
                            B, gamma, V, r, k, nT, seed);
-    else
+    } else if (dtype == 1) {
+        hipLaunchKernelGGL(k_draft_locate<Bf16>, dim3(B), dim3(kThreads), 0, s, static_cast<const uint16_t*>(L),
+                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
+                           B, gamma, V, r, k, nT, seed);
+    } else
         hipLaunchKernelGGL(k_draft_locate<F32>, dim3(B), dim3(kThreads), 0, s, static_cast<const float*>(L),
-                           static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, p, lse, pm, ps, B,
+                           static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, p, lse, part, B,
                            gamma, V, r, k, nT, seed);
     prof_end(K_DRAFT_LOCATE, s);
     return hipGetLastError();

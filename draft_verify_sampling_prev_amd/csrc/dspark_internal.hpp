@@ -20,14 +20,14 @@ inline int n_chunks(int V) { return (V + kChunkElems - 1) / kChunkElems; }
 
 // Byte offsets into the caller's workspace (each 256-byte aligned).
 struct WsLayout {
-    size_t draft_m, draft_s;      // [B][nT] f32 / f64 : draft tile max and sum of exp
+    size_t draft_part;            // [B][nT] float2 : draft tile max and sum of exp(f - max)
     size_t tgt_m, tgt_s;          // [B*gamma][nC] f32 / f64 : target chunk max and sum of exp
     size_t lse_t;                 // [B][gamma] f64 : target log-normalisers of verified rows
     size_t pt;                    // [B][gamma] f64 : p_t(x_k) of verified rows
     size_t resid_idx;             // [B] i32 : compact residual index of request b, or -1
     size_t resid_list;            // [B] i32 : requests with a rejection, ascending
     size_t resid_count;           // [1] i32
-    size_t res_w, res_p;          // [B][nT] f64 : per tile sum of max(0, p_t - p_d) and of p_t
+    size_t res_part;              // [B][nT] float2 : per tile sum of max(0, p_t - p_d) and of p_t
     size_t bon_m, bon_s;          // [B][nC] f32 / f64 : bonus-row chunk max and sum of exp
     size_t total;
 };

@@ -17,11 +17,14 @@
 
 namespace dspark {
 
-// Mass of a (max m, sum of exp(x - m) = s) partial relative to the row max M;
-// partials without a finite value weigh 0.
+// Mass of a (max m, sum of exp(x - m) = s) partial relative to the row max
+// M >= m: s * 2^((m - M) log2 e) with the single-precision exponential.  The
+// relative error is about 1e-7 * (1 + |m - M|), i.e. below 3e-6 for every
+// partial within 30 of the max; farther ones weigh less than e^-30 of the
+// row.  Partials without a finite value weigh 0.
 __device__ __forceinline__ double tile_mass(float m, double s, float M)
 {
-    return m == -INFINITY ? 0.0 : s * exp_to_double((double)m - (double)M);
+    return m == -INFINITY ? 0.0 : s * (double)__builtin_amdgcn_exp2f((m - M) * kLog2e);
 }
 
 struct Located {
@@ -112,13 +115,12 @@ template <> struct TileTraits<F32> {
 };
 template <> struct TileTraits<Bf16> {
     static constexpr int kCols = kTcols;  // 64
-    static constexpr int kNB = kCols / 16;
     static constexpr int kLdsBytes = kBmTileBytes;
 };
 
-// Biased logits f = L_row + A[prev] . Bm of the tile starting at column n0,
-// bit-identical to the tile kernel of the same dtype.  All threads of the
-// 4-wave workgroup call; wave 0, lane l receives column 16*nb + (l & 15) in f[nb].
+// fp32: biased logits f = L_row + A[prev] . Bm of the tile starting at column
+// n0, bit-identical to the fp32 tile kernel.  All threads of the 4-wave
+// workgroup call; wave 0, lane l receives column 16*nb + (l & 15) in f[nb].
 __device__ __forceinline__ void row_tile_f(const float* L_row, const float* A, const float* Bm, int prev, int V, int r,
                                            int n0, char* lds, float (&f)[TileTraits<F32>::kNB])
 {
@@ -136,36 +138,181 @@ __device__ __forceinline__ void row_tile_f(const float* L_row, const float* A, c
     for (int nb = 0; nb < 8; ++nb) f[nb] = acc[0][nb][0];
 }
 
-__device__ __forceinline__ void row_tile_f(const uint16_t* L_row, const uint16_t* A, const uint16_t* Bm, int prev,
-                                           int V, int r, int n0, char* lds, float (&f)[TileTraits<Bf16>::kNB])
+// bf16: biased logits of one row over the tile starting at column n0, in the
+// vocabulary-major layout of the bf16 tile kernels (dspark_tile.hpp) and
+// bit-identical to them: every batch column of the MFMA carries the row's A
+// operand, and wave 0, lane (G, c) receives in f[vb][i] column
+// n0 + vm_col(G, vb) + i.  All threads of the 4-wave workgroup call.
+__device__ __forceinline__ void row_tile_vm(const uint16_t* L_row, const uint16_t* A, const uint16_t* Bm, int prev,
+                                            int V, int r, int n0, char* lds, floatx4 (&f)[4])
 {
-    const int lane = threadIdx.x & 63;
     const bool w0 = (threadIdx.x >> 6) == 0;
     const int nks = (r + 31) / 32;
-    dma_bm_tile<kThreads / 64>(Bm, V, r, n0, 32 * nks, lds);
+    dma_bm_tile<kThreads / 64>(Bm, V, r, n0, false, lds);
     uint4 a[1][8];
-    float lv[4];
+    uint2 lv[4];
     if (w0) {
         const uint16_t* arow[1] = { A + (size_t)prev * r };
         load_a_frags<1>(arow, r, a);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int col = n0 + 16 * nb + (lane & 15);
-            lv[nb] = col < V ? Bf16::to_f32(L_row[col]) : 0.0f;
-        }
+        load_row16(L_row, n0, V, false, lv);
     }
     wait_all_mem();
     __syncthreads();
     if (w0) {
-        floatx4 acc[1][4];
+        floatx4 acc[4][1];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[0][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
-        if (nks == 8) tile_mma64<1, 8>(a, lds, nks, acc);
-        else tile_mma64<1, 0>(a, lds, nks, acc);
+        for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(lv[vb]);
+        if (nks == 8) tile_mma_vm<1, 8>(a, lds, nks, acc);
+        else tile_mma_vm<1, 0>(a, lds, nks, acc);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) f[nb] = acc[0][nb][0] + lv[nb];
+        for (int vb = 0; vb < 4; ++vb) f[vb] = acc[vb][0];
     }
     __syncthreads();  // LDS may be reused after this point
+}
+
+// One-wave form of row_tile_vm for kernels that run one wave per row: the
+// wave stages the Bm tile in its own LDS buffer and waits only for its own
+// loads (no barrier).  The A operand (a, k steps < nks) is loaded by the
+// caller ahead of time.
+template <int KS>
+__device__ __forceinline__ void row_tile_vm_wave(const uint16_t* L_row, const uint4 (&a)[1][8], const uint16_t* Bm,
+                                                 int V, int r, int n0, char* lds, floatx4 (&f)[4])
+{
+    dma_bm_tile<1>(Bm, V, r, n0, false, lds);
+    uint2 lv[4];
+    load_row16(L_row, n0, V, false, lv);
+    wait_all_mem();
+    floatx4 acc[4][1];
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(lv[vb]);
+    tile_mma_vm<1, KS>(a, lds, (r + 31) / 32, acc);
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) f[vb] = acc[vb][0];
+}
+
+// One wave, masses held in registers: lane l owns the contiguous slice
+// [i0, i0 + PER) (i0 = l * per, per <= PER; slots past the slice or past n
+// must have mass 0) and mass(j) gives the mass of its slot j.  Same rule as
+// locate(): slice sums combined by a wave scan in lane order, first index
+// whose running mass exceeds u*S, else the last index of positive mass,
+// else 0.  mass(j) is evaluated twice per slot.
+template <int PER, class MassFn>
+__device__ __forceinline__ Located wave_locate_slices(int i0, MassFn mass, float u)
+{
+    const int lane = threadIdx.x & 63;
+    Located L;
+    double sl = 0.0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) sl += mass(j);
+    const double inc = wave_incl_scan(sl);
+    const double off = wave_excl_from_incl(inc);
+    L.S = wave_last(inc);
+    L.tau = (double)u * L.S;
+    int hit = -1, lastpos = -1;
+    double c = off, cph = 0.0, cpl = 0.0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const double mj = mass(j);
+        const double cb = c;
+        c += mj;
+        if (hit < 0 && c > L.tau) {
+            hit = i0 + j;
+            cph = cb;
+        }
+        if (mj > 0.0) {
+            lastpos = i0 + j;
+            cpl = cb;
+        }
+    }
+    const uint64_t mh = __ballot(hit >= 0), mp = __ballot(lastpos >= 0);
+    if (mh) {
+        const int src = __builtin_ctzll(mh);
+        L.idx = __shfl(hit, src, 64);
+        L.cprev = __shfl(cph, src, 64);
+    } else if (mp) {
+        const int src = 63 - __builtin_clzll(mp);
+        L.idx = __shfl(lastpos, src, 64);
+        L.cprev = __shfl(cpl, src, 64);
+    } else {
+        L.idx = 0;
+        L.cprev = 0.0;
+    }
+    return L;
+}
+
+// Lane l's slice [l*per, l*per + PER) of a row of n float2 entries, loaded
+// with every load in flight at once (clamped addresses); slots past the
+// slice or past n get `pad`.
+template <int PER>
+__device__ __forceinline__ void load_slices(const float2* __restrict__ row, int n, float2 pad, float2 (&q)[PER],
+                                            int* i0_out)
+{
+    const int lane = threadIdx.x & 63;
+    const int per = (n + 63) / 64;
+    const int i0 = lane * per;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const float2 v = row[min(i0 + j, n - 1)];
+        q[j] = (j < per && i0 + j < n) ? v : pad;
+    }
+    *i0_out = i0;
+}
+
+// Wave 0: inverse-CDF scan of a 64-column tile held as by row_tile_vm.  The
+// row sits in MFMA batch column pos & 15 (the column it occupied in the tile
+// pass), i.e. lanes 16G + (pos & 15), G = 0..3.  wfn(vb, i, col) gives the
+// weight of the lane's element i of block vb, which is column col (the
+// function returns 0 for col >= V).  Returns the tile column where
+// cprev + scale * (running weight in column order) first exceeds tau, else
+// the last column of positive weight, else 0; *w_sel receives its weight.
+template <class WFn>
+__device__ __forceinline__ int scan_vm_tile(int n0, int pos, double scale, double cprev, double tau, WFn wfn,
+                                            double* w_sel)
+{
+    const int lane = threadIdx.x & 63, G = lane >> 4, c = lane & 15, cp = pos & 15;
+    double w[16];
+    double tot = 0.0;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const int vb = q4 ^ (G & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[4 * q4 + i] = wfn(vb, i, n0 + 16 * G + 4 * q4 + i);
+            tot += w[4 * q4 + i];
+        }
+    }
+    const double t0 = __shfl(tot, cp, 64), t1 = __shfl(tot, 16 + cp, 64), t2 = __shfl(tot, 32 + cp, 64);
+    double run = G == 0 ? 0.0 : (G == 1 ? t0 : (G == 2 ? t0 + t1 : (t0 + t1) + t2));
+    int hit = -1, last = -1;
+    double whit = 0.0, wlast = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        run += w[j];
+        if (hit < 0 && cprev + scale * run > tau) {
+            hit = 16 * G + j;
+            whit = w[j];
+        }
+        if (w[j] > 0.0) {
+            last = 16 * G + j;
+            wlast = w[j];
+        }
+    }
+    const uint64_t mh = __ballot(c == cp && hit >= 0);
+    const uint64_t mp = __ballot(c == cp && last >= 0);
+    int src, col;
+    if (mh) {
+        src = __builtin_ctzll(mh);
+        col = __shfl(hit, src, 64);
+        *w_sel = __shfl(whit, src, 64);
+    } else if (mp) {
+        src = 63 - __builtin_clzll(mp);
+        col = __shfl(last, src, 64);
+        *w_sel = __shfl(wlast, src, 64);
+    } else {
+        col = 0;
+        *w_sel = 0.0;
+    }
+    return col;
 }
 
 }  // namespace dspark

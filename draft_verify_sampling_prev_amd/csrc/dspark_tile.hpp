@@ -1,32 +1,34 @@
-// dspark_tile.hpp -- bf16 Markov-bias tiles for gfx950, staged by LDS DMA.
+// dspark_tile.hpp -- bf16 Markov-bias tiles for gfx950 in vocabulary-major
+// MFMA form.
 //
-//   f[m][n] = sum_i A[x_m][i] * Bm[i][n]   (+ L_m[n] added after the MFMAs)
+//   f[m][n] = L_m[n] + sum_i A[x_m][i] * Bm[i][n]
 //
-// Tile = 64 vocabulary columns.  A workgroup of NW wave64s covers 32*NW rows;
-// each wave owns 32 rows (two 16-row MFMA blocks, v_mfma_f32_16x16x32_bf16)
-// and the 64 columns (four 16-column blocks).  The wave's A operand (its 32
-// gathered A rows, all k <= 256) stays in registers for the whole launch.
+// is computed as the transposed product D = Bm_tile^T . A_rows^T with
+// v_mfma_f32_16x16x32_bf16: the MFMA row axis runs over vocabulary columns
+// and its column axis over batch rows.  A tile is 64 vocabulary columns
+// (four 16-column blocks vb); a wave covers 16*NBB batch rows (blocks bb).
 //
-// Staging: the Bm tile (k rows x 64 columns, 128 bytes per row) and the
-// logit tiles (rows x 64 columns) are copied global -> LDS with
-// global_load_lds_dwordx4 (no registers involved): each wave instruction
-// writes 1 KB = 8 LDS rows, lane l landing at byte 16*l, while its global
-// address is free, which is used to XOR-swizzle the eight 16-byte chunks of
-// each row.  Kernels double-buffer the staging so the DMA of the next tile
-// runs under the MFMAs of the current one.
+// Operands:
+//   B (batch rows)  lane (G = lane>>4, c = lane&15) holds A[x_row][32ks + 8G
+//                   .. +7] of batch row c of block bb; all k of a wave's rows
+//                   stay in registers for the whole launch.
+//   A (Bm^T)        read from an LDS copy of the Bm tile (staged with
+//                   global_load_lds_dwordx4) by ds_read_b64_tr_b16.
+//   C (initial)     the L values, loaded from global memory straight into
+//                   the accumulator layout (8-byte loads).
 //
-// Operand fetch with ds_read_b64_tr_b16: inside a 16-lane group, source lane
-// 4r+q addresses row r, columns 4q..4q+3 of a 4x16 block and lane j receives
-// column j of rows 0..3.  Two such reads give the B operand of a lane (8
-// consecutive k of one column); one read gives the four logit values a lane
-// needs in the MFMA accumulator layout (4 consecutive rows of one column).
-// With the swizzles below, every transpose read touches each LDS bank once
-// per 32 lanes.
+// Column map: element i of accumulator block vb in lane (G, c) is vocabulary
+// column n0 + 16G + 4*(vb ^ (G&1)) + i of batch row c.  So each lane holds 16
+// consecutive columns of one batch row per batch block, and a row's 64 tile
+// columns sit in the four lanes c, c+16, c+32, c+48.  (The XOR with G's low
+// bit makes the transpose reads of one instruction use both 8-byte halves of
+// the 16-byte LDS chunks; with the row swizzle below, every 32 lanes of a
+// transpose read then touch 64 distinct LDS banks.)
 //
-// Accumulator layout: acc[mb][nb][i] holds row 16*mb + 4*(lane>>4) + i of the
-// wave and tile column 16*nb + (lane&15).  An element depends only on its own
-// A row, Bm column and the fixed k-step order, so recomputing one row with
-// tile_mma64<1> reproduces it bit for bit.
+// Bit-exact recompute: an output element depends only on its initial value,
+// its Bm column, its A row and the fixed k-step order, and it occupies the
+// same (vocabulary row, batch column) position of the MFMA in the tile pass
+// and in the one-row recompute, so both produce the same bits.
 #pragma once
 
 #include "dspark_device.hpp"
@@ -34,62 +36,67 @@
 namespace dspark {
 
 constexpr int kTcols = 64;                   // vocabulary columns per tile
-constexpr int kTrowBytes = kTcols * 2;       // 128 bytes per LDS row
+constexpr int kTrowBytes = kTcols * 2;       // 128 bytes per LDS row of a Bm tile
 constexpr int kTileKmax = 256;
 constexpr int kBmTileBytes = kTileKmax * kTrowBytes;  // 32 KB
+constexpr int kTileWaves = 8;                // waves of a tile workgroup (32 rows each)
+constexpr int kTileRows = 32 * kTileWaves;   // batch rows of a tile workgroup
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Position of 16-byte chunk c inside LDS row k of a Bm tile / row `row` of a logit tile.
-__device__ __forceinline__ int swz_k(int k) { return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2); }
-__device__ __forceinline__ int swz_row(int row) { return (((row >> 1) & 1) << 1) | (((row >> 2) & 1) << 2); }
+// Position of 16-byte chunk c inside LDS row k of a Bm tile is c ^ swz_k(k).
+__device__ __forceinline__ int swz_k(int k) { return ((k >> 3) & 1) | (((k >> 1) & 1) << 1); }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
-__device__ __forceinline__ void dma16(const void* g, char* lds_wave_dst)
+// Offset (in columns, within the tile) of the 4 columns of accumulator block vb held by lane group G.
+__device__ __forceinline__ int vm_col(int G, int vb) { return 16 * G + 4 * (vb ^ (G & 1)); }
+
+// One buffer_load_dwordx4 ... lds per wave: lane i's 16 bytes, at byte
+// offset voff from the wave-uniform base, land at lds_wave_dst + 16 i.
+//
+// Two details keep the compiler's vector-memory waits exact in the tile
+// pipelines, whose loads into registers and into LDS are all outstanding at
+// once: the MUBUF form is used rather than global_load_lds (a FLAT-encoded
+// instruction that writes LDS makes the compiler treat the vector-memory
+// counter as unordered and wait for zero), and the LDS address is passed
+// through readfirstlane, so the compiler does not track the write against
+// later LDS reads (its alias tracking cannot tell the staging buffers of one
+// kernel apart and would wait for every outstanding load before each read).
+// Every caller orders the DMA and the reads itself: wait_vmem / wait_all_mem
+// (this wave's DMA done), then a workgroup barrier.
+__device__ __forceinline__ void dma16(const uint16_t* base, uint32_t voff, char* lds_wave_dst)
 {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_dst, 16, 0, 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_wave_dst);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)a, 16, voff, 0, 0, 0);
 }
 
-// DMA rows [0, kr) (kr a multiple of 32) of the Bm tile starting at column n0.
-// Rows >= r and chunks past V are fetched from clamped (valid, finite)
-// addresses: the A operand is zero for k >= r, and columns >= V are masked.
+// DMA the Bm tile starting at column n0 into buf: 32 blocks of 8 LDS rows,
+// block w + NW*t issued by wave w (t < 32/NW, so every wave issues the same
+// number of DMA instructions).  Rows >= r and chunks past V come from clamped
+// (valid, finite) addresses: the A operand is zero for k >= r and columns >= V
+// are masked.  `dummy` (wave-uniform) issues the same instructions with every
+// lane reading Bm[0][0..7], for pipelines that keep a fixed number of
+// outstanding loads past their last tile.
 template <int NW>
-__device__ __forceinline__ void dma_bm_tile(const uint16_t* __restrict__ Bm, int V, int r, int n0, int kr, char* buf)
-{
-    const int w = wave_id(), lane = threadIdx.x & 63;
-    const int nblk = kr >> 3;
-    for (int blk = w; blk < nblk; blk += NW) {
-        const int k = 8 * blk + (lane >> 3);
-        const int c = (lane & 7) ^ swz_k(k);
-        const int col = min(n0 + 8 * c, V - 8);
-        dma16(Bm + (size_t)min(k, r - 1) * V + col, buf + blk * 1024);
-    }
-}
-
-// DMA a logit tile of 32*NW rows: lane row 8*(w + NW*t) + (lane >> 3) comes
-// from global row ridx[t] (row stride V), columns n0..n0+63.
-template <int NW>
-__device__ __forceinline__ void dma_row_tile(const uint16_t* __restrict__ base, const int (&ridx)[4], int V, int n0,
-                                             char* buf)
+__device__ __forceinline__ void dma_bm_tile(const uint16_t* __restrict__ Bm, int V, int r, int n0, bool dummy,
+                                            char* buf)
 {
     const int w = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 32 / NW; ++t) {
         const int blk = w + NW * t;
-        const int row = 8 * blk + (lane >> 3);
-        const int c = (lane & 7) ^ swz_row(row);
+        const int kb = min(8 * blk, r - 1);  // wave-uniform base row of the block
+        const int k = min(8 * blk + (lane >> 3), r - 1);
+        const int c = (lane & 7) ^ swz_k(8 * blk + (lane >> 3));
         const int col = min(n0 + 8 * c, V - 8);
-        dma16(base + (size_t)ridx[t] * V + col, buf + blk * 1024);
+        const uint16_t* base = dummy ? Bm : Bm + (size_t)kb * V + n0;
+        const uint32_t voff = dummy ? 0u : (uint32_t)(((k - kb) * V + (col - n0)) * 2);
+        dma16(base, voff, buf + blk * 1024);
     }
-}
-
-// Tile row handled by this lane in dma_row_tile for slot t.
-template <int NW> __device__ __forceinline__ int dma_row_of(int t)
-{
-    return 8 * ((int)(threadIdx.x >> 6) + NW * t) + ((int)(threadIdx.x & 63) >> 3);
 }
 
 __device__ __forceinline__ v4s tr_read(const char* buf, int off)
@@ -97,110 +104,205 @@ __device__ __forceinline__ v4s tr_read(const char* buf, int off)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off));
 }
 
-// B operand of k step ks, column block nb: lane (g = lane>>4, j = lane&15)
-// gets k = 32ks + 8g .. +7 of tile column 16nb + j.
-__device__ __forceinline__ bf16x8 b_frag(const char* bufB, int ks, int nb)
+// A operand (Bm^T) of k step ks, vocabulary block vb: lane (G', j) gets
+// k = 32ks + 8G' .. +7 of tile column 16(j>>2) + 4(vb ^ ((j>>2)&1)) + (j&3).
+// In each 16-lane group, source lane 4r+q addresses LDS row k0 + r at the
+// four columns 16q + 4(vb ^ (q&1)) .. +3.
+__device__ __forceinline__ bf16x8 bm_frag(const char* bufB, int ks, int vb)
 {
     const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, j = lane & 15, r = j >> 2, q = j & 3;
-    const int c = 2 * nb + (q >> 1);
-    const int k0 = 32 * ks + 8 * g + r, k1 = k0 + 4;
-    const v4s lo = tr_read(bufB, k0 * kTrowBytes + 16 * (c ^ swz_k(k0)) + 8 * (q & 1));
-    const v4s hi = tr_read(bufB, k1 * kTrowBytes + 16 * (c ^ swz_k(k1)) + 8 * (q & 1));
+    const int Gk = lane >> 4, r = (lane & 15) >> 2, q = lane & 3;
+    const int chunk = 2 * q + (vb >> 1);
+    const int half = (vb ^ q) & 1;
+    const int k0 = 32 * ks + 8 * Gk + r, k1 = k0 + 4;
+    const v4s lo = tr_read(bufB, k0 * kTrowBytes + 16 * (chunk ^ swz_k(k0)) + 8 * half);
+    const v4s hi = tr_read(bufB, k1 * kTrowBytes + 16 * (chunk ^ swz_k(k1)) + 8 * half);
     typedef short v8s __attribute__((ext_vector_type(8)));
     const v8s v = { lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3] };
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// Logit values in accumulator layout: lane (g, j) gets rows row0 + 4g + 0..3
-// of tile column 16nb + j (row0 a multiple of 16), as floats.
-__device__ __forceinline__ floatx4 row_vals(const char* bufR, int row0, int nb)
-{
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, j = lane & 15, r = j >> 2, q = j & 3;
-    const int c = 2 * nb + (q >> 1);
-    const int row = row0 + 4 * g + r;
-    const v4s v = tr_read(bufR, row * kTrowBytes + 16 * (c ^ swz_row(row)) + 8 * (q & 1));
-    floatx4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __uint_as_float((uint32_t)(uint16_t)v[i] << 16);
-    return o;
-}
-
-// A-operand fragments of MB 16-row blocks for all k steps: lane l holds, for
-// row (l & 15) of block mb, k = 32*ks + 8*(l>>4) .. +7 (zero beyond r).
-template <int MB>
-__device__ __forceinline__ void load_a_frags(const uint16_t* const (&arow)[MB], int r, uint4 (&a)[MB][8])
+// B-operand fragments of NBB 16-row batch blocks for all k steps: lane l
+// holds, for batch row (l & 15) of block bb, k = 32*ks + 8*(l>>4) .. +7
+// (zero beyond r).
+template <int NBB>
+__device__ __forceinline__ void load_a_frags(const uint16_t* const (&arow)[NBB], int r, uint4 (&a)[NBB][8])
 {
     const int kq8 = 8 * ((threadIdx.x & 63) >> 4);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int bb = 0; bb < NBB; ++bb)
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int k = 32 * ks + kq8;
-            a[mb][ks] = k < r ? ld16(arow[mb] + k) : make_uint4(0u, 0u, 0u, 0u);
+            a[bb][ks] = k < r ? ld16(arow[bb] + k) : make_uint4(0u, 0u, 0u, 0u);
         }
 }
 
-// acc[mb][nb] += A block mb x Bm tile over k steps 0..nks-1 (B operand from
-// LDS).  KS > 0 fixes the number of k steps at compile time (straight-line
-// code, which also keeps the compiler's LDS-DMA alias tracking precise);
-// KS == 0 takes nks at run time.
-template <int MB, int KS>
-__device__ __forceinline__ void tile_mma64(const uint4 (&a)[MB][8], const char* bufB, int nks,
-                                           floatx4 (&acc)[MB][4])
+// Four bf16 values (8 bytes) -> floats.
+__device__ __forceinline__ floatx4 bf16x4_to_f32(uint2 v)
 {
+    return floatx4{ __uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
+                    __uint_as_float(v.y & 0xFFFF0000u) };
+}
+
+__device__ __forceinline__ uint2 ld8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// Load the 16 values of one row that lane group G holds in a tile starting
+// at column n0, in accumulator-block order: v[vb] = columns n0 + vm_col(G, vb)
+// .. +3.  Two 16-byte loads of columns n0 + 16G .. +15; for odd G the two
+// 8-byte halves of each load are swapped (vm_col's XOR).  A load at or past V
+// reads a clamped (valid) address; `dummy` reads the row start (fixed load
+// count past the last tile).
+constexpr int kRow16Loads = 2;  // vector-memory loads issued by one load_row16
+
+__device__ __forceinline__ void load_row16(const uint16_t* __restrict__ row, int n0, int V, bool dummy,
+                                           uint2 (&v)[4])
+{
+    const int G = (threadIdx.x & 63) >> 4;
+    const int keep = dummy ? 0 : -1;  // branch-free: a dummy reads the row start
+    const bool odd = (G & 1) != 0;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        if (KS > 0 ? ks >= KS : ks >= nks) break;
+    for (int h = 0; h < 2; ++h) {
+        const int col = min(n0 + 16 * G + 8 * h, V - 8) & keep;
+        const uint4 x = ld16(row + col);
+        const uint2 lo = make_uint2(x.x, x.y), hi = make_uint2(x.z, x.w);
+        v[2 * h] = odd ? hi : lo;
+        v[2 * h + 1] = odd ? lo : hi;
+    }
+}
+
+template <int NBB, int KS>
+__device__ __forceinline__ void tile_mma_vm(const uint4 (&a)[NBB][8], const char* bufB, int nks,
+                                            floatx4 (&acc)[4][NBB])
+{
+    if constexpr (KS > 0) {
+        // The Bm^T fragments of k step ks+1 are read while the MFMAs of step ks run.
+        bf16x8 b[4], bn[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const bf16x8 b = b_frag(bufB, ks, nb);
+        for (int vb = 0; vb < 4; ++vb) b[vb] = bm_frag(bufB, 0, vb);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][ks]), b,
-                                                                      acc[mb][nb], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) {
+#pragma unroll
+                for (int vb = 0; vb < 4; ++vb) bn[vb] = bm_frag(bufB, ks + 1, vb);
+            }
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+                for (int bb = 0; bb < NBB; ++bb)
+                    acc[vb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        b[vb], __builtin_bit_cast(bf16x8, a[bb][ks]), acc[vb][bb], 0, 0, 0);
+            if (ks + 1 < KS) {
+#pragma unroll
+                for (int vb = 0; vb < 4; ++vb) b[vb] = bn[vb];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            if (ks >= nks) break;
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb) {
+                const bf16x8 b = bm_frag(bufB, ks, vb);
+#pragma unroll
+                for (int bb = 0; bb < NBB; ++bb)
+                    acc[vb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        b, __builtin_bit_cast(bf16x8, a[bb][ks]), acc[vb][bb], 0, 0, 0);
+            }
         }
     }
 }
 
-// Wait for this wave's outstanding DMA / memory operations.
+// s_waitcnt encodings (gfx9 family): wait until at most n vector-memory
+// operations of this wave are outstanding; LDS/scalar and export counters untouched.
+template <int N> __device__ __forceinline__ void wait_vmem()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Stage wait of the tile pipelines.  Issue order per wave: prologue
+// [rows(0)] [Bm(0)] [Bm(1)] [Bm(2)], then iteration i issues [rows(i+1)]
+// [Bm(i+3)] after its barrier, where rows(.) is NL register loads and Bm(.)
+// is ND DMA instructions, always issued (dummies past the last tile).  Before
+// the barrier of iteration i this wave's Bm(i) must have landed; the loads
+// issued after it number 2ND (i = 0), 2ND + NL (i = 1), 2(NL + ND) (i >= 2).
+// Vector-memory loads complete in order, so waiting until at most that many
+// are outstanding is exact.
+template <int NL, int ND>
+__device__ __forceinline__ void wait_stage(int i)
+{
+    if (i >= 2) wait_vmem<2 * (NL + ND)>();
+    else if (i == 1) wait_vmem<2 * ND + NL>();
+    else wait_vmem<2 * ND>();
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() also waits for
+// every outstanding vector-memory load of the wave (its release fence), which
+// would drain a multi-stage load pipeline; the tile pipelines only share LDS
+// written by DMA, whose completion each wave establishes with wait_vmem
+// before the barrier.
+__device__ __forceinline__ void barrier_lds() { __builtin_amdgcn_s_barrier(); }
+
+// Wait for every outstanding memory operation of this wave.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Persistent double-buffered tile loop: tiles first, first + S, ... < nT.
-// issue(tile, buf) starts the DMA of a tile into a buffer, compute(tile, buf)
-// consumes it.  b0 and b1 must be two distinct __shared__ arrays and the loop
-// is unrolled by two, so each compute statically reads one array while the
-// DMA into the other is in flight; the compiler can then see that they do
-// not alias and does not make the LDS reads wait for that DMA.
-//
-// flush() runs right after each loop-top barrier, before the next DMA is
-// issued: kernels use it to store results kept in registers from earlier
-// tiles, so those stores drain during a whole iteration instead of being
-// waited for at the next loop top.
-template <class IssueFn, class ComputeFn, class FlushFn>
-__device__ __forceinline__ void persistent_tiles(int first, int nT, int S, char* b0, char* b1, IssueFn issue,
-                                                 ComputeFn compute, FlushFn flush)
+// A float pair as one 64-bit word: LDS staging stores it with a single
+// ds_write_b64 whose alias information the compiler keeps (two float stores
+// merged late lose it, and an LDS store without it waits for every
+// outstanding vector-memory load).
+__device__ __forceinline__ unsigned long long pack_f2(float x, float y)
 {
-    int tile = first;
-    if (tile >= nT) return;
-    issue(tile, b0);
-    for (;;) {
-        wait_all_mem();
-        __syncthreads();  // this tile has landed in b0; every wave is done with b1
-        flush();
-        if (tile + S < nT) issue(tile + S, b1);
-        compute(tile, b0);
-        tile += S;
-        if (tile >= nT) break;
-        wait_all_mem();
-        __syncthreads();
-        flush();
-        if (tile + S < nT) issue(tile + S, b0);
-        compute(tile, b1);
-        tile += S;
-        if (tile >= nT) break;
+    return (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
+}
+__device__ __forceinline__ float2 unpack_f2(unsigned long long v)
+{
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// Tiles of persistent slot s of S over nT tiles: t0, t0 + ts, ... (cnt of
+// them), a contiguous range per slot (ts = 1).  (Measured on MI355X at the
+// 129280-column shape, contiguous ranges stream faster than slots
+// interleaved tile by tile.)
+__device__ __forceinline__ void slot_tiles(int s, int S, int nT, int* t0, int* ts, int* cnt)
+{
+    const int q = nT / S, rem = nT - q * S;
+    *t0 = s * q + min(s, rem);
+    *ts = 1;
+    *cnt = q + (s < rem ? 1 : 0);
+}
+
+// Row-wise max and sum of exp over the 64 columns of a tile held as 16
+// values per lane (lanes c, c+16, c+32, c+48 hold one row).  Values of
+// columns at or past ncol (tail only) count as absent.  All four lanes of the
+// row receive the max m (-inf if no finite value) and s = sum exp(f - m)
+// (fp32, fixed order: within the lane in block order, then the xor-16 and
+// xor-32 butterflies).
+__device__ __forceinline__ void row64_max_sum(floatx4 (&v)[4], bool tail, int ncol, float* m_out, float* s_out)
+{
+    const int G = (threadIdx.x & 63) >> 4;
+    if (tail) {
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb)
+            if (vm_col(G, vb) >= ncol) v[vb] = floatx4{ -INFINITY, -INFINITY, -INFINITY, -INFINITY };
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, v[vb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float ml = row_mlog2(mx);
+    float s = 0.0f;
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += softmax_w(v[vb][i], ml);
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    *m_out = mx;
+    *s_out = s;
 }
 
 }  // namespace dspark

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T*
     }
     const float M = block_max(mloc, bs);
     // exp(x - M) is 0 for x = -inf; each 16-byte vector is summed in fp32, vectors in fp64.
-    const float ml = M * kLog2e;
+    const float ml = row_mlog2(M);
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
     const float* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int gamma, int V, int r, int nT,
-    int nM, double* __restrict__ rw, double* __restrict__ rp)
+    int nM, float2* __restrict__ rpart)
 {
     __shared__ __attribute__((aligned(16))) char lds[markov_lds_bytes<F32>()];
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -308,123 +308,148 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
             }
             sw = sum16(sw);
             sp = sum16(sp);
-            if ((lane & 15) == 0 && row < cnt) {
-                rw[(size_t)row * nT + tile] = sw;
-                rp[(size_t)row * nT + tile] = sp;
-            }
+            if ((lane & 15) == 0 && row < cnt) rpart[(size_t)row * nT + tile] = make_float2((float)sw, (float)sp);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Residual tiles, bf16: persistent workgroups of NW waves (dspark_tile.hpp)
-// over 64-column tiles; each LDS buffer holds the Bm tile, the rejected
-// rows' draft-logit tile and their target tile, all staged by DMA.
+// Residual tiles, bf16: persistent 8-wave workgroups over 64-column tiles in
+// vocabulary-major MFMA form (dspark_tile.hpp), the same pipeline as the
+// draft tile kernel: Bm tiles through four LDS buffers, the rejected rows'
+// draft logits (L) and target logits (T) loaded into registers one tile
+// ahead, and the per-tile sums staged in LDS.  (With the L and T registers,
+// holding a second tile's logits for a deferred epilogue would not fit the
+// register file.)  Loads per iteration and wave: the L and T rows of two
+// batch blocks (four load_row16) and the Bm DMA (wait_stage).
 // ---------------------------------------------------------------------------
-template <int NW, int KS>
-__global__ __launch_bounds__(64 * NW) void k_resid_tiles_bf16(
+constexpr int kResPartTiles = 12;
+
+template <int KS>
+__global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     const uint16_t* __restrict__ Tg, const uint16_t* __restrict__ L, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int gamma, int V, int r, int nT,
-    int nM, int S, double* __restrict__ rw, double* __restrict__ rp)
+    int nM, int S, float2* __restrict__ rpart)
 {
-    constexpr int R = 32 * NW;
-    constexpr int kRowBytes = R * kTrowBytes;
-    constexpr int kBuf = kBmTileBytes + 2 * kRowBytes;
-    __shared__ __attribute__((aligned(1024))) char buf0[kBuf];
-    __shared__ __attribute__((aligned(1024))) char buf1[kBuf];
-    __shared__ SplitLse sh_lse[R][2];
+    constexpr int NW = kTileWaves, R = kTileRows;
+    __shared__ __attribute__((aligned(1024))) char s0[kBmTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s1[kBmTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s2[kBmTileBytes];
+    __shared__ __attribute__((aligned(1024))) char s3[kBmTileBytes];
+    __shared__ unsigned long long stage[kResPartTiles][R];  // float2 pairs, stored as one 64-bit word each
 
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int mblk = lid % nM, slot = lid / nM;
-    const int cnt = *resid_count;
+    const int cntr = *resid_count;
     const int m0 = mblk * R;
-    if (m0 >= cnt || slot >= nT) return;  // uniform
-    const int w = wave_id(), lane = threadIdx.x & 63;
+    int t0, ts, cnt;
+    slot_tiles(slot, S, nT, &t0, &ts, &cnt);
+    if (m0 >= cntr || cnt <= 0) return;  // uniform
+    const int w = wave_id(), lane = threadIdx.x & 63, G = lane >> 4, c = lane & 15;
     const int mw = m0 + 32 * w;
-    const bool active = mw < cnt;
+    const bool active = mw < cntr;
 
     uint4 a[2][8];
+    const uint16_t* lrow[2];
+    const uint16_t* trow[2];
+    SplitLse ld[2], lt[2];
     {
         const uint16_t* arow[2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const ResidRow ra = resid_row(resid_list, accepted, min(mw + 16 * mb + (lane & 15), cnt - 1));
-            arow[mb] = A + (size_t)cond_token_v(x0, tok, ra.b, gamma, ra.ks, V) * r;
+        for (int bb = 0; bb < 2; ++bb) {
+            const ResidRow rr = resid_row(resid_list, accepted, min(mw + 16 * bb + c, cntr - 1));
+            arow[bb] = A + (size_t)cond_token_v(x0, tok, rr.b, gamma, rr.ks, V) * r;
+            lrow[bb] = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
+            trow[bb] = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
+            ld[bb] = split_lse(lse_d[(size_t)rr.b * gamma + rr.ks - 1]);
+            lt[bb] = split_lse(lse_t[(size_t)rr.b * gamma + rr.ks - 1]);
         }
         load_a_frags<2>(arow, r, a);
     }
-    int lidx[4], tidx[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const ResidRow rr = resid_row(resid_list, accepted, min(m0 + dma_row_of<NW>(t), cnt - 1));
-        lidx[t] = rr.b * gamma + rr.ks - 1;
-        tidx[t] = rr.b * (gamma + 1) + rr.ks - 1;
-    }
-    for (int i = threadIdx.x; i < R; i += 64 * NW) {
-        const int m = m0 + i;
-        SplitLse d{ 0.f, 0.f }, t{ 0.f, 0.f };
-        if (m < cnt) {
-            const ResidRow rr = resid_row(resid_list, accepted, m);
-            d = split_lse(lse_d[(size_t)rr.b * gamma + rr.ks - 1]);
-            t = split_lse(lse_t[(size_t)rr.b * gamma + rr.ks - 1]);
-        }
-        sh_lse[i][0] = d;
-        sh_lse[i][1] = t;
-    }
     const int nks = KS > 0 ? KS : (r + 31) / 32;
 
-    persistent_tiles(
-        slot, nT, S, buf0, buf1,
-        [&](int tile, char* buf) {
-            dma_bm_tile<NW>(Bm, V, r, tile * kTcols, 32 * nks, buf);
-            dma_row_tile<NW>(L, lidx, V, tile * kTcols, buf + kBmTileBytes);
-            dma_row_tile<NW>(Tg, tidx, V, tile * kTcols, buf + kBmTileBytes + kRowBytes);
-        },
-        [&](int tile, const char* buf) {
-            if (!active) return;
-            floatx4 acc[2][4];
+    auto load_lt = [&](int i, uint2 (&lv)[2][4], uint2 (&tv)[2][4]) {
+        const bool dummy = i >= cnt;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+        for (int bb = 0; bb < 2; ++bb) {
+            load_row16(lrow[bb], (t0 + i * ts) * kTcols, V, dummy, lv[bb]);
+            load_row16(trow[bb], (t0 + i * ts) * kTcols, V, dummy, tv[bb]);
+        }
+    };
+    auto dma = [&](int i, char* buf) { dma_bm_tile<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf); };
+
+    // Row sums of tile i from its logits f (accumulators) and target values.
+    auto epilogue = [&](int i, const floatx4 (&f)[4][2], const uint2 (&tv)[2][4]) {
+        const int n0 = (t0 + i * ts) * kTcols;
+        const bool tail = n0 + kTcols > V;
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = floatx4{ 0.f, 0.f, 0.f, 0.f };
-            tile_mma64<2, KS>(a, buf, nks, acc);
-            const int n0 = tile * kTcols;
-            const int nl = lane & 15;
-            const bool tail = n0 + kTcols > V;
+        for (int bb = 0; bb < 2; ++bb) {
+            float sw = 0.0f, sp = 0.0f;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                floatx4 tv[4];
+            for (int vb = 0; vb < 4; ++vb) {
+                const floatx4 t = bf16x4_to_f32(tv[bb][vb]);
+                const bool ok = !tail || n0 + vm_col(G, vb) < V;
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    acc[mb][nb] += row_vals(buf + kBmTileBytes, 32 * w + 16 * mb, nb);
-                    tv[nb] = row_vals(buf + kBmTileBytes + kRowBytes, 32 * w + 16 * mb, nb);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int lr = 32 * w + 16 * mb + 4 * (lane >> 4) + i;
-                    const SplitLse ld = sh_lse[lr][0], ltg = sh_lse[lr][1];
-                    double sw = 0.0, sp = 0.0;
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
-                        float ptv;
-                        float wr = resid_weight(acc[mb][nb][i], tv[nb][i], ld, ltg, &ptv);
-                        if (tail && n0 + 16 * nb + nl >= V) wr = ptv = 0.0f;
-                        sw += (double)wr;
-                        sp += (double)ptv;
-                    }
-                    sw = sum16(sw);
-                    sp = sum16(sp);
-                    const int row = m0 + lr;
-                    if (nl == 0 && row < cnt) {
-                        rw[(size_t)row * nT + tile] = sw;
-                        rp[(size_t)row * nT + tile] = sp;
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    float ptv;
+                    const float wr = resid_weight(f[vb][bb][e], t[e], ld[bb], lt[bb], &ptv);
+                    sw += ok ? wr : 0.0f;
+                    sp += ok ? ptv : 0.0f;
                 }
             }
-        },
-        [&]() {});
+            sw += __shfl_xor(sw, 16, 64);
+            sw += __shfl_xor(sw, 32, 64);
+            sp += __shfl_xor(sp, 16, 64);
+            sp += __shfl_xor(sp, 32, 64);
+            if (G == bb) stage[i][32 * w + 16 * bb + c] = pack_f2(sw, sp);
+        }
+    };
+    uint2 lc[2][4], tc[2][4], ln[2][4], tn[2][4];
+    auto body = [&](int i, const char* cur, char* nxt) {
+        wait_stage<4 * kRow16Loads, 32 / NW>(i);
+        barrier_lds();  // Bm tile i has landed in cur; every wave is done with nxt
+        load_lt(i + 1, ln, tn);
+        dma(i + 3, nxt);
+        if (active) {
+            floatx4 acc[4][2];
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(lc[bb][vb]);
+            tile_mma_vm<2, KS>(a, cur, nks, acc);
+            epilogue(i, acc, tc);
+        }
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb) {
+                lc[bb][vb] = ln[bb][vb];
+                tc[bb][vb] = tn[bb][vb];
+            }
+    };
+
+    load_lt(0, lc, tc);
+    dma(0, s0);
+    dma(1, s1);
+    dma(2, s2);
+    for (int i = 0;;) {
+        body(i, s0, s3);
+        if (++i >= cnt) break;
+        body(i, s1, s0);
+        if (++i >= cnt) break;
+        body(i, s2, s1);
+        if (++i >= cnt) break;
+        body(i, s3, s2);
+        if (++i >= cnt) break;
+    }
+    wait_all_mem();
+    __syncthreads();
+    for (int e = threadIdx.x; e < R * cnt; e += 64 * NW) {
+        const int row = e / cnt, i = e - row * cnt;
+        if (m0 + row < cntr) rpart[(size_t)(m0 + row) * nT + t0 + i * ts] = unpack_f2(stage[i][row]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -435,9 +460,9 @@ __global__ __launch_bounds__(kThreads) void k_final(
     const typename DT::T* __restrict__ Tg, const typename DT::T* __restrict__ L, const typename DT::T* __restrict__ A,
     const typename DT::T* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ len,
-    const int32_t* __restrict__ accepted, const int32_t* __restrict__ resid_idx, const double* __restrict__ rw,
-    const double* __restrict__ rp, const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V,
-    int r, int nT, int nC, uint64_t seed, int32_t* __restrict__ out_tok)
+    const int32_t* __restrict__ accepted, const int32_t* __restrict__ resid_idx, const float2* __restrict__ rpart,
+    const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC,
+    uint64_t seed, int32_t* __restrict__ out_tok)
 {
     typedef typename DT::T T;
     typedef TileTraits<DT> TT;
@@ -455,42 +480,59 @@ __global__ __launch_bounds__(kThreads) void k_final(
         // ---- residual at the first rejected position ks -------------------
         const int ks = a + 1;
         const int m = resid_idx[b];
-        const double* w = rw + (size_t)m * nT;
-        const double* p = rp + (size_t)m * nT;
+        const float2* rq = rpart + (size_t)m * nT;
         // Total residual mass decides between the residual and its p_t fallback.
         double sloc = 0.0;
         {
             const int per = (nT + kThreads - 1) / kThreads;
             const int i0 = min(t * per, nT), i1 = min(i0 + per, nT);
-            for (int i = i0; i < i1; ++i) sloc += w[i];
+            for (int i = i0; i < i1; ++i) sloc += (double)rq[i].x;
         }
         const bool degen = !(block_sum(sloc, bs) > 0.0);
-        const double* src = degen ? p : w;
         const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)ks, 2u);
-        const Located loc = locate(nT, [&](int i) { return src[i]; }, u, bs, &sh_cprev);
+        const Located loc = locate(
+            nT, [&](int i) { const float2 q = rq[i]; return (double)(degen ? q.y : q.x); }, u, bs, &sh_cprev);
 
         const int n0 = loc.idx * TT::kCols;
         const T* trow = Tg + ((size_t)b * (gamma + 1) + (ks - 1)) * V;
-        float f[TT::kNB];
-        row_tile_f(L + ((size_t)b * gamma + (ks - 1)) * V, A, Bm, cond_token_v(x0, tok, b, gamma, ks, V), V, r, n0,
-                   lds, f);
-        if ((t >> 6) == 0) {
-            const SplitLse ld = split_lse(lse_d[(size_t)b * gamma + ks - 1]);
-            const SplitLse lt = split_lse(lse_t[(size_t)b * gamma + ks - 1]);
-            double wv[TT::kNB];
+        const T* lrow = L + ((size_t)b * gamma + (ks - 1)) * V;
+        const int prev = cond_token_v(x0, tok, b, gamma, ks, V);
+        const SplitLse ld = split_lse(lse_d[(size_t)b * gamma + ks - 1]);
+        const SplitLse lt = split_lse(lse_t[(size_t)b * gamma + ks - 1]);
+        auto weight = [&](float fv, float tv) {
+            float ptv;
+            const float wr = resid_weight(fv, tv, ld, lt, &ptv);
+            return (double)(degen ? ptv : wr);
+        };
+        if constexpr (std::is_same<DT, Bf16>::value) {
+            floatx4 f[4];
+            row_tile_vm(lrow, A, Bm, prev, V, r, n0, lds, f);
+            if ((t >> 6) == 0) {
+                uint2 tv[4];
+                load_row16(trow, n0, V, false, tv);
+                floatx4 tf[4];
 #pragma unroll
-            for (int nb = 0; nb < TT::kNB; ++nb) {
-                const int col = n0 + 16 * nb + (lane & 15);
-                wv[nb] = 0.0;
-                if (col < V) {
-                    float ptv;
-                    const float wr = resid_weight(f[nb], DT::to_f32(trow[col]), ld, lt, &ptv);
-                    wv[nb] = (double)(degen ? ptv : wr);
-                }
+                for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(tv[vb]);
+                double wsel;
+                const int j = scan_vm_tile(
+                    n0, m, 1.0, loc.cprev, loc.tau,
+                    [&](int vb, int i, int col) { return col < V ? weight(f[vb][i], tf[vb][i]) : 0.0; }, &wsel);
+                if (lane == 0) sh_tok = clamp_tok(n0 + j, V);
             }
-            double wsel;
-            const int j = scan_tile_weights<TT::kNB>(wv, 1.0, loc.cprev, loc.tau, &wsel);
-            if (lane == 0) sh_tok = clamp_tok(n0 + j, V);
+        } else {
+            float f[TT::kNB];
+            row_tile_f(lrow, A, Bm, prev, V, r, n0, lds, f);
+            if ((t >> 6) == 0) {
+                double wv[TT::kNB];
+#pragma unroll
+                for (int nb = 0; nb < TT::kNB; ++nb) {
+                    const int col = n0 + 16 * nb + (lane & 15);
+                    wv[nb] = col < V ? weight(f[nb], DT::to_f32(trow[col])) : 0.0;
+                }
+                double wsel;
+                const int j = scan_tile_weights<TT::kNB>(wv, 1.0, loc.cprev, loc.tau, &wsel);
+                if (lane == 0) sh_tok = clamp_tok(n0 + j, V);
+            }
         }
     } else {
         // ---- bonus token from target row l (position l + 1) ----------------
@@ -506,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void k_final(
 
         // rescan the chunk in index order: 32 contiguous elements per thread
         const float mc = pm[loc.idx];
-        const float mcl = mc * kLog2e;
+        const float mcl = row_mlog2(mc);
         const double scale = tile_mass(mc, 1.0, M);
         const T* x = Tg + ((size_t)b * (gamma + 1) + l) * V;
         constexpr int EPT = kChunkElems / kThreads;  // 32
@@ -544,6 +586,152 @@ __global__ __launch_bounds__(kThreads) void k_final(
         out_tok[(size_t)b * (gamma + 1) + kk] = kk < a ? tok[(size_t)b * gamma + kk] : (kk == a ? token : -1);
 }
 
+// ---------------------------------------------------------------------------
+// Final token, bf16: one wave per request.  Residual: the residual tile sums
+// are located with wave scans and the chosen tile is recomputed by the wave
+// from its own LDS copy of the Bm tile (row_tile_vm_wave), in the MFMA batch
+// column the row had in the residual pass.  Bonus: the target chunk is
+// located from the chunk partials; each lane sums the weights of 128
+// contiguous elements of the chunk, the lane slice holding the crossing is
+// found by a wave scan, and that slice is rescanned two elements per lane.
+// ---------------------------------------------------------------------------
+template <int KS, int PER>
+__global__ __launch_bounds__(64) void k_final_bf16(
+    const uint16_t* __restrict__ Tg, const uint16_t* __restrict__ L, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
+    const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ len,
+    const int32_t* __restrict__ accepted, const int32_t* __restrict__ resid_idx, const float2* __restrict__ rpart,
+    const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC,
+    uint64_t seed, int32_t* __restrict__ out_tok)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int l = clamp_len(len[b], gamma);
+    const int a = accepted[b];
+    int token;
+
+    if (a < l) {
+        // ---- residual at the first rejected position ks -------------------
+        const int ks = a + 1;
+        const int m = resid_idx[b];
+        float2 q[PER];
+        int i0;
+        load_slices<PER>(rpart + (size_t)m * nT, nT, make_float2(0.0f, 0.0f), q, &i0);
+        uint4 af[1][8];
+        {
+            const uint16_t* arow[1] = { A + (size_t)cond_token_v(x0, tok, b, gamma, ks, V) * r };
+            load_a_frags<1>(arow, r, af);
+        }
+        float sw = 0.0f;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) sw += q[j].x;
+        const bool degen = !(wave_last(wave_incl_scan((double)sw)) > 0.0);  // no residual mass: sample p_t
+        const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)ks, 2u);
+        const Located loc = wave_locate_slices<PER>(
+            i0, [&](int j) { return (double)(degen ? q[j].y : q[j].x); }, u);
+
+        const int n0 = loc.idx * kTcols;
+        const uint16_t* trow = Tg + ((size_t)b * (gamma + 1) + (ks - 1)) * V;
+        uint2 tv[4];
+        load_row16(trow, n0, V, false, tv);
+        floatx4 f[4];
+        row_tile_vm_wave<KS>(L + ((size_t)b * gamma + (ks - 1)) * V, af, Bm, V, r, n0, lds, f);
+        const SplitLse ld = split_lse(lse_d[(size_t)b * gamma + ks - 1]);
+        const SplitLse lt = split_lse(lse_t[(size_t)b * gamma + ks - 1]);
+        floatx4 tf[4];
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(tv[vb]);
+        double wsel;
+        const int j = scan_vm_tile(
+            n0, m, 1.0, loc.cprev, loc.tau,
+            [&](int vb, int i, int col) {
+                if (col >= V) return 0.0;
+                float ptv;
+                const float wr = resid_weight(f[vb][i], tf[vb][i], ld, lt, &ptv);
+                return (double)(degen ? ptv : wr);
+            },
+            &wsel);
+        token = clamp_tok(n0 + j, V);
+    } else {
+        // ---- bonus token from target row l (position l + 1) ----------------
+        const float* pm = bm + (size_t)b * nC;
+        const double* ps = bsum + (size_t)b * nC;
+        float mloc = -INFINITY;
+        for (int c = lane; c < nC; c += 64) mloc = fmaxf(mloc, pm[c]);
+        const float M = wave_max(mloc);
+        const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)(l + 1), 3u);
+        // nC <= 64 * 4 chunks (lengths up to 2^21), slices of at most 4 per lane.
+        const int cper = (nC + 63) / 64, c0l = lane * cper;
+        float cm[4];
+        double cs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ci = min(c0l + j, nC - 1);
+            const bool ok = j < cper && c0l + j < nC;
+            cm[j] = ok ? pm[ci] : -INFINITY;
+            cs[j] = ok ? ps[ci] : 0.0;
+        }
+        const Located loc = wave_locate_slices<4>(c0l, [&](int j) { return tile_mass(cm[j], cs[j], M); }, u);
+
+        const float mc = pm[loc.idx];
+        const float mcl = row_mlog2(mc);
+        const double scale = tile_mass(mc, 1.0, M);
+        const uint16_t* x = Tg + ((size_t)b * (gamma + 1) + l) * V;
+        constexpr int EPL = kChunkElems / 64;  // 128 elements per lane
+        const int c0 = loc.idx * kChunkElems;
+        auto w_of = [&](int e, float xv) { return e < V && mc != -INFINITY ? (double)softmax_w(xv, mcl) : 0.0; };
+        // Pass 1: lane totals over contiguous 128-element slices (16-byte
+        // loads, all in flight at once).
+        const int e0 = c0 + lane * EPL;
+        uint4 xv[EPL / 8];
+#pragma unroll
+        for (int qv = 0; qv < EPL / 8; ++qv) xv[qv] = ld16(x + min(e0 + 8 * qv, V - 8));
+        double tl = 0.0;
+#pragma unroll
+        for (int qv = 0; qv < EPL / 8; ++qv) {
+            float tv = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) tv += (float)w_of(e0 + 8 * qv + jj, Bf16::get(xv[qv], jj));
+            tl += (double)tv;
+        }
+        const double inc = wave_incl_scan(tl);
+        const double off = wave_excl_from_incl(inc);
+        const uint64_t mh = __ballot(tl > 0.0 && loc.cprev + scale * inc > loc.tau);
+        const uint64_t mp = __ballot(tl > 0.0);
+        int src;
+        if (mh) src = __builtin_ctzll(mh);
+        else if (mp) src = 63 - __builtin_clzll(mp);
+        else src = 0;
+        // Pass 2: the chosen slice, two elements per lane, scanned in index order.
+        const double base = __shfl(off, src, 64);
+        const int s0 = c0 + src * EPL + 2 * lane;
+        const double w0 = s0 < V ? w_of(s0, Bf16::to_f32(x[s0])) : 0.0;
+        const double w1 = s0 + 1 < V ? w_of(s0 + 1, Bf16::to_f32(x[s0 + 1])) : 0.0;
+        const double pin = wave_incl_scan(w0 + w1);
+        const double pex = pin - (w0 + w1);
+        const double r0 = base + pex + w0, r1 = base + pex + w0 + w1;
+        const bool h0 = loc.cprev + scale * r0 > loc.tau, h1 = loc.cprev + scale * r1 > loc.tau;
+        const uint64_t ch = __ballot(h0 || h1);
+        const uint64_t cp = __ballot(w0 > 0.0 || w1 > 0.0);
+        int e;
+        if (ch) {
+            const int sl = __builtin_ctzll(ch);
+            const int which = __shfl((int)(h0 ? 0 : 1), sl, 64);
+            e = c0 + src * EPL + 2 * sl + which;
+        } else if (cp) {
+            const int sl = 63 - __builtin_clzll(cp);
+            const int which = __shfl((int)(w1 > 0.0 ? 1 : 0), sl, 64);
+            e = c0 + src * EPL + 2 * sl + which;
+        } else {
+            e = 0;
+        }
+        token = clamp_tok(e, V);
+    }
+    for (int kk = lane; kk <= gamma; kk += 64)
+        out_tok[(size_t)b * (gamma + 1) + kk] = kk < a ? tok[(size_t)b * gamma + kk] : (kk == a ? token : -1);
+}
+
 template <class DT>
 static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, const void* Bm_, const int32_t* x0,
                            const int32_t* tok, const float* pd, const double* lse_d, const int32_t* len, int B,
@@ -563,8 +751,7 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     int32_t* ridx = reinterpret_cast<int32_t*>(w + lay.resid_idx);
     int32_t* rlist = reinterpret_cast<int32_t*>(w + lay.resid_list);
     int32_t* rcnt = reinterpret_cast<int32_t*>(w + lay.resid_count);
-    double* rw = reinterpret_cast<double*>(w + lay.res_w);
-    double* rp = reinterpret_cast<double*>(w + lay.res_p);
+    float2* rpart = reinterpret_cast<float2*>(w + lay.res_part);
     float* bm = reinterpret_cast<float*>(w + lay.bon_m);
     double* bsum = reinterpret_cast<double*>(w + lay.bon_s);
     const int nT = n_tiles(std::is_same<DT, Bf16>::value ? 1 : 0, V), nC = n_chunks(V);
@@ -581,20 +768,19 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     prof_end(K_ACCEPT, s);
     prof_begin(K_RESID_TILES, s);
     if (std::is_same<DT, Bf16>::value) {
-        constexpr int NW = 4;
-        const int nM = (B + 32 * NW - 1) / (32 * NW);
-        const int S = std::min(nT, (cu_count() + nM - 1) / nM);
-        auto kern = (r + 31) / 32 == 8 ? k_resid_tiles_bf16<NW, 8> : k_resid_tiles_bf16<NW, 0>;
-        hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * NW), 0, s,
+        const int nM = (B + kTileRows - 1) / kTileRows;
+        const int S = std::min(nT, std::max((cu_count() + nM - 1) / nM, (nT + kResPartTiles - 1) / kResPartTiles));
+        auto kern = (r + 31) / 32 == 8 ? k_resid_tiles_bf16<8> : k_resid_tiles_bf16<0>;
+        hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s,
                            reinterpret_cast<const uint16_t*>(Tg), reinterpret_cast<const uint16_t*>(L),
                            reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(Bm), x0, tok,
-                           lse_d, lse_t, accepted, rlist, rcnt, gamma, V, r, nT, nM, S, rw, rp);
+                           lse_d, lse_t, accepted, rlist, rcnt, gamma, V, r, nT, nM, S, rpart);
     } else {
         const int nM = (B + 255) / 256;
         hipLaunchKernelGGL(k_resid_tiles_f32, dim3(nT * nM), dim3(kThreads), 0, s,
                            reinterpret_cast<const float*>(Tg), reinterpret_cast<const float*>(L),
                            reinterpret_cast<const float*>(A), reinterpret_cast<const float*>(Bm), x0, tok, lse_d,
-                           lse_t, accepted, rlist, rcnt, gamma, V, r, nT, nM, rw, rp);
+                           lse_t, accepted, rlist, rcnt, gamma, V, r, nT, nM, rpart);
     }
     prof_end(K_RESID_TILES, s);
     prof_begin(K_BONUS_PARTIALS, s);
@@ -602,8 +788,18 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
                        bm, bsum);
     prof_end(K_BONUS_PARTIALS, s);
     prof_begin(K_FINAL, s);
-    hipLaunchKernelGGL(k_final<DT>, dim3(B), dim3(kThreads), 0, s, Tg, L, A, Bm, x0, tok, lse_d, lse_t, len, accepted,
-                       ridx, rw, rp, bm, bsum, gamma, V, r, nT, nC, seed, out_tok);
+    if (std::is_same<DT, Bf16>::value && nT <= 64 * 64 && nC <= 64 * 4) {
+        const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32;
+        auto kern = small ? (k8 ? k_final_bf16<8, 32> : k_final_bf16<0, 32>)
+                          : (k8 ? k_final_bf16<8, 64> : k_final_bf16<0, 64>);
+        hipLaunchKernelGGL(kern, dim3(B), dim3(64), 0, s, reinterpret_cast<const uint16_t*>(Tg),
+                           reinterpret_cast<const uint16_t*>(L), reinterpret_cast<const uint16_t*>(A),
+                           reinterpret_cast<const uint16_t*>(Bm), x0, tok, lse_d, lse_t, len, accepted, ridx, rpart, bm,
+                           bsum, gamma, V, r, nT, nC, seed, out_tok);
+    } else {
+        hipLaunchKernelGGL(k_final<DT>, dim3(B), dim3(kThreads), 0, s, Tg, L, A, Bm, x0, tok, lse_d, lse_t, len,
+                           accepted, ridx, rpart, bm, bsum, gamma, V, r, nT, nC, seed, out_tok);
+    }
     prof_end(K_FINAL, s);
     return hipGetLastError();
 }

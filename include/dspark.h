@@ -23,7 +23,10 @@
  *   - Positions are 1-based, k = 1..gamma; array index k-1.
  *   - dtype: DSPARK_BF16 (bfloat16 logits and Markov factors) or DSPARK_F32;
  *     logits L, target logits Tgt, A and Bm share it.  All arithmetic is at
- *     least fp32; probability masses are summed in fp64.
+ *     least fp32: the rank-r product accumulates in fp32, exponentials are
+ *     fp32, sums within a 64-column (bf16) or 128-column (fp32) tile or a
+ *     16-byte vector are fp32, and sums across tiles, chunks and vectors are
+ *     fp64.
  *   - Limits: 1 <= gamma <= 16; B*gamma <= 16384; V a multiple of 8 in
  *     [8, 2^24]; r a multiple of 8 in [8, 256].  L, Tgt, A and Bm must be
  *     16-byte aligned.  B == 0 is a no-op that returns DSPARK_OK.
