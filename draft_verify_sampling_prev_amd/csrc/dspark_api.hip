@@ -42,7 +42,7 @@ WsLayout ws_layout(int B, int gamma, int V)
     l.lse_t = take(Bz * G * 8);
     l.pt = take(Bz * G * 8);
     l.resid_idx = take(Bz * 4);
-    l.resid_list = take(Bz * 4);
+    l.resid_list = take(Bz * 16);
     l.resid_count = take(4);
     l.res_part = take(Bz * nT * 8);
     l.bon_m = take(Bz * nC * 4);

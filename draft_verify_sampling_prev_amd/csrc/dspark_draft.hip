@@ -148,8 +148,8 @@ constexpr int kPartTiles = 12;  // tiles per slot whose partials fit the LDS sta
 template <int KS>
 __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
-    const int32_t* __restrict__ x0, const int32_t* tok, int B, int gamma, int V, int r, int k, int nT, int nM, int S,
-    float2* __restrict__ part)
+    const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, int B, int gamma, int V, int r, int k, int nT,
+    int nM, int S, float2* __restrict__ part)
 {
     constexpr int NW = kTileWaves, R = kTileRows;
     __shared__ __attribute__((aligned(1024))) char s0[kBmTileBytes];
@@ -168,21 +168,13 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     const int mw = m0 + 32 * w;  // first row of this wave
     const bool active = mw < B;
 
-    uint4 a[2][8];
+    uint4 a[2][8];  // B operand: the rows' A vectors (loaded in the prologue)
     const uint16_t* lrow[2];
-    {
-        const uint16_t* arow[2];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int row = min(mw + 16 * bb + c, B - 1);
-            arow[bb] = A + (size_t)cond_token(x0, tok, row, gamma, k, V) * r;
-            lrow[bb] = L + ((size_t)row * gamma + (k - 1)) * V;
-        }
-        load_a_frags<2>(arow, r, a);
-    }
+    for (int bb = 0; bb < 2; ++bb) lrow[bb] = L + ((size_t)min(mw + 16 * bb + c, B - 1) * gamma + (k - 1)) * V;
     const int nks = KS > 0 ? KS : (r + 31) / 32;
 
-    auto load_l = [&](int i, uint2 (&lv)[2][4]) {
+    auto load_l = [&](int i, uint4 (&lv)[2][2]) {
         const bool dummy = i >= cnt;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) load_row16(lrow[bb], (t0 + i * ts) * kTcols, V, dummy, lv[bb]);
@@ -204,18 +196,31 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
             if (G == bb) stage[prev][32 * w + 16 * bb + c] = pack_f2(m, sum);
         }
     };
-    uint2 lc[2][4], ln[2][4];
-    auto body = [&](int i, const char* cur, char* nxt) {
-        wait_stage<2 * kRow16Loads, 32 / NW>(i);
+    // L values of two tiles in flight: the four unrolled bodies alternate
+    // between two register sets, so no copy waits on a load just issued.
+    uint4 l0[2][2], l1[2][2];
+    auto body = [&](int i, const char* cur, char* nxt, uint4 (&lc)[2][2], uint4 (&ln)[2][2]) {
+        if (KS > 0) wait_stage<2 * kRow16Loads, 32 / NW, 16>(i);
+        else if (i == 0) wait_all_mem();  // run-time rank: the A-operand load count varies
+        else wait_stage<2 * kRow16Loads, 32 / NW, 16>(i);
         barrier_lds();  // Bm tile i has landed in cur; every wave is done with nxt (tile i-1)
+        issue_fence();
         load_l(i + 1, ln);
+        issue_fence();
+        if (i == 0) {  // ramp-up: tiles 1 and 2 (buffers s1, s2) behind tile 3
+            dma(1, s1);
+            issue_fence();
+            dma(2, s2);
+            issue_fence();
+        }
         dma(i + 3, nxt);
+        issue_fence();
         if (active) {
             floatx4 acc[4][2];
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-                for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(lc[bb][vb]);
+                for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(row16_block(lc[bb], vb));
             // The epilogue of the previous tile is independent of these
             // MFMAs.  Waves 0-3 and 4-7 take the two phases in opposite
             // order, so each SIMD (one wave of each half) has one wave on the
@@ -235,24 +240,32 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
                 for (int bb = 0; bb < 2; ++bb) fprev[vb][bb] = acc[vb][bb];
             prev = i;
         }
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int vb = 0; vb < 4; ++vb) lc[bb][vb] = ln[bb][vb];
     };
 
-    load_l(0, lc);
+    // Prologue: the conditioning tokens are loaded first (the oldest loads,
+    // so waiting for them does not wait for the tile loads behind them), then
+    // only the first tile, then the A-operand gather.
+    int tk[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) tk[bb] = cond_token(x0, tok, min(mw + 16 * bb + c, B - 1), gamma, k, V);
+    issue_fence();
+    load_l(0, l0);
+    issue_fence();
     dma(0, s0);
-    dma(1, s1);
-    dma(2, s2);
+    issue_fence();
+    {
+        const uint16_t* arow[2] = { A + (size_t)tk[0] * r, A + (size_t)tk[1] * r };
+        load_a_frags<2>(arow, r, a);
+    }
+    issue_fence();
     for (int i = 0;;) {
-        body(i, s0, s3);
+        body(i, s0, s3, l0, l1);
         if (++i >= cnt) break;
-        body(i, s1, s0);
+        body(i, s1, s0, l1, l0);
         if (++i >= cnt) break;
-        body(i, s2, s1);
+        body(i, s2, s1, l0, l1);
         if (++i >= cnt) break;
-        body(i, s3, s2);
+        body(i, s3, s2, l1, l0);
         if (++i >= cnt) break;
     }
     epilogue();

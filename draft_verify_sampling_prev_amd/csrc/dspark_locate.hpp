@@ -150,7 +150,7 @@ __device__ __forceinline__ void row_tile_vm(const uint16_t* L_row, const uint16_
     const int nks = (r + 31) / 32;
     dma_bm_tile<kThreads / 64>(Bm, V, r, n0, false, lds);
     uint4 a[1][8];
-    uint2 lv[4];
+    uint4 lv[2];
     if (w0) {
         const uint16_t* arow[1] = { A + (size_t)prev * r };
         load_a_frags<1>(arow, r, a);
@@ -161,7 +161,7 @@ __device__ __forceinline__ void row_tile_vm(const uint16_t* L_row, const uint16_
     if (w0) {
         floatx4 acc[4][1];
 #pragma unroll
-        for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(lv[vb]);
+        for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(row16_block(lv, vb));
         if (nks == 8) tile_mma_vm<1, 8>(a, lds, nks, acc);
         else tile_mma_vm<1, 0>(a, lds, nks, acc);
 #pragma unroll
@@ -179,12 +179,12 @@ __device__ __forceinline__ void row_tile_vm_wave(const uint16_t* L_row, const ui
                                                  int V, int r, int n0, char* lds, floatx4 (&f)[4])
 {
     dma_bm_tile<1>(Bm, V, r, n0, false, lds);
-    uint2 lv[4];
+    uint4 lv[2];
     load_row16(L_row, n0, V, false, lv);
     wait_all_mem();
     floatx4 acc[4][1];
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(lv[vb]);
+    for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(row16_block(lv, vb));
     tile_mma_vm<1, KS>(a, lds, (r + 31) / 32, acc);
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb) f[vb] = acc[vb][0];

@@ -134,7 +134,10 @@ __device__ __forceinline__ void load_a_frags(const uint16_t* const (&arow)[NBB],
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int k = 32 * ks + kq8;
-            a[bb][ks] = k < r ? ld16(arow[bb] + k) : make_uint4(0u, 0u, 0u, 0u);
+            // Branch-free (a fixed number of loads): k >= r reads a valid
+            // address and is replaced by zeros.
+            const uint4 v = ld16(arow[bb] + min(k, r - 8));
+            a[bb][ks] = k < r ? v : make_uint4(0u, 0u, 0u, 0u);
         }
 }
 
@@ -148,27 +151,30 @@ __device__ __forceinline__ floatx4 bf16x4_to_f32(uint2 v)
 __device__ __forceinline__ uint2 ld8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
 // Load the 16 values of one row that lane group G holds in a tile starting
-// at column n0, in accumulator-block order: v[vb] = columns n0 + vm_col(G, vb)
-// .. +3.  Two 16-byte loads of columns n0 + 16G .. +15; for odd G the two
-// 8-byte halves of each load are swapped (vm_col's XOR).  A load at or past V
-// reads a clamped (valid) address; `dummy` reads the row start (fixed load
-// count past the last tile).
+// at column n0: raw[h] = columns n0 + 16G + 8h .. +7 (two 16-byte loads).  A
+// load at or past V reads a clamped (valid) address; `dummy` reads the row
+// start (fixed load count past the last tile).  The values are used through
+// row16_block, after the loads have been waited for: doing the lane-dependent
+// rearrangement here would make the compiler wait for the loads at once.
 constexpr int kRow16Loads = 2;  // vector-memory loads issued by one load_row16
 
 __device__ __forceinline__ void load_row16(const uint16_t* __restrict__ row, int n0, int V, bool dummy,
-                                           uint2 (&v)[4])
+                                           uint4 (&raw)[2])
 {
     const int G = (threadIdx.x & 63) >> 4;
     const int keep = dummy ? 0 : -1;  // branch-free: a dummy reads the row start
-    const bool odd = (G & 1) != 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int col = min(n0 + 16 * G + 8 * h, V - 8) & keep;
-        const uint4 x = ld16(row + col);
-        const uint2 lo = make_uint2(x.x, x.y), hi = make_uint2(x.z, x.w);
-        v[2 * h] = odd ? hi : lo;
-        v[2 * h + 1] = odd ? lo : hi;
-    }
+    for (int h = 0; h < 2; ++h) raw[h] = ld16(row + (min(n0 + 16 * G + 8 * h, V - 8) & keep));
+}
+
+// Columns n0 + vm_col(G, vb) .. +3 (accumulator block vb) from load_row16's
+// registers: for odd G the two 8-byte halves of each 16-byte load trade places.
+__device__ __forceinline__ uint2 row16_block(const uint4 (&raw)[2], int vb)
+{
+    const bool odd = (((threadIdx.x & 63) >> 4) & 1) != 0;
+    const uint4 x = raw[vb >> 1];
+    const bool high = ((vb & 1) != 0) != odd;
+    return high ? make_uint2(x.z, x.w) : make_uint2(x.x, x.y);
 }
 
 template <int NBB, int KS>
@@ -221,21 +227,29 @@ template <int N> __device__ __forceinline__ void wait_vmem()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Stage wait of the tile pipelines.  Issue order per wave: prologue
-// [rows(0)] [Bm(0)] [Bm(1)] [Bm(2)], then iteration i issues [rows(i+1)]
-// [Bm(i+3)] after its barrier, where rows(.) is NL register loads and Bm(.)
-// is ND DMA instructions, always issued (dummies past the last tile).  Before
-// the barrier of iteration i this wave's Bm(i) must have landed; the loads
-// issued after it number 2ND (i = 0), 2ND + NL (i = 1), 2(NL + ND) (i >= 2).
-// Vector-memory loads complete in order, so waiting until at most that many
-// are outstanding is exact.
-template <int NL, int ND>
+// Stage wait of the tile pipelines, whose prefetch ramps up: the prologue
+// issues [rows(0)] [Bm(0)] [NA other loads]; iteration 0 issues, after its
+// barrier, [rows(1)] [Bm(1)] [Bm(2)] [Bm(3)]; iteration i >= 1 issues
+// [rows(i+1)] [Bm(i+3)].  rows(.) is NL register loads and Bm(.) is ND DMA
+// instructions, always issued (dummies past the last tile).  (Asking for only
+// the first tile up front lets it arrive before the rest of the launch-wide
+// burst of prefetches.)  Before the barrier of iteration i this wave's Bm(i)
+// must have landed; the loads issued after it number NA (i = 0), 2ND (i = 1),
+// 2ND + NL (i = 2) and 2(NL + ND) (i >= 3).  Vector-memory loads complete in
+// order, so waiting until at most that many are outstanding is exact.
+template <int NL, int ND, int NA>
 __device__ __forceinline__ void wait_stage(int i)
 {
-    if (i >= 2) wait_vmem<2 * (NL + ND)>();
-    else if (i == 1) wait_vmem<2 * ND + NL>();
-    else wait_vmem<2 * ND>();
+    if (i >= 3) wait_vmem<2 * (NL + ND)>();
+    else if (i == 2) wait_vmem<2 * ND + NL>();
+    else if (i == 1) wait_vmem<2 * ND>();
+    else wait_vmem<NA>();
 }
+
+// Scheduling fence: the compiler moves no instruction across it.  The tile
+// pipelines put one between consecutive groups of loads, so the loads are
+// issued in program order -- the order wait_stage's counts assume.
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Workgroup barrier without a memory fence.  __syncthreads() also waits for
 // every outstanding vector-memory load of the wave (its release fence), which

@@ -174,11 +174,13 @@ __global__ __launch_bounds__(kThreads) void k_target_lse(const typename DT::T* _
 constexpr int kAcceptThreads = 1024;
 
 __global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restrict__ pd, const int32_t* __restrict__ len,
-                                                           const double* __restrict__ pt, int B, int gamma,
+                                                           const double* __restrict__ pt,
+                                                           const int32_t* __restrict__ x0,
+                                                           const int32_t* __restrict__ tok, int B, int gamma,
                                                            uint64_t seed, int32_t* __restrict__ accepted,
                                                            int32_t* __restrict__ n_out, float* __restrict__ target_p,
                                                            int32_t* __restrict__ resid_idx,
-                                                           int32_t* __restrict__ resid_list,
+                                                           int4* __restrict__ resid_list,
                                                            int32_t* __restrict__ resid_count)
 {
     __shared__ int wsum[kAcceptThreads / 64];
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restri
     __syncthreads();
     for (int b0 = 0; b0 < B; b0 += kAcceptThreads) {
         const int b = b0 + t;
-        int rej = 0;
+        int rej = 0, accepted_b = 0;
         if (b < B) {
             const int l = clamp_len(len[b], gamma);
             int a = l;
@@ -205,6 +207,7 @@ __global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restri
                 }
             }
             accepted[b] = a;
+            accepted_b = a;
             n_out[b] = a + 1;
             rej = a < l;
         }
@@ -225,7 +228,11 @@ __global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restri
         const int idx = off + inc - rej;
         if (b < B) {
             resid_idx[b] = rej ? idx : -1;
-            if (rej) resid_list[idx] = b;
+            if (rej) {
+                const int ks = accepted_b + 1;
+                const int xprev = ks == 1 ? x0[b] : tok[(size_t)b * gamma + ks - 2];
+                resid_list[idx] = make_int4(b, ks, xprev, 0);
+            }
         }
         __syncthreads();
         if (t == 0) base += tot;
@@ -234,16 +241,20 @@ __global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restri
     if (t == 0) *resid_count = base;
 }
 
-// Row m of the compacted residual list: request b at its first rejected position ks.
+// Row m of the compacted residual list: request b at its first rejected
+// position ks, conditioned on token x (x_{ks-1}), as written by k_accept.
+// Every field is clamped into range, so a row read past the count (stale
+// workspace) still addresses valid memory; such rows are never reported.
 struct ResidRow {
-    int b, ks;
+    int b, ks, x;
 };
-__device__ __forceinline__ ResidRow resid_row(const int32_t* __restrict__ resid_list,
-                                              const int32_t* __restrict__ accepted, int m)
+__device__ __forceinline__ ResidRow resid_row(const int4* __restrict__ resid_list, int m, int B, int gamma, int V)
 {
+    const int4 q = resid_list[m];
     ResidRow r;
-    r.b = resid_list[m];
-    r.ks = accepted[r.b] + 1;
+    r.b = min(max(q.x, 0), B - 1);
+    r.ks = min(max(q.y, 1), gamma);
+    r.x = min(max(q.z, 0), V - 1);
     return r;
 }
 
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
     const float* __restrict__ Tg, const float* __restrict__ L, const float* __restrict__ A,
     const float* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ accepted,
-    const int32_t* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int gamma, int V, int r, int nT,
+    const int4* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int B, int gamma, int V, int r, int nT,
     int nM, float2* __restrict__ rpart)
 {
     __shared__ __attribute__((aligned(16))) char lds[markov_lds_bytes<F32>()];
@@ -271,12 +282,12 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
     floatx4 acc[4][8];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-        const ResidRow ra = resid_row(resid_list, accepted, min(mw0 + 16 * mb + (lane & 15), cnt - 1));
-        arow[mb] = A + (size_t)cond_token_v(x0, tok, ra.b, gamma, ra.ks, V) * r;
+        const ResidRow ra = resid_row(resid_list, min(mw0 + 16 * mb + (lane & 15), cnt - 1), B, gamma, V);
+        arow[mb] = A + (size_t)ra.x * r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = mw0 + 16 * mb + 4 * (lane >> 4) + i;
-            const ResidRow rr = resid_row(resid_list, accepted, min(row, cnt - 1));
+            const ResidRow rr = resid_row(resid_list, min(row, cnt - 1), B, gamma, V);
             const float* lrow = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = mw0 + 16 * mb + 4 * (lane >> 4) + i;
-            const ResidRow rr = resid_row(resid_list, accepted, min(row, cnt - 1));
+            const ResidRow rr = resid_row(resid_list, min(row, cnt - 1), B, gamma, V);
             const float* trow = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
             const SplitLse ld = split_lse(lse_d[(size_t)rr.b * gamma + rr.ks - 1]);
             const SplitLse lt = split_lse(lse_t[(size_t)rr.b * gamma + rr.ks - 1]);
@@ -330,7 +341,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     const uint16_t* __restrict__ Tg, const uint16_t* __restrict__ L, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ accepted,
-    const int32_t* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int gamma, int V, int r, int nT,
+    const int4* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int B, int gamma, int V, int r, int nT,
     int nM, int S, float2* __restrict__ rpart)
 {
     constexpr int NW = kTileWaves, R = kTileRows;
@@ -351,26 +362,23 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     const int mw = m0 + 32 * w;
     const bool active = mw < cntr;
 
-    uint4 a[2][8];
+    uint4 a[2][8];  // B operand: the rows' A vectors (loaded in the prologue)
     const uint16_t* lrow[2];
     const uint16_t* trow[2];
+    const uint16_t* arow[2];
+    int lrow_idx[2];
     SplitLse ld[2], lt[2];
-    {
-        const uint16_t* arow[2];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const ResidRow rr = resid_row(resid_list, accepted, min(mw + 16 * bb + c, cntr - 1));
-            arow[bb] = A + (size_t)cond_token_v(x0, tok, rr.b, gamma, rr.ks, V) * r;
-            lrow[bb] = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
-            trow[bb] = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
-            ld[bb] = split_lse(lse_d[(size_t)rr.b * gamma + rr.ks - 1]);
-            lt[bb] = split_lse(lse_t[(size_t)rr.b * gamma + rr.ks - 1]);
-        }
-        load_a_frags<2>(arow, r, a);
+    for (int bb = 0; bb < 2; ++bb) {
+        const ResidRow rr = resid_row(resid_list, min(mw + 16 * bb + c, cntr - 1), B, gamma, V);
+        arow[bb] = A + (size_t)rr.x * r;
+        lrow[bb] = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
+        trow[bb] = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
+        lrow_idx[bb] = rr.b * gamma + rr.ks - 1;
     }
     const int nks = KS > 0 ? KS : (r + 31) / 32;
 
-    auto load_lt = [&](int i, uint2 (&lv)[2][4], uint2 (&tv)[2][4]) {
+    auto load_lt = [&](int i, uint4 (&lv)[2][2], uint4 (&tv)[2][2]) {
         const bool dummy = i >= cnt;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
@@ -381,7 +389,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     auto dma = [&](int i, char* buf) { dma_bm_tile<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf); };
 
     // Row sums of tile i from its logits f (accumulators) and target values.
-    auto epilogue = [&](int i, const floatx4 (&f)[4][2], const uint2 (&tv)[2][4]) {
+    auto epilogue = [&](int i, const floatx4 (&f)[4][2], const uint4 (&tv)[2][2]) {
         const int n0 = (t0 + i * ts) * kTcols;
         const bool tail = n0 + kTcols > V;
 #pragma unroll
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
             float sw = 0.0f, sp = 0.0f;
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb) {
-                const floatx4 t = bf16x4_to_f32(tv[bb][vb]);
+                const floatx4 t = bf16x4_to_f32(row16_block(tv[bb], vb));
                 const bool ok = !tail || n0 + vm_col(G, vb) < V;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -406,42 +414,66 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
             if (G == bb) stage[i][32 * w + 16 * bb + c] = pack_f2(sw, sp);
         }
     };
-    uint2 lc[2][4], tc[2][4], ln[2][4], tn[2][4];
-    auto body = [&](int i, const char* cur, char* nxt) {
-        wait_stage<4 * kRow16Loads, 32 / NW>(i);
+    // L and T values of two tiles in flight: the four unrolled bodies
+    // alternate between two register sets, so no copy waits on a load just issued.
+    uint4 l0[2][2], t0r[2][2], l1[2][2], t1r[2][2];
+    auto body = [&](int i, const char* cur, char* nxt, uint4 (&lc)[2][2], uint4 (&tc)[2][2], uint4 (&ln)[2][2],
+                    uint4 (&tn)[2][2]) {
+        if (KS > 0) wait_stage<4 * kRow16Loads, 32 / NW, 20>(i);
+        else if (i == 0) wait_all_mem();  // run-time rank
+        else wait_stage<4 * kRow16Loads, 32 / NW, 20>(i);
         barrier_lds();  // Bm tile i has landed in cur; every wave is done with nxt
+        issue_fence();
         load_lt(i + 1, ln, tn);
+        issue_fence();
+        if (i == 0) {  // ramp-up: tiles 1 and 2 (buffers s1, s2) behind tile 3
+            dma(1, s1);
+            issue_fence();
+            dma(2, s2);
+            issue_fence();
+        }
         dma(i + 3, nxt);
+        issue_fence();
         if (active) {
             floatx4 acc[4][2];
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-                for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(lc[bb][vb]);
+                for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(row16_block(lc[bb], vb));
             tile_mma_vm<2, KS>(a, cur, nks, acc);
             epilogue(i, acc, tc);
         }
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int vb = 0; vb < 4; ++vb) {
-                lc[bb][vb] = ln[bb][vb];
-                tc[bb][vb] = tn[bb][vb];
-            }
     };
 
-    load_lt(0, lc, tc);
+    // Prologue: the rows' records were loaded first; then only the first
+    // tile, then the A-operand gather and the rows' normalisers (NA = 16 + 4
+    // loads after the first Bm tile).
+    issue_fence();
+    load_lt(0, l0, t0r);
+    issue_fence();
     dma(0, s0);
-    dma(1, s1);
-    dma(2, s2);
+    issue_fence();
+    load_a_frags<2>(arow, r, a);
+    double lsd[2], lst[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        lsd[bb] = lse_d[lrow_idx[bb]];
+        lst[bb] = lse_t[lrow_idx[bb]];
+    }
+    issue_fence();
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        ld[bb] = split_lse(lsd[bb]);
+        lt[bb] = split_lse(lst[bb]);
+    }
     for (int i = 0;;) {
-        body(i, s0, s3);
+        body(i, s0, s3, l0, t0r, l1, t1r);
         if (++i >= cnt) break;
-        body(i, s1, s0);
+        body(i, s1, s0, l1, t1r, l0, t0r);
         if (++i >= cnt) break;
-        body(i, s2, s1);
+        body(i, s2, s1, l0, t0r, l1, t1r);
         if (++i >= cnt) break;
-        body(i, s3, s2);
+        body(i, s3, s2, l1, t1r, l0, t0r);
         if (++i >= cnt) break;
     }
     wait_all_mem();
@@ -508,11 +540,11 @@ __global__ __launch_bounds__(kThreads) void k_final(
             floatx4 f[4];
             row_tile_vm(lrow, A, Bm, prev, V, r, n0, lds, f);
             if ((t >> 6) == 0) {
-                uint2 tv[4];
+                uint4 tv[2];
                 load_row16(trow, n0, V, false, tv);
                 floatx4 tf[4];
 #pragma unroll
-                for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(tv[vb]);
+                for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(row16_block(tv, vb));
                 double wsel;
                 const int j = scan_vm_tile(
                     n0, m, 1.0, loc.cprev, loc.tau,
@@ -633,7 +665,7 @@ __global__ __launch_bounds__(64) void k_final_bf16(
 
         const int n0 = loc.idx * kTcols;
         const uint16_t* trow = Tg + ((size_t)b * (gamma + 1) + (ks - 1)) * V;
-        uint2 tv[4];
+        uint4 tv[2];
         load_row16(trow, n0, V, false, tv);
         floatx4 f[4];
         row_tile_vm_wave<KS>(L + ((size_t)b * gamma + (ks - 1)) * V, af, Bm, V, r, n0, lds, f);
@@ -641,7 +673,7 @@ __global__ __launch_bounds__(64) void k_final_bf16(
         const SplitLse lt = split_lse(lse_t[(size_t)b * gamma + ks - 1]);
         floatx4 tf[4];
 #pragma unroll
-        for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(tv[vb]);
+        for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(row16_block(tv, vb));
         double wsel;
         const int j = scan_vm_tile(
             n0, m, 1.0, loc.cprev, loc.tau,
@@ -749,7 +781,7 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     double* lse_t = reinterpret_cast<double*>(w + lay.lse_t);
     double* ptw = reinterpret_cast<double*>(w + lay.pt);
     int32_t* ridx = reinterpret_cast<int32_t*>(w + lay.resid_idx);
-    int32_t* rlist = reinterpret_cast<int32_t*>(w + lay.resid_list);
+    int4* rlist = reinterpret_cast<int4*>(w + lay.resid_list);
     int32_t* rcnt = reinterpret_cast<int32_t*>(w + lay.resid_count);
     float2* rpart = reinterpret_cast<float2*>(w + lay.res_part);
     float* bm = reinterpret_cast<float*>(w + lay.bon_m);
@@ -763,8 +795,8 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
                        gamma, V, nC, lse_t, ptw);
     prof_end(K_TARGET_PARTIALS, s);
     prof_begin(K_ACCEPT, s);
-    hipLaunchKernelGGL(k_accept, dim3(1), dim3(kAcceptThreads), 0, s, pd, len, ptw, B, gamma, seed, accepted, n_out,
-                       target_p, ridx, rlist, rcnt);
+    hipLaunchKernelGGL(k_accept, dim3(1), dim3(kAcceptThreads), 0, s, pd, len, ptw, x0, tok, B, gamma, seed, accepted,
+                       n_out, target_p, ridx, rlist, rcnt);
     prof_end(K_ACCEPT, s);
     prof_begin(K_RESID_TILES, s);
     if (std::is_same<DT, Bf16>::value) {
@@ -774,13 +806,13 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
         hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s,
                            reinterpret_cast<const uint16_t*>(Tg), reinterpret_cast<const uint16_t*>(L),
                            reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(Bm), x0, tok,
-                           lse_d, lse_t, accepted, rlist, rcnt, gamma, V, r, nT, nM, S, rpart);
+                           lse_d, lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, S, rpart);
     } else {
         const int nM = (B + 255) / 256;
         hipLaunchKernelGGL(k_resid_tiles_f32, dim3(nT * nM), dim3(kThreads), 0, s,
                            reinterpret_cast<const float*>(Tg), reinterpret_cast<const float*>(L),
                            reinterpret_cast<const float*>(A), reinterpret_cast<const float*>(Bm), x0, tok, lse_d,
-                           lse_t, accepted, rlist, rcnt, gamma, V, r, nT, nM, rpart);
+                           lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, rpart);
     }
     prof_end(K_RESID_TILES, s);
     prof_begin(K_BONUS_PARTIALS, s);
