@@ -55,6 +55,33 @@ def draft_tiles_bytes_flops(wl) -> tuple:
     return byts, flops
 
 
+def kernel_source_digest() -> str:
+    """SHA-256 over the HIP sources and headers of the library (file names and contents, sorted)."""
+    import hashlib
+    d = os.path.join(ROOT, "draft_verify_sampling_prev_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the draft tile kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), if it was taken on the current
+    kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"k_draft_tiles_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("csrc_sha256") != kernel_source_digest():
+        return None
+    return t
+
+
 def cpu_baseline(inp, wl, seed: int, n_req: int) -> dict:
     """The oracle, as it stands, on the first n_req requests of the same inputs (1 thread)."""
     import numpy as np
@@ -203,6 +230,7 @@ def main():
     byts, flops = draft_tiles_bytes_flops(wl)
     avg_s = tiles_ms / max(tiles_n, 1) / 1000.0
     achieved = byts / avg_s / 1e9
+    tr = measured_traffic(wl.name)
     acc_rate = None
     result = {
         "metric": "draft+verify tokens/s at B=256,V=129280,gamma=5 (emitted tokens per step time)",
@@ -222,7 +250,9 @@ def main():
                    "accumulation": "fp32 MFMA, fp64 softmax masses"},
         "roofline": {"kernel": "draft Markov tiles (k_draft_tiles)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (tr["bytes_per_launch"] if tr else None),
+                     "traffic_source": (tr["source"] if tr else "no counter summary for the current kernel sources"),
                      "algorithmic_bytes_per_launch": byts, "avg_launch_us": round(avg_s * 1e6, 3),
                      "launches": tiles_n,
                      "mfma_tflops": round(flops / avg_s / 1e12, 2),

@@ -258,15 +258,19 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
         load_a_frags<2>(arow, r, a);
     }
     issue_fence();
-    for (int i = 0;;) {
-        body(i, s0, s3, l0, l1);
-        if (++i >= cnt) break;
+    // Tile 0 is peeled off the loop: its MFMAs then wait for the A operand
+    // k step by k step as it arrives (loads made before a loop and used in it
+    // would otherwise all be waited for before the loop is entered).
+    body(0, s0, s3, l0, l1);
+    for (int i = 1; i < cnt;) {
         body(i, s1, s0, l1, l0);
         if (++i >= cnt) break;
         body(i, s2, s1, l0, l1);
         if (++i >= cnt) break;
         body(i, s3, s2, l1, l0);
         if (++i >= cnt) break;
+        body(i, s0, s3, l0, l1);
+        ++i;
     }
     epilogue();
     wait_all_mem();  // the dummy loads past the last tile

@@ -80,11 +80,15 @@ __device__ __forceinline__ void dma16(const uint16_t* base, uint32_t voff, char*
 // (valid, finite) addresses: the A operand is zero for k >= r and columns >= V
 // are masked.  `dummy` (wave-uniform) issues the same instructions with every
 // lane reading Bm[0][0..7], for pipelines that keep a fixed number of
-// outstanding loads past their last tile.
+// outstanding loads past their last tile.  n0 must be wave-uniform; it is
+// re-read from lane 0 so that the buffer descriptor provably is (a descriptor
+// the compiler cannot prove uniform costs a loop over the lanes per load).
 template <int NW>
 __device__ __forceinline__ void dma_bm_tile(const uint16_t* __restrict__ Bm, int V, int r, int n0, bool dummy,
                                             char* buf)
 {
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    dummy = __builtin_amdgcn_readfirstlane((int)dummy) != 0;
     const int w = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
     for (int t = 0; t < 32 / NW; ++t) {

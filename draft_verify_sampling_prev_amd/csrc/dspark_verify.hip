@@ -466,15 +466,17 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
         ld[bb] = split_lse(lsd[bb]);
         lt[bb] = split_lse(lst[bb]);
     }
-    for (int i = 0;;) {
-        body(i, s0, s3, l0, t0r, l1, t1r);
-        if (++i >= cnt) break;
+    // Tile 0 is peeled off the loop (see the draft tile kernel).
+    body(0, s0, s3, l0, t0r, l1, t1r);
+    for (int i = 1; i < cnt;) {
         body(i, s1, s0, l1, t1r, l0, t0r);
         if (++i >= cnt) break;
         body(i, s2, s1, l0, t0r, l1, t1r);
         if (++i >= cnt) break;
         body(i, s3, s2, l1, t1r, l0, t0r);
         if (++i >= cnt) break;
+        body(i, s0, s3, l0, t0r, l1, t1r);
+        ++i;
     }
     wait_all_mem();
     __syncthreads();
