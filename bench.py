@@ -115,7 +115,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv4")
-    ap.add_argument("--cpu-requests", type=int, default=24, help="requests in the oracle CPU-baseline sample")
+    ap.add_argument("--cpu-requests", type=int, default=160, help="requests in the oracle CPU-baseline sample (~10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="also time HIP-graph replay of the whole step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

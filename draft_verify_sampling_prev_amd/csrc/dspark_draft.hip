@@ -133,9 +133,10 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
 // unrolled so every copy reads and fills fixed buffers):
 //   wait until Bm tile i has landed, barrier;
 //   load the L values of tile i+1 into registers, DMA Bm tile i+3;
-//   acc = L values of tile i, MFMAs over Bm tile i, and the epilogue (row
-//   max and sum of exp) of tile i-1 written to LDS staging -- in opposite
-//   orders in the two halves of the workgroup.
+//   acc = L values of tile i, MFMAs over Bm tile i, then the epilogue (row
+//   max and sum of exp) of tile i-1, written to LDS staging.  (Measured on
+//   MI355X: running the two phases in opposite orders in the two halves of
+//   the workgroup was slower.)
 // Every iteration issues the same number of loads (past the last tile they
 // are dummies reading one location), so the wait for Bm tile i is a constant
 // count of outstanding loads per wave (wait_stage).
@@ -183,8 +184,12 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
 
     floatx4 fprev[4][2];
     int prev = -1;  // local index of the tile held in fprev
-    auto epilogue = [&]() {
-        if (prev < 0 || !active) return;
+    // Row max and sum of exp of the tile held in fprev, written to the LDS
+    // staging by every lane of the row (they hold the same bits, so the store
+    // needs no lane predicate).  Inside the loop the tile is never the last
+    // tile of the vocabulary (that one is each slot's last and is finished
+    // after the loop), so that form has no branch at all.
+    auto epilogue = [&](auto tail) {
         const int n0 = (t0 + prev * ts) * kTcols;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
@@ -192,14 +197,14 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb) v[vb] = fprev[vb][bb];
             float m, sum;
-            row64_max_sum(v, n0 + kTcols > V, V - n0, &m, &sum);
-            if (G == bb) stage[prev][32 * w + 16 * bb + c] = pack_f2(m, sum);
+            row64_max_sum<decltype(tail)::value>(v, V - n0, &m, &sum);
+            stage[prev][32 * w + 16 * bb + c] = pack_f2(m, sum);
         }
     };
     // L values of two tiles in flight: the four unrolled bodies alternate
     // between two register sets, so no copy waits on a load just issued.
     uint4 l0[2][2], l1[2][2];
-    auto body = [&](int i, const char* cur, char* nxt, uint4 (&lc)[2][2], uint4 (&ln)[2][2]) {
+    auto body = [&](auto has_prev, int i, const char* cur, char* nxt, uint4 (&lc)[2][2], uint4 (&ln)[2][2]) {
         if (KS > 0) wait_stage<2 * kRow16Loads, 32 / NW, 16>(i);
         else if (i == 0) wait_all_mem();  // run-time rank: the A-operand load count varies
         else wait_stage<2 * kRow16Loads, 32 / NW, 16>(i);
@@ -221,19 +226,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(row16_block(lc[bb], vb));
-            // The epilogue of the previous tile is independent of these
-            // MFMAs.  Waves 0-3 and 4-7 take the two phases in opposite
-            // order, so each SIMD (one wave of each half) has one wave on the
-            // matrix cores while the other runs the vector ALU.  (Only with a
-            // compile-time k-step count: the run-time variant has no
-            // registers to spare for the second code path.)
-            if (KS > 0 && (w & 4)) {
-                epilogue();
-                tile_mma_vm<2, KS>(a, cur, nks, acc);
-            } else {
-                tile_mma_vm<2, KS>(a, cur, nks, acc);
-                epilogue();
-            }
+            tile_mma_vm<2, KS>(a, cur, nks, acc);
+            if constexpr (decltype(has_prev)::value)
+                epilogue(std::false_type{});  // previous tile; independent of the MFMAs above
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
@@ -261,18 +256,19 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     // Tile 0 is peeled off the loop: its MFMAs then wait for the A operand
     // k step by k step as it arrives (loads made before a loop and used in it
     // would otherwise all be waited for before the loop is entered).
-    body(0, s0, s3, l0, l1);
+    const std::true_type more{};
+    body(std::false_type{}, 0, s0, s3, l0, l1);
     for (int i = 1; i < cnt;) {
-        body(i, s1, s0, l1, l0);
+        body(more, i, s1, s0, l1, l0);
         if (++i >= cnt) break;
-        body(i, s2, s1, l0, l1);
+        body(more, i, s2, s1, l0, l1);
         if (++i >= cnt) break;
-        body(i, s3, s2, l1, l0);
+        body(more, i, s3, s2, l1, l0);
         if (++i >= cnt) break;
-        body(i, s0, s3, l0, l1);
+        body(more, i, s0, s3, l0, l1);
         ++i;
     }
-    epilogue();
+    if (active) epilogue(std::true_type{});  // the slot's last tile (the vocabulary's tail for the last slot)
     wait_all_mem();  // the dummy loads past the last tile
     __syncthreads();
     // Write the staged partials (consecutive threads take consecutive tiles of a row).

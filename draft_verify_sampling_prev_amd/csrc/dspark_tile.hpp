@@ -291,15 +291,18 @@ __device__ __forceinline__ void slot_tiles(int s, int S, int nT, int* t0, int* t
 }
 
 // Row-wise max and sum of exp over the 64 columns of a tile held as 16
-// values per lane (lanes c, c+16, c+32, c+48 hold one row).  Values of
-// columns at or past ncol (tail only) count as absent.  All four lanes of the
-// row receive the max m (-inf if no finite value) and s = sum exp(f - m)
-// (fp32, fixed order: within the lane in block order, then the xor-16 and
-// xor-32 butterflies).
-__device__ __forceinline__ void row64_max_sum(floatx4 (&v)[4], bool tail, int ncol, float* m_out, float* s_out)
+// values per lane (lanes c, c+16, c+32, c+48 hold one row).  With TAIL,
+// values of columns at or past ncol count as absent (without it the code has
+// no branch, so the compiler can interleave it with independent MFMAs).  All
+// four lanes of the row receive the same bits: the max m (-inf if no finite
+// value) and s = sum exp(f - m) (fp32, fixed order: within the lane in block
+// order, then the xor-16 and xor-32 butterflies, whose operand swaps do not
+// change a floating-point add or max).
+template <bool TAIL>
+__device__ __forceinline__ void row64_max_sum(floatx4 (&v)[4], int ncol, float* m_out, float* s_out)
 {
     const int G = (threadIdx.x & 63) >> 4;
-    if (tail) {
+    if (TAIL) {
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb)
             if (vm_col(G, vb) >= ncol) v[vb] = floatx4{ -INFINITY, -INFINITY, -INFINITY, -INFINITY };
