@@ -35,11 +35,16 @@ namespace dspark {
 
 // Conditioning token of request b at draft step k (1-based), clamped into the
 // vocabulary so that an out-of-range caller token can never address outside A.
+__device__ __forceinline__ int cond_token_raw(const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, int b,
+                                              int gamma, int k)
+{
+    return (k == 1) ? x0[b] : tok[b * gamma + (k - 2)];
+}
+__device__ __forceinline__ int clamp_token(int x, int V) { return min(max(x, 0), V - 1); }
 __device__ __forceinline__ int cond_token(const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, int b,
                                           int gamma, int k, int V)
 {
-    int x = (k == 1) ? x0[b] : tok[b * gamma + (k - 2)];
-    return min(max(x, 0), V - 1);
+    return clamp_token(cond_token_raw(x0, tok, b, gamma, k), V);
 }
 
 // Tile max m_t and s_t = sum exp(f - m_t) (fp32 within the tile) for the
@@ -239,17 +244,18 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
 
     // Prologue: the conditioning tokens are loaded first (the oldest loads,
     // so waiting for them does not wait for the tile loads behind them), then
-    // only the first tile, then the A-operand gather.
+    // only the first tile; the tokens are used (clamped) only after that, and
+    // then the A-operand gather is issued.
     int tk[2];
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) tk[bb] = cond_token(x0, tok, min(mw + 16 * bb + c, B - 1), gamma, k, V);
+    for (int bb = 0; bb < 2; ++bb) tk[bb] = cond_token_raw(x0, tok, min(mw + 16 * bb + c, B - 1), gamma, k);
     issue_fence();
     load_l(0, l0);
     issue_fence();
     dma(0, s0);
     issue_fence();
     {
-        const uint16_t* arow[2] = { A + (size_t)tk[0] * r, A + (size_t)tk[1] * r };
+        const uint16_t* arow[2] = { A + (size_t)clamp_token(tk[0], V) * r, A + (size_t)clamp_token(tk[1], V) * r };
         load_a_frags<2>(arow, r, a);
     }
     issue_fence();

@@ -111,16 +111,32 @@ __device__ __forceinline__ v4s tr_read(const char* buf, int off)
 // A operand (Bm^T) of k step ks, vocabulary block vb: lane (G', j) gets
 // k = 32ks + 8G' .. +7 of tile column 16(j>>2) + 4(vb ^ ((j>>2)&1)) + (j&3).
 // In each 16-lane group, source lane 4r+q addresses LDS row k0 + r at the
-// four columns 16q + 4(vb ^ (q&1)) .. +3.
-__device__ __forceinline__ bf16x8 bm_frag(const char* bufB, int ks, int vb)
+// four columns 16q + 4(vb ^ (q&1)) .. +3; rows k0 + 4 + r follow 512 bytes
+// later (the swizzle of k0 and k0 + 4 is the same).  Only the lane part of
+// the address depends on the lane: bm_lane_offsets computes it per vb, and
+// k step ks adds 32 rows (4096 bytes) per step.
+__device__ __forceinline__ void bm_lane_offsets(int (&off)[4])
 {
     const int lane = threadIdx.x & 63;
     const int Gk = lane >> 4, r = (lane & 15) >> 2, q = lane & 3;
-    const int chunk = 2 * q + (vb >> 1);
-    const int half = (vb ^ q) & 1;
-    const int k0 = 32 * ks + 8 * Gk + r, k1 = k0 + 4;
-    const v4s lo = tr_read(bufB, k0 * kTrowBytes + 16 * (chunk ^ swz_k(k0)) + 8 * half);
-    const v4s hi = tr_read(bufB, k1 * kTrowBytes + 16 * (chunk ^ swz_k(k1)) + 8 * half);
+    const int k0 = 8 * Gk + r;
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) {
+        const int chunk = 2 * q + (vb >> 1), half = (vb ^ q) & 1;
+        off[vb] = k0 * kTrowBytes + 16 * (chunk ^ swz_k(k0)) + 8 * half;
+        // Opaque to the optimizer: every LDS read address is then this value
+        // plus a constant, a short chain from the buffer.  (The LDS lowering
+        // attributes an access to its buffer only through a few address
+        // steps; a read it cannot attribute makes the compiler wait for every
+        // outstanding LDS DMA before it.)
+        asm("" : "+v"(off[vb]));
+    }
+}
+
+__device__ __forceinline__ bf16x8 bm_frag(const char* bufB, const int (&off)[4], int ks, int vb)
+{
+    const v4s lo = tr_read(bufB, off[vb] + 32 * ks * kTrowBytes);
+    const v4s hi = tr_read(bufB, off[vb] + 32 * ks * kTrowBytes + 4 * kTrowBytes);
     typedef short v8s __attribute__((ext_vector_type(8)));
     const v8s v = { lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3] };
     return __builtin_bit_cast(bf16x8, v);
@@ -133,16 +149,21 @@ template <int NBB>
 __device__ __forceinline__ void load_a_frags(const uint16_t* const (&arow)[NBB], int r, uint4 (&a)[NBB][8])
 {
     const int kq8 = 8 * ((threadIdx.x & 63) >> 4);
+    // A fixed number of loads: k >= r reads a valid address ...
 #pragma unroll
     for (int bb = 0; bb < NBB; ++bb)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int k = 32 * ks + kq8;
-            // Branch-free (a fixed number of loads): k >= r reads a valid
-            // address and is replaced by zeros.
-            const uint4 v = ld16(arow[bb] + min(k, r - 8));
-            a[bb][ks] = k < r ? v : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int ks = 0; ks < 8; ++ks) a[bb][ks] = ld16(arow[bb] + min(32 * ks + kq8, r - 8));
+    // ... and is replaced by zeros.  Only ranks that are not a multiple of 32
+    // have such slots; the (uniform) branch keeps the other ranks from waiting
+    // for the loads here, so callers can issue more loads behind them.
+    if (r & 31) {
+#pragma unroll
+        for (int bb = 0; bb < NBB; ++bb)
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                if (32 * ks + kq8 >= r) a[bb][ks] = make_uint4(0u, 0u, 0u, 0u);
+    }
 }
 
 // Four bf16 values (8 bytes) -> floats.
@@ -185,16 +206,18 @@ template <int NBB, int KS>
 __device__ __forceinline__ void tile_mma_vm(const uint4 (&a)[NBB][8], const char* bufB, int nks,
                                             floatx4 (&acc)[4][NBB])
 {
+    int off[4];
+    bm_lane_offsets(off);
     if constexpr (KS > 0) {
         // The Bm^T fragments of k step ks+1 are read while the MFMAs of step ks run.
         bf16x8 b[4], bn[4];
 #pragma unroll
-        for (int vb = 0; vb < 4; ++vb) b[vb] = bm_frag(bufB, 0, vb);
+        for (int vb = 0; vb < 4; ++vb) b[vb] = bm_frag(bufB, off, 0, vb);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS) {
 #pragma unroll
-                for (int vb = 0; vb < 4; ++vb) bn[vb] = bm_frag(bufB, ks + 1, vb);
+                for (int vb = 0; vb < 4; ++vb) bn[vb] = bm_frag(bufB, off, ks + 1, vb);
             }
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb)
@@ -213,7 +236,7 @@ __device__ __forceinline__ void tile_mma_vm(const uint4 (&a)[NBB][8], const char
             if (ks >= nks) break;
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb) {
-                const bf16x8 b = bm_frag(bufB, ks, vb);
+                const bf16x8 b = bm_frag(bufB, off, ks, vb);
 #pragma unroll
                 for (int bb = 0; bb < NBB; ++bb)
                     acc[vb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(

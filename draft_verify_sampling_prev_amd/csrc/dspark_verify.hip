@@ -248,6 +248,14 @@ __global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restri
 struct ResidRow {
     int b, ks, x;
 };
+__device__ __forceinline__ ResidRow resid_decode(int4 q, int B, int gamma, int V)
+{
+    ResidRow r;
+    r.b = min(max(q.x, 0), B - 1);
+    r.ks = min(max(q.y, 1), gamma);
+    r.x = min(max(q.z, 0), V - 1);
+    return r;
+}
 __device__ __forceinline__ ResidRow resid_row(const int4* __restrict__ resid_list, int m, int B, int gamma, int V)
 {
     const int4 q = resid_list[m];
@@ -368,14 +376,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     const uint16_t* arow[2];
     int lrow_idx[2];
     SplitLse ld[2], lt[2];
+    int4 rec[2];  // the rows' records (decoded after the first Bm tile is issued)
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        const ResidRow rr = resid_row(resid_list, min(mw + 16 * bb + c, cntr - 1), B, gamma, V);
-        arow[bb] = A + (size_t)rr.x * r;
-        lrow[bb] = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
-        trow[bb] = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
-        lrow_idx[bb] = rr.b * gamma + rr.ks - 1;
-    }
+    for (int bb = 0; bb < 2; ++bb) rec[bb] = resid_list[min(mw + 16 * bb + c, cntr - 1)];
     const int nks = KS > 0 ? KS : (r + 31) / 32;
 
     auto load_lt = [&](int i, uint4 (&lv)[2][2], uint4 (&tv)[2][2]) {
@@ -445,13 +448,22 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
         }
     };
 
-    // Prologue: the rows' records were loaded first; then only the first
-    // tile, then the A-operand gather and the rows' normalisers (NA = 16 + 4
-    // loads after the first Bm tile).
-    issue_fence();
-    load_lt(0, l0, t0r);
+    // Prologue: the rows' records were loaded first; the first Bm tile does
+    // not depend on them and is issued before they are used; then the first
+    // L and T tiles, the A-operand gather and the rows' normalisers (NA =
+    // 16 + 4 loads after the first tile).
     issue_fence();
     dma(0, s0);
+    issue_fence();
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        const ResidRow rr = resid_decode(rec[bb], B, gamma, V);
+        arow[bb] = A + (size_t)rr.x * r;
+        lrow[bb] = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
+        trow[bb] = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
+        lrow_idx[bb] = rr.b * gamma + rr.ks - 1;
+    }
+    load_lt(0, l0, t0r);
     issue_fence();
     load_a_frags<2>(arow, r, a);
     double lsd[2], lst[2];
