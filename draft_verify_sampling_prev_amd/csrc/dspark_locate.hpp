@@ -270,17 +270,24 @@ __device__ __forceinline__ int scan_vm_tile(int n0, int pos, double scale, doubl
                                             double* w_sel)
 {
     const int lane = threadIdx.x & 63, G = lane >> 4, c = lane & 15, cp = pos & 15;
+    // Weights per stored block (compile-time block index, so the caller's
+    // register arrays are indexed statically), then put in column order: the
+    // lane's column group q4 is stored in block q4 ^ (G & 1).
+    double ws[4][4];
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ws[vb][i] = wfn(vb, i, n0 + vm_col(G, vb) + i);
+    const bool odd = (G & 1) != 0;
     double w[16];
     double tot = 0.0;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-        const int vb = q4 ^ (G & 1);
+    for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            w[4 * q4 + i] = wfn(vb, i, n0 + 16 * G + 4 * q4 + i);
+            w[4 * q4 + i] = odd ? ws[q4 ^ 1][i] : ws[q4][i];
             tot += w[4 * q4 + i];
         }
-    }
     const double t0 = __shfl(tot, cp, 64), t1 = __shfl(tot, 16 + cp, 64), t2 = __shfl(tot, 32 + cp, 64);
     double run = G == 0 ? 0.0 : (G == 1 ? t0 : (G == 2 ? t0 + t1 : (t0 + t1) + t2));
     int hit = -1, last = -1;

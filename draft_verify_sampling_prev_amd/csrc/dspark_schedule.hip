@@ -66,20 +66,34 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(const float* __restr
     const int N = B * gamma;
 
     for (int b = t; b < B; b += kSchedThreads) {
-        float th = 1.0f;
-        for (int kk = 0; kk < gamma; ++kk) {
-            float v;
-            if (z) {
-                const float q = z[b * gamma + kk] / temps[kk];
-                const float c = 1.0f / (1.0f + expf(-q));
-                th = th * c;
-                v = th;
-                surv[b * gamma + kk] = v;
-            } else {
-                v = surv[b * gamma + kk];
-            }
-            keys[b * gamma + kk] = order_key(v);
+        // All of the row's inputs are loaded before any is used (one memory
+        // round trip, not one per position).
+        float v[kMaxGamma];
+        const float* src = z ? z : surv;
+#pragma unroll
+        for (int kk = 0; kk < kMaxGamma; ++kk)
+            if (kk < gamma) v[kk] = src[b * gamma + kk];
+        if (z) {
+            float tk[kMaxGamma];
+#pragma unroll
+            for (int kk = 0; kk < kMaxGamma; ++kk)
+                if (kk < gamma) tk[kk] = temps[kk];
+            float th = 1.0f;
+#pragma unroll
+            for (int kk = 0; kk < kMaxGamma; ++kk)
+                if (kk < gamma) {
+                    const float q = v[kk] / tk[kk];
+                    const float c = 1.0f / (1.0f + expf(-q));
+                    th = th * c;
+                    v[kk] = th;
+                }
+#pragma unroll
+            for (int kk = 0; kk < kMaxGamma; ++kk)
+                if (kk < gamma) surv[b * gamma + kk] = v[kk];
         }
+#pragma unroll
+        for (int kk = 0; kk < kMaxGamma; ++kk)
+            if (kk < gamma) keys[b * gamma + kk] = order_key(v[kk]);
     }
     __syncthreads();
 

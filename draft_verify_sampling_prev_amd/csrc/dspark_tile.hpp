@@ -149,11 +149,12 @@ template <int NBB>
 __device__ __forceinline__ void load_a_frags(const uint16_t* const (&arow)[NBB], int r, uint4 (&a)[NBB][8])
 {
     const int kq8 = 8 * ((threadIdx.x & 63) >> 4);
-    // A fixed number of loads: k >= r reads a valid address ...
+    // A fixed number of loads, in k-step order (the MFMAs of k step ks can
+    // start once its loads have landed): k >= r reads a valid address ...
 #pragma unroll
-    for (int bb = 0; bb < NBB; ++bb)
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) a[bb][ks] = ld16(arow[bb] + min(32 * ks + kq8, r - 8));
+        for (int bb = 0; bb < NBB; ++bb) a[bb][ks] = ld16(arow[bb] + min(32 * ks + kq8, r - 8));
     // ... and is replaced by zeros.  Only ranks that are not a multiple of 32
     // have such slots; the (uniform) branch keeps the other ranks from waiting
     // for the loads here, so callers can issue more loads behind them.

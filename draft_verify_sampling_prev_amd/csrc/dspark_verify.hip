@@ -367,8 +367,11 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     slot_tiles(slot, S, nT, &t0, &ts, &cnt);
     if (m0 >= cntr || cnt <= 0) return;  // uniform
     const int w = wave_id(), lane = threadIdx.x & 63, G = lane >> 4, c = lane & 15;
-    const int mw = m0 + 32 * w;
-    const bool active = mw < cntr;
+    // Batch block bb of wave w holds the workgroup's rows 128bb + 16w .. +15,
+    // so the first rejected rows spread over all waves (and SIMDs) and a
+    // block past the last rejected row is skipped.
+    auto row_of = [&](int bb) { return 128 * bb + 16 * w; };
+    const bool act0 = m0 + row_of(0) < cntr, act1 = m0 + row_of(1) < cntr;
 
     uint4 a[2][8];  // B operand: the rows' A vectors (loaded in the prologue)
     const uint16_t* lrow[2];
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     SplitLse ld[2], lt[2];
     int4 rec[2];  // the rows' records (decoded after the first Bm tile is issued)
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) rec[bb] = resid_list[min(mw + 16 * bb + c, cntr - 1)];
+    for (int bb = 0; bb < 2; ++bb) rec[bb] = resid_list[min(m0 + row_of(bb) + c, cntr - 1)];
     const int nks = KS > 0 ? KS : (r + 31) / 32;
 
     auto load_lt = [&](int i, uint4 (&lv)[2][2], uint4 (&tv)[2][2]) {
@@ -391,30 +394,43 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     };
     auto dma = [&](int i, char* buf) { dma_bm_tile<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf); };
 
-    // Row sums of tile i from its logits f (accumulators) and target values.
-    auto epilogue = [&](int i, const floatx4 (&f)[4][2], const uint4 (&tv)[2][2]) {
-        const int n0 = (t0 + i * ts) * kTcols;
-        const bool tail = n0 + kTcols > V;
+    // Row sums of tile i from its logits f (accumulators) and target values,
+    // for the first NBB batch blocks.  Every lane of a row ends with the same
+    // bits, so the staging store needs no lane predicate.
+    auto epilogue = [&](auto nbb, int i, const floatx4 (&f)[4][decltype(nbb)::value], const uint4 (&tv)[2][2]) {
+        constexpr int NBB = decltype(nbb)::value;
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
+        for (int bb = 0; bb < NBB; ++bb) {
             float sw = 0.0f, sp = 0.0f;
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb) {
                 const floatx4 t = bf16x4_to_f32(row16_block(tv[bb], vb));
-                const bool ok = !tail || n0 + vm_col(G, vb) < V;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float ptv;
-                    const float wr = resid_weight(f[vb][bb][e], t[e], ld[bb], lt[bb], &ptv);
-                    sw += ok ? wr : 0.0f;
-                    sp += ok ? ptv : 0.0f;
+                    sw += resid_weight(f[vb][bb][e], t[e], ld[bb], lt[bb], &ptv);
+                    sp += ptv;
                 }
             }
             sw += __shfl_xor(sw, 16, 64);
             sw += __shfl_xor(sw, 32, 64);
             sp += __shfl_xor(sp, 16, 64);
             sp += __shfl_xor(sp, 32, 64);
-            if (G == bb) stage[i][32 * w + 16 * bb + c] = pack_f2(sw, sp);
+            stage[i][row_of(bb) + c] = pack_f2(sw, sp);
+        }
+    };
+    // The vocabulary's tail tile: target values of columns at or past V
+    // become -inf, so their residual weight and target probability are 0
+    // (V is a multiple of 8: a 16-byte group is entirely in or out).
+    auto mask_tail = [&](int i, uint4 (&tv)[2][2]) {
+        const int n0 = (t0 + i * ts) * kTcols;
+        if (n0 + kTcols > V) {  // uniform
+            const uint4 ninf = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int h = 0; h < kRow16Loads; ++h)
+                    if (n0 + 16 * G + 8 * h >= V) tv[bb][h] = ninf;
         }
     };
     // L and T values of two tiles in flight: the four unrolled bodies
@@ -437,14 +453,22 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
         }
         dma(i + 3, nxt);
         issue_fence();
-        if (active) {
+        if (act1) {
+            mask_tail(i, tc);
             floatx4 acc[4][2];
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(row16_block(lc[bb], vb));
             tile_mma_vm<2, KS>(a, cur, nks, acc);
-            epilogue(i, acc, tc);
+            epilogue(std::integral_constant<int, 2>{}, i, acc, tc);
+        } else if (act0) {  // only the first batch block holds rejected rows
+            mask_tail(i, tc);
+            floatx4 acc[4][1];
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(row16_block(lc[0], vb));
+            tile_mma_vm<1, KS>(*reinterpret_cast<const uint4(*)[1][8]>(&a[0]), cur, nks, acc);
+            epilogue(std::integral_constant<int, 1>{}, i, acc, tc);
         }
     };
 
