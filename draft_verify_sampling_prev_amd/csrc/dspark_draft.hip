@@ -397,25 +397,22 @@ __global__ __launch_bounds__(64) void k_draft_locate_bf16(const uint16_t* __rest
             if constexpr (kCache) return ms[j];
             else return tile_mass(q[j].x, (double)q[j].y, M);
         },
-        u);
+        u, reinterpret_cast<double*>(lds));
     const int idx = loc.idx;
     const double cprev = loc.cprev, tau = loc.tau, S = loc.S;
 
     const int n0 = idx * kTcols;
+    // Max of the chosen tile (reloaded: the partials are cached; its latency
+    // hides behind the tile's own loads).
+    const float mt = pr[idx].x;
     floatx4 f[4];
     row_tile_vm_wave<KS>(L + ((size_t)b * gamma + (k - 1)) * V, a, Bm, V, r, n0, lds, f);
-    // Max of the chosen tile, from the registers of the lane whose slice holds it.
-    float mt_l = -INFINITY;
-#pragma unroll
-    for (int jj = 0; jj < PER; ++jj)
-        if (i0 + jj == idx) mt_l = q[jj].x;
-    const float mt = __shfl(mt_l, min(idx / ((nT + 63) / 64), 63), 64);
     const double scale = tile_mass(mt, 1.0, M);
     const float ml = row_mlog2(mt);
     double wsel;
-    const int j = scan_vm_tile(
-        n0, b, scale, cprev, tau,
-        [&](int vb, int i, int col) { return col < V && mt != -INFINITY ? (double)softmax_w(f[vb][i], ml) : 0.0; },
+    const int j = scan_row_tile_lanes(
+        n0, scale, cprev, tau,
+        [&](int col, auto pick) { return col < V && mt != -INFINITY ? (double)softmax_w(pick(f), ml) : 0.0; },
         &wsel);
     if (lane == 0) {
         tok[b * gamma + (k - 1)] = min(n0 + j, V - 1);

@@ -191,14 +191,24 @@ __device__ __forceinline__ void row_tile_vm_wave(const uint16_t* L_row, const ui
 }
 
 // One wave, masses held in registers: lane l owns the contiguous slice
-// [i0, i0 + PER) (i0 = l * per, per <= PER; slots past the slice or past n
-// must have mass 0) and mass(j) gives the mass of its slot j.  Same rule as
-// locate(): slice sums combined by a wave scan in lane order, first index
-// whose running mass exceeds u*S, else the last index of positive mass,
-// else 0.  mass(j) is evaluated twice per slot.
+// [i0, i0 + PER) (i0 = l * per, per <= PER <= 64; slots past the slice or
+// past n must have mass 0) and mass(j) gives the mass of its slot j.  Same
+// rule as locate(): the first index whose running mass exceeds u*S, else the
+// last index of positive mass, else 0.
+//
+// Slice sums are combined by a wave scan in lane order.  The slice holding
+// the crossing is the first lane whose inclusive sum exceeds tau; that
+// lane's PER masses are then spread over lanes 0..PER-1 (through `scratch`,
+// LDS with room for PER doubles) and scanned by a second wave scan from the
+// slice's exclusive prefix, so no lane walks its slots one by one.  If
+// rounding leaves every running sum in that slice at or below tau, its last
+// slot of positive mass is taken.  With no crossing at all the last slice
+// with positive mass is treated the same way.  The chosen slot always has
+// positive mass (a crossing slot must, too).
 template <int PER, class MassFn>
-__device__ __forceinline__ Located wave_locate_slices(int i0, MassFn mass, float u)
+__device__ __forceinline__ Located wave_locate_slices(int i0, MassFn mass, float u, double* scratch)
 {
+    static_assert(PER <= 64, "one slot per lane in the second scan");
     const int lane = threadIdx.x & 63;
     Located L;
     double sl = 0.0;
@@ -208,35 +218,31 @@ __device__ __forceinline__ Located wave_locate_slices(int i0, MassFn mass, float
     const double off = wave_excl_from_incl(inc);
     L.S = wave_last(inc);
     L.tau = (double)u * L.S;
-    int hit = -1, lastpos = -1;
-    double c = off, cph = 0.0, cpl = 0.0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const double mj = mass(j);
-        const double cb = c;
-        c += mj;
-        if (hit < 0 && c > L.tau) {
-            hit = i0 + j;
-            cph = cb;
-        }
-        if (mj > 0.0) {
-            lastpos = i0 + j;
-            cpl = cb;
-        }
-    }
-    const uint64_t mh = __ballot(hit >= 0), mp = __ballot(lastpos >= 0);
-    if (mh) {
-        const int src = __builtin_ctzll(mh);
-        L.idx = __shfl(hit, src, 64);
-        L.cprev = __shfl(cph, src, 64);
-    } else if (mp) {
-        const int src = 63 - __builtin_clzll(mp);
-        L.idx = __shfl(lastpos, src, 64);
-        L.cprev = __shfl(cpl, src, 64);
-    } else {
+    // (A slice needs positive mass to hold the crossing: the two scans round
+    // differently, so a slice of zero mass can sit just past tau.)
+    const uint64_t mh = __ballot(inc > L.tau && sl > 0.0), mp = __ballot(sl > 0.0);
+    if (!mh && !mp) {  // no mass at all
         L.idx = 0;
         L.cprev = 0.0;
+        return L;
     }
+    const int src = mh ? __builtin_ctzll(mh) : 63 - __builtin_clzll(mp);
+    if (lane == src) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) scratch[j] = mass(j);
+    }
+    __builtin_amdgcn_wave_barrier();  // one wave: its LDS accesses complete in order
+    const double mj = lane < PER ? scratch[lane] : 0.0;
+    __builtin_amdgcn_wave_barrier();
+    const double base = __shfl(off, src, 64);
+    const int s0 = __shfl(i0, src, 64);
+    const double ej = wave_incl_scan(mj);
+    const double cj = base + ej, cb = base + wave_excl_from_incl(ej);
+    const uint64_t hj = mh ? __ballot(lane < PER && mj > 0.0 && cj > L.tau) : 0ull;
+    const uint64_t pj = __ballot(lane < PER && mj > 0.0);
+    const int j = hj ? __builtin_ctzll(hj) : 63 - __builtin_clzll(pj);
+    L.idx = s0 + j;
+    L.cprev = __shfl(cb, j, 64);
     return L;
 }
 
@@ -256,6 +262,45 @@ __device__ __forceinline__ void load_slices(const float2* __restrict__ row, int 
         q[j] = (j < per && i0 + j < n) ? v : pad;
     }
     *i0_out = i0;
+}
+
+// One-wave kernels whose 16 MFMA batch columns all hold the same row (the A
+// operand and the L row are broadcast to every column), with the tile's 64
+// values held as row_tile_vm_wave leaves them: lane L takes tile column L,
+// which is element L & 3 of stored block ((L >> 2) & 3) ^ ((L >> 4) & 1) in
+// its own registers.  wfn(col, pick) returns the weight of column col and
+// reads the lane's values through pick(x), x a floatx4[4] array in that
+// layout.  Running weights in column order come from one wave scan; the
+// result is the first column of positive weight where cprev + scale * run
+// exceeds tau, else the last column of positive weight, else 0, and *w_sel
+// receives its weight.
+template <class WFn>
+__device__ __forceinline__ int scan_row_tile_lanes(int n0, double scale, double cprev, double tau, WFn wfn,
+                                                   double* w_sel)
+{
+    const int lane = threadIdx.x & 63;
+    const int vbs = ((lane >> 2) & 3) ^ ((lane >> 4) & 1), e = lane & 3;
+    auto pick = [&](const floatx4(&x)[4]) {
+        floatx4 blk = x[0];
+        blk = vbs == 1 ? x[1] : blk;
+        blk = vbs == 2 ? x[2] : blk;
+        blk = vbs == 3 ? x[3] : blk;
+        float v = blk[0];
+        v = e == 1 ? blk[1] : v;
+        v = e == 2 ? blk[2] : v;
+        v = e == 3 ? blk[3] : v;
+        return v;
+    };
+    const double w = wfn(n0 + lane, pick);
+    const double run = wave_incl_scan(w);
+    const uint64_t mh = __ballot(w > 0.0 && cprev + scale * run > tau);
+    const uint64_t mp = __ballot(w > 0.0);
+    int col = 0;
+    if (mh) col = __builtin_ctzll(mh);
+    else if (mp) col = 63 - __builtin_clzll(mp);
+    const double ws = __shfl(w, col, 64);
+    *w_sel = (mh | mp) ? ws : 0.0;
+    return col;
 }
 
 // Wave 0: inverse-CDF scan of a 64-column tile held as by row_tile_vm.  The

@@ -699,7 +699,7 @@ __global__ __launch_bounds__(64) void k_final_bf16(
         const bool degen = !(wave_last(wave_incl_scan((double)sw)) > 0.0);  // no residual mass: sample p_t
         const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)ks, 2u);
         const Located loc = wave_locate_slices<PER>(
-            i0, [&](int j) { return (double)(degen ? q[j].y : q[j].x); }, u);
+            i0, [&](int j) { return (double)(degen ? q[j].y : q[j].x); }, u, reinterpret_cast<double*>(lds));
 
         const int n0 = loc.idx * kTcols;
         const uint16_t* trow = Tg + ((size_t)b * (gamma + 1) + (ks - 1)) * V;
@@ -713,12 +713,12 @@ __global__ __launch_bounds__(64) void k_final_bf16(
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(row16_block(tv, vb));
         double wsel;
-        const int j = scan_vm_tile(
-            n0, m, 1.0, loc.cprev, loc.tau,
-            [&](int vb, int i, int col) {
+        const int j = scan_row_tile_lanes(
+            n0, 1.0, loc.cprev, loc.tau,
+            [&](int col, auto pick) {
                 if (col >= V) return 0.0;
                 float ptv;
-                const float wr = resid_weight(f[vb][i], tf[vb][i], ld, lt, &ptv);
+                const float wr = resid_weight(pick(f), pick(tf), ld, lt, &ptv);
                 return (double)(degen ? ptv : wr);
             },
             &wsel);
@@ -742,7 +742,8 @@ __global__ __launch_bounds__(64) void k_final_bf16(
             cm[j] = ok ? pm[ci] : -INFINITY;
             cs[j] = ok ? ps[ci] : 0.0;
         }
-        const Located loc = wave_locate_slices<4>(c0l, [&](int j) { return tile_mass(cm[j], cs[j], M); }, u);
+        const Located loc = wave_locate_slices<4>(c0l, [&](int j) { return tile_mass(cm[j], cs[j], M); }, u,
+                                                  reinterpret_cast<double*>(lds));
 
         const float mc = pm[loc.idx];
         const float mcl = row_mlog2(mc);
