@@ -65,35 +65,29 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(const float* __restr
     const int t = threadIdx.x;
     const int N = B * gamma;
 
-    for (int b = t; b < B; b += kSchedThreads) {
-        // All of the row's inputs are loaded before any is used (one memory
-        // round trip, not one per position).
-        float v[kMaxGamma];
-        const float* src = z ? z : surv;
-#pragma unroll
-        for (int kk = 0; kk < kMaxGamma; ++kk)
-            if (kk < gamma) v[kk] = src[b * gamma + kk];
-        if (z) {
-            float tk[kMaxGamma];
-#pragma unroll
-            for (int kk = 0; kk < kMaxGamma; ++kk)
-                if (kk < gamma) tk[kk] = temps[kk];
+    // Inputs (z, or the given survivals) into LDS with coalesced loads, and
+    // the temperatures; then one thread per row runs the product.
+    __shared__ float tsh[kMaxGamma];
+    const float* src = z ? z : surv;
+    for (int i = t; i < N; i += kSchedThreads) keys[i] = __float_as_uint(src[i]);
+    if (z && t < gamma) tsh[t] = temps[t];
+    __syncthreads();
+    if (z) {
+        for (int b = t; b < B; b += kSchedThreads) {
             float th = 1.0f;
-#pragma unroll
-            for (int kk = 0; kk < kMaxGamma; ++kk)
-                if (kk < gamma) {
-                    const float q = v[kk] / tk[kk];
-                    const float c = 1.0f / (1.0f + expf(-q));
-                    th = th * c;
-                    v[kk] = th;
-                }
-#pragma unroll
-            for (int kk = 0; kk < kMaxGamma; ++kk)
-                if (kk < gamma) surv[b * gamma + kk] = v[kk];
+            for (int kk = 0; kk < gamma; ++kk) {
+                const float q = __uint_as_float(keys[b * gamma + kk]) / tsh[kk];
+                const float c = 1.0f / (1.0f + expf(-q));
+                th = th * c;
+                keys[b * gamma + kk] = __float_as_uint(th);  // the row's own slots only
+            }
         }
-#pragma unroll
-        for (int kk = 0; kk < kMaxGamma; ++kk)
-            if (kk < gamma) keys[b * gamma + kk] = order_key(v[kk]);
+        __syncthreads();
+    }
+    for (int i = t; i < N; i += kSchedThreads) {
+        const float v = __uint_as_float(keys[i]);
+        if (z) surv[i] = v;
+        keys[i] = order_key(v);
     }
     __syncthreads();
 
