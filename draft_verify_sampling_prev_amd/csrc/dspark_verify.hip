@@ -45,25 +45,20 @@ __device__ __forceinline__ int cond_token_v(const int32_t* __restrict__ x0, cons
 }
 
 // A log-normaliser split into two floats, hi + lo = lse to ~2^-48 relative.
-struct SplitLse {
-    float hi, lo;
-};
-__device__ __forceinline__ SplitLse split_lse(double v)
-{
-    SplitLse s;
-    s.hi = (float)v;
-    s.lo = (float)(v - (double)s.hi);
-    return s;
-}
+// A row's log-normaliser as the base-2 offset used by resid_weight:
+// c = lse * log2(e), rounded to float.
+__device__ __forceinline__ float lse_log2(double lse) { return (float)(lse * kLog2eD); }
 
 // Residual weight of one vocabulary entry: w = max(0, p_t - p_d) with
-// p = exp((x - hi) - lo) in fp32; *pt receives p_t.  The same expression is
+// p = exp(x - lse) = 2^(x log2 e - c), one FMA and the hardware base-2
+// exponential (the exponent carries an absolute error of a few 1e-6, from
+// rounding log2 e and c to float); *pt receives p_t.  The same expression is
 // used by the residual tile pass and by the final rescan, so the weights the
 // final sample scans are exactly those summed into the tile partials.
-__device__ __forceinline__ float resid_weight(float f, float t, SplitLse d, SplitLse tg, float* pt)
+__device__ __forceinline__ float resid_weight(float f, float t, float cd, float ct, float* pt)
 {
-    const float ptv = exp_fast((t - tg.hi) - tg.lo);
-    const float pdv = exp_fast((f - d.hi) - d.lo);
+    const float ptv = __builtin_amdgcn_exp2f(__builtin_fmaf(t, kLog2e, -ct));
+    const float pdv = __builtin_amdgcn_exp2f(__builtin_fmaf(f, kLog2e, -cd));
     *pt = ptv;
     const float w = ptv - pdv;
     return w > 0.0f ? w : 0.0f;
@@ -313,8 +308,8 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
             const int row = mw0 + 16 * mb + 4 * (lane >> 4) + i;
             const ResidRow rr = resid_row(resid_list, min(row, cnt - 1), B, gamma, V);
             const float* trow = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
-            const SplitLse ld = split_lse(lse_d[(size_t)rr.b * gamma + rr.ks - 1]);
-            const SplitLse lt = split_lse(lse_t[(size_t)rr.b * gamma + rr.ks - 1]);
+            const float ld = lse_log2(lse_d[(size_t)rr.b * gamma + rr.ks - 1]);
+            const float lt = lse_log2(lse_t[(size_t)rr.b * gamma + rr.ks - 1]);
             double sw = 0.0, sp = 0.0;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
@@ -378,7 +373,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     const uint16_t* trow[2];
     const uint16_t* arow[2];
     int lrow_idx[2];
-    SplitLse ld[2], lt[2];
+    float ld[2], lt[2];
     int4 rec[2];  // the rows' records (decoded after the first Bm tile is issued)
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) rec[bb] = resid_list[min(m0 + row_of(bb) + c, cntr - 1)];
@@ -499,8 +494,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     issue_fence();
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-        ld[bb] = split_lse(lsd[bb]);
-        lt[bb] = split_lse(lst[bb]);
+        ld[bb] = lse_log2(lsd[bb]);
+        lt[bb] = lse_log2(lst[bb]);
     }
     // Tile 0 is peeled off the loop (see the draft tile kernel).
     body(0, s0, s3, l0, t0r, l1, t1r);
@@ -567,8 +562,8 @@ __global__ __launch_bounds__(kThreads) void k_final(
         const T* trow = Tg + ((size_t)b * (gamma + 1) + (ks - 1)) * V;
         const T* lrow = L + ((size_t)b * gamma + (ks - 1)) * V;
         const int prev = cond_token_v(x0, tok, b, gamma, ks, V);
-        const SplitLse ld = split_lse(lse_d[(size_t)b * gamma + ks - 1]);
-        const SplitLse lt = split_lse(lse_t[(size_t)b * gamma + ks - 1]);
+        const float ld = lse_log2(lse_d[(size_t)b * gamma + ks - 1]);
+        const float lt = lse_log2(lse_t[(size_t)b * gamma + ks - 1]);
         auto weight = [&](float fv, float tv) {
             float ptv;
             const float wr = resid_weight(fv, tv, ld, lt, &ptv);
@@ -707,8 +702,8 @@ __global__ __launch_bounds__(64) void k_final_bf16(
         load_row16(trow, n0, V, false, tv);
         floatx4 f[4];
         row_tile_vm_wave<KS>(L + ((size_t)b * gamma + (ks - 1)) * V, af, Bm, V, r, n0, lds, f);
-        const SplitLse ld = split_lse(lse_d[(size_t)b * gamma + ks - 1]);
-        const SplitLse lt = split_lse(lse_t[(size_t)b * gamma + ks - 1]);
+        const float ld = lse_log2(lse_d[(size_t)b * gamma + ks - 1]);
+        const float lt = lse_log2(lse_t[(size_t)b * gamma + ks - 1]);
         floatx4 tf[4];
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(row16_block(tv, vb));
