@@ -47,6 +47,7 @@ WsLayout ws_layout(int B, int gamma, int V)
     l.res_part = take(Bz * nT * 8);
     l.bon_m = take(Bz * nC * 4);
     l.bon_s = take(Bz * nC * 8);
+    l.ag = take(((Bz + 15) / 16) * 16 * (size_t)kAgRank * 2);
     l.total = o;
     return l;
 }

@@ -154,8 +154,8 @@ constexpr int kPartTiles = 12;  // tiles per slot whose partials fit the LDS sta
 template <int KS>
 __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
-    const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, int B, int gamma, int V, int r, int k, int nT,
-    int nM, int S, float2* __restrict__ part)
+    const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const uint16_t* __restrict__ ag, int B,
+    int gamma, int V, int r, int k, int nT, int nM, int S, float2* __restrict__ part)
 {
     constexpr int NW = kTileWaves, R = kTileRows;
     __shared__ __attribute__((aligned(1024))) char s0[kBmTileBytes];
@@ -245,16 +245,31 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     // Prologue: the conditioning tokens are loaded first (the oldest loads,
     // so waiting for them does not wait for the tile loads behind them), then
     // only the first tile; the tokens are used (clamped) only after that, and
-    // then the A-operand gather is issued.
-    int tk[2];
+    // then the A-operand gather is issued.  With `ag` (written by the previous
+    // step's locate kernel, rank 256) the A operand is read from there instead,
+    // 1 KB contiguous per load, and no token is read.
+    // (Two separate paths: a token load pending on one side of a join would
+    // make the compiler wait for every load at the join.)
+    auto first_tile = [&]() {
+        issue_fence();
+        load_l(0, l0);
+        issue_fence();
+        dma(0, s0);
+        issue_fence();
+    };
+    if (ag) {
+        first_tile();
+        const int last_blk = (B - 1) >> 4;  // blocks past the batch read the last one (rows never reported)
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) tk[bb] = cond_token_raw(x0, tok, min(mw + 16 * bb + c, B - 1), gamma, k);
-    issue_fence();
-    load_l(0, l0);
-    issue_fence();
-    dma(0, s0);
-    issue_fence();
-    {
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+                a[bb][ks] = ld16(ag + ag_offset(16 * min((mw >> 4) + bb, last_blk), ks, 0) + (size_t)lane * 8);
+    } else {
+        int tk[2];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) tk[bb] = cond_token_raw(x0, tok, min(mw + 16 * bb + c, B - 1), gamma, k);
+        first_tile();
         const uint16_t* arow[2] = { A + (size_t)clamp_token(tk[0], V) * r, A + (size_t)clamp_token(tk[1], V) * r };
         load_a_frags<2>(arow, r, a);
     }
@@ -356,16 +371,22 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
 // loads in flight at once; the partials are combined with wave scans (no
 // barriers, no LDS) by the same rule as locate(); the chosen tile is
 // recomputed by the wave alone from its own LDS copy of the Bm tile.
-template <int KS, int PER>
+template <int KS, int PER, bool AG>
 __global__ __launch_bounds__(64) void k_draft_locate_bf16(const uint16_t* __restrict__ L,
                                                           const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ Bm,
                                                           const int32_t* __restrict__ x0, int32_t* tok,
                                                           float* __restrict__ p_out, double* __restrict__ lse_out,
-                                                          const float2* __restrict__ part, int B, int gamma, int V,
-                                                          int r, int k, int nT, uint64_t seed)
+                                                          const float2* __restrict__ part, uint16_t* __restrict__ ag,
+                                                          int B, int gamma, int V, int r, int k, int nT,
+                                                          uint64_t seed)
 {
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
+    // With AG (rank 256): the A rows of the chosen tile's 64 columns, the
+    // candidates for the sampled token, DMA'd alongside the Bm tile; the
+    // sampled one is copied into `ag` in MFMA order for the next step's tile
+    // kernel, with no memory round trip after the sample.
+    __shared__ __attribute__((aligned(1024))) char lds_a[AG ? kBmTileBytes : 1024];
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     // The partial loads go first: the A-operand loads wait for the token.
@@ -406,7 +427,18 @@ __global__ __launch_bounds__(64) void k_draft_locate_bf16(const uint16_t* __rest
     // hides behind the tile's own loads).
     const float mt = pr[idx].x;
     floatx4 f[4];
-    row_tile_vm_wave<KS>(L + ((size_t)b * gamma + (k - 1)) * V, a, Bm, V, r, n0, lds, f);
+    auto dma_candidates = [&]() {
+        if constexpr (AG) {
+            // Rows n0 .. n0+63 of A are 32 KB contiguous; rows past V read the last 16 bytes of A.
+            const int n0u = __builtin_amdgcn_readfirstlane(n0);
+            const uint32_t lim = V - n0u >= 64 ? 32768u - 16u : (uint32_t)(V - n0u) * (kAgRank * 2) - 16u;
+            const uint16_t* base = A + (size_t)n0u * kAgRank;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) dma16(base, min((uint32_t)(i * 1024 + lane * 16), lim), lds_a + i * 1024);
+        }
+    };
+    row_tile_vm_wave<KS, AG ? 32 : 0>(L + ((size_t)b * gamma + (k - 1)) * V, a, Bm, V, r, n0, lds, f,
+                                      dma_candidates);
     const double scale = tile_mass(mt, 1.0, M);
     const float ml = row_mlog2(mt);
     double wsel;
@@ -414,8 +446,16 @@ __global__ __launch_bounds__(64) void k_draft_locate_bf16(const uint16_t* __rest
         n0, scale, cprev, tau,
         [&](int col, auto pick) { return col < V && mt != -INFINITY ? (double)softmax_w(pick(f), ml) : 0.0; },
         &wsel);
+    const int xk = min(n0 + j, V - 1);
+    if constexpr (AG) {
+        wait_all_mem();   // the candidate rows
+        if (lane < 32) {  // piece (ks, G) = (lane >> 2, lane & 3) of A[xk]: elements 8 * lane .. +7
+            const uint4 v = *reinterpret_cast<const uint4*>(lds_a + (xk - n0) * (kAgRank * 2) + lane * 16);
+            *reinterpret_cast<uint4*>(ag + ag_offset(b, lane >> 2, lane & 3)) = v;
+        }
+    }
     if (lane == 0) {
-        tok[b * gamma + (k - 1)] = min(n0 + j, V - 1);
+        tok[b * gamma + (k - 1)] = xk;
         p_out[b * gamma + (k - 1)] = (float)(scale * wsel / S);
         lse_out[b * gamma + (k - 1)] = (double)M + log(S);
     }
@@ -426,15 +466,21 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
                              void* ws, const WsLayout& lay, hipStream_t s)
 {
     float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.draft_part);
+    uint16_t* ag = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.ag);
     const int nT = n_tiles(dtype, V);
+    // The one-wave locate (bf16, up to 4096 tiles) hands the next step its A
+    // rows in MFMA order when the rank is 256.
+    const bool wave_locate = dtype == 1 && nT <= 64 * 64;
+    const bool ag_path = wave_locate && r == kAgRank;
     prof_begin(K_DRAFT_TILES, s);
     if (dtype == 1) {
         const int nM = (B + kTileRows - 1) / kTileRows;
         const int S = std::min(nT, std::max((cu_count() + nM - 1) / nM, (nT + kPartTiles - 1) / kPartTiles));
         auto kern = (r + 31) / 32 == 8 ? k_draft_tiles_bf16<8> : k_draft_tiles_bf16<0>;
         hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s, static_cast<const uint16_t*>(L),
-                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, B, gamma, V,
-                           r, k, nT, nM, S, part);
+                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok,
+                           static_cast<const uint16_t*>(ag_path && k >= 2 ? ag : nullptr), B, gamma, V, r, k, nT, nM,
+                           S, part);
     } else {
         const int nM = (B + 255) / 256;
         hipLaunchKernelGGL(k_draft_tiles_f32, dim3(nT * nM), dim3(kThreads), 0, s, static_cast<const float*>(L),
@@ -443,13 +489,15 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     }
     prof_end(K_DRAFT_TILES, s);
     prof_begin(K_DRAFT_LOCATE, s);
-    if (dtype == 1 && nT <= 64 * 64) {
-        const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32;
-        auto kern = small ? (k8 ? k_draft_locate_bf16<8, 32> : k_draft_locate_bf16<0, 32>)
-                          : (k8 ? k_draft_locate_bf16<8, 64> : k_draft_locate_bf16<0, 64>);
+    if (wave_locate) {
+        const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32, wag = ag_path && k < gamma;
+        auto kern = small ? (k8 ? (wag ? k_draft_locate_bf16<8, 32, true> : k_draft_locate_bf16<8, 32, false>)
+                                : k_draft_locate_bf16<0, 32, false>)
+                          : (k8 ? (wag ? k_draft_locate_bf16<8, 64, true> : k_draft_locate_bf16<8, 64, false>)
+                                : k_draft_locate_bf16<0, 64, false>);
         hipLaunchKernelGGL(kern, dim3(B), dim3(64), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
-                           B, gamma, V, r, k, nT, seed);
+                           ag, B, gamma, V, r, k, nT, seed);
     } else if (dtype == 1) {
         hipLaunchKernelGGL(k_draft_locate<Bf16>, dim3(B), dim3(kThreads), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,

@@ -18,6 +18,10 @@ inline int tile_cols(int dtype) { return dtype == 1 ? 64 : 128; }
 inline int n_tiles(int dtype, int V) { return (V + tile_cols(dtype) - 1) / tile_cols(dtype); }
 inline int n_chunks(int V) { return (V + kChunkElems - 1) / kChunkElems; }
 
+// Rank of the Markov factors whose draft steps hand the next step its A rows
+// in MFMA order (the "ag" workspace region, see dspark_tile.hpp).
+constexpr int kAgRank = 256;
+
 // Byte offsets into the caller's workspace (each 256-byte aligned).
 struct WsLayout {
     size_t draft_part;            // [B][nT] float2 : draft tile max and sum of exp(f - max)
@@ -29,6 +33,7 @@ struct WsLayout {
     size_t resid_count;           // [1] i32
     size_t res_part;              // [B][nT] float2 : per tile sum of max(0, p_t - p_d) and of p_t
     size_t bon_m, bon_s;          // [B][nC] f32 / f64 : bonus-row chunk max and sum of exp
+    size_t ag;                    // [ceil(B/16)*16][256] bf16 : the next draft step's A rows, MFMA order (rank 256)
     size_t total;
 };
 

@@ -174,14 +174,24 @@ __device__ __forceinline__ void row_tile_vm(const uint16_t* L_row, const uint16_
 // wave stages the Bm tile in its own LDS buffer and waits only for its own
 // loads (no barrier).  The A operand (a, k steps < nks) is loaded by the
 // caller ahead of time.
-template <int KS>
+struct NoExtraLoads {
+    __device__ __forceinline__ void operator()() const {}
+};
+// `extra` issues NEXTRA more vector-memory loads of the caller's behind the
+// tile's; they stay in flight (the caller waits for them).
+template <int KS, int NEXTRA = 0, class Extra = NoExtraLoads>
 __device__ __forceinline__ void row_tile_vm_wave(const uint16_t* L_row, const uint4 (&a)[1][8], const uint16_t* Bm,
-                                                 int V, int r, int n0, char* lds, floatx4 (&f)[4])
+                                                 int V, int r, int n0, char* lds, floatx4 (&f)[4],
+                                                 Extra extra = Extra{})
 {
     dma_bm_tile<1>(Bm, V, r, n0, false, lds);
     uint4 lv[2];
     load_row16(L_row, n0, V, false, lv);
-    wait_all_mem();
+    issue_fence();
+    extra();
+    issue_fence();
+    if constexpr (NEXTRA == 0) wait_all_mem();
+    else wait_vmem<NEXTRA>();  // loads complete in order: the tile's (and everything older) have landed
     floatx4 acc[4][1];
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(row16_block(lv, vb));
@@ -274,21 +284,33 @@ __device__ __forceinline__ void load_slices(const float2* __restrict__ row, int 
 // result is the first column of positive weight where cprev + scale * run
 // exceeds tau, else the last column of positive weight, else 0, and *w_sel
 // receives its weight.
+// Lanes L whose tile column L is held in stored block vb.
+constexpr uint64_t scan_lanes_of_block(int vb)
+{
+    uint64_t m = 0;
+    for (int L = 0; L < 64; ++L)
+        if ((((L >> 2) & 3) ^ ((L >> 4) & 1)) == vb) m |= 1ull << L;
+    return m;
+}
+
 template <class WFn>
 __device__ __forceinline__ int scan_row_tile_lanes(int n0, double scale, double cprev, double tau, WFn wfn,
                                                    double* w_sel)
 {
     const int lane = threadIdx.x & 63;
-    const int vbs = ((lane >> 2) & 3) ^ ((lane >> 4) & 1), e = lane & 3;
+    // Lane L needs element L & 3 of block ((L >> 2) & 3) ^ ((L >> 4) & 1):
+    // selects with compile-time lane masks.
     auto pick = [&](const floatx4(&x)[4]) {
         floatx4 blk = x[0];
-        blk = vbs == 1 ? x[1] : blk;
-        blk = vbs == 2 ? x[2] : blk;
-        blk = vbs == 3 ? x[3] : blk;
+#pragma unroll
+        for (int vb = 1; vb < 4; ++vb) {
+            const uint64_t m = scan_lanes_of_block(vb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) blk[i] = lane_select(blk[i], x[vb][i], m);
+        }
         float v = blk[0];
-        v = e == 1 ? blk[1] : v;
-        v = e == 2 ? blk[2] : v;
-        v = e == 3 ? blk[3] : v;
+#pragma unroll
+        for (int i = 1; i < 4; ++i) v = lane_select(v, blk[i], 0x1111111111111111ull << i);
         return v;
     };
     const double w = wfn(n0 + lane, pick);

@@ -167,6 +167,16 @@ __device__ __forceinline__ void load_a_frags(const uint16_t* const (&arow)[NBB],
     }
 }
 
+// The conditioning rows' A vectors in MFMA B-operand order ("Ag"), for rank
+// 256: row R's 16-byte piece (k step ks, lane group G), A[x_R][32ks + 8G ..
+// +7], lives at element ag_offset(R, ks, G), so the wave holding rows
+// 16j .. 16j+15 as one batch block reads each k step as 1 KB contiguous
+// (the gather from A reads half cache lines of 16 scattered rows instead).
+__device__ __forceinline__ size_t ag_offset(int R, int ks, int G)
+{
+    return ((size_t)((R >> 4) * 8 + ks) * 64 + 16 * G + (R & 15)) * 8;
+}
+
 // Four bf16 values (8 bytes) -> floats.
 __device__ __forceinline__ floatx4 bf16x4_to_f32(uint2 v)
 {
@@ -193,14 +203,30 @@ __device__ __forceinline__ void load_row16(const uint16_t* __restrict__ row, int
     for (int h = 0; h < 2; ++h) raw[h] = ld16(row + (min(n0 + 16 * G + 8 * h, V - 8) & keep));
 }
 
+// Per-lane select with a compile-time lane mask: lanes whose bit is set in
+// `mask` take b, the others a.  Written as one v_cndmask so the compiler
+// cannot turn a chain of lane-dependent selects over a register array into
+// an indexed access (which it may place in scratch memory).
+__device__ __forceinline__ uint32_t lane_select(uint32_t a, uint32_t b, uint64_t mask)
+{
+    uint32_t r;
+    asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+    return r;
+}
+__device__ __forceinline__ float lane_select(float a, float b, uint64_t mask)
+{
+    return __uint_as_float(lane_select(__float_as_uint(a), __float_as_uint(b), mask));
+}
+// Lanes of odd lane group G = lane >> 4 (16..31, 48..63).
+constexpr uint64_t kOddGroupLanes = 0xFFFF0000FFFF0000ull;
+
 // Columns n0 + vm_col(G, vb) .. +3 (accumulator block vb) from load_row16's
 // registers: for odd G the two 8-byte halves of each 16-byte load trade places.
 __device__ __forceinline__ uint2 row16_block(const uint4 (&raw)[2], int vb)
 {
-    const bool odd = (((threadIdx.x & 63) >> 4) & 1) != 0;
     const uint4 x = raw[vb >> 1];
-    const bool high = ((vb & 1) != 0) != odd;
-    return high ? make_uint2(x.z, x.w) : make_uint2(x.x, x.y);
+    const uint64_t high = (vb & 1) ? ~kOddGroupLanes : kOddGroupLanes;  // lanes taking the upper half
+    return make_uint2(lane_select(x.x, x.z, high), lane_select(x.y, x.w, high));
 }
 
 template <int NBB, int KS>

@@ -46,6 +46,18 @@ def test_ragged_tiles_and_rank(dtype):
     _run_and_check(wl)
 
 
+def test_rank256_ragged_batch_and_vocab():
+    # r = 256: each draft step hands the next one its A rows in MFMA order.
+    # B = 37 leaves a partial 16-row block, V = 3000 a partial 64-column tile.
+    _run_and_check(synth.tiny(B=37, gamma=4, V=3000, r=256, budget=100, dtype="bf16"))
+
+
+def test_rank256_two_row_blocks():
+    # B = 300 at r = 256: two 256-row blocks in the tile kernels, the second ragged.
+    wl = synth.tiny(B=300, gamma=3, V=2048, r=256, budget=600, dtype="bf16")
+    _run_and_check(wl, requests=range(0, 300, 5))
+
+
 @pytest.mark.parametrize("B,gamma,budget", [(1, 1, 1), (1, 16, 7), (3, 16, 48), (17, 2, 0), (9, 4, 10**9)])
 def test_edge_shapes_and_budgets(B, gamma, budget):
     wl = synth.tiny(B=B, gamma=gamma, V=256, r=8, budget=budget, dtype="bf16")
