@@ -102,6 +102,44 @@ def test_qwen_shape_sampled():
     _run_and_check(wl, draft_rows=rows, requests=range(0, wl.B, 3))
 
 
+def _sample(wl, rng_seed, n=16):
+    g = np.random.default_rng(rng_seed)
+    rows = [(int(b), int(k)) for b, k in zip(g.integers(0, wl.B, n), g.integers(1, wl.gamma + 1, n))]
+    rows += [(0, 1), (wl.B - 1, wl.gamma)]
+    reqs = sorted(set(int(b) for b in g.integers(0, wl.B, n)) | {0, wl.B - 1})
+    return rows, reqs
+
+
+@pytest.mark.parametrize("gamma", [4, 8, 12, 16])
+def test_long_block_sampled(gamma):
+    """Long-block sweep point: B=128, V=151936, r=256, bf16, every drafted token verified."""
+    wl = synth.long_block(gamma)
+    rows, reqs = _sample(wl, 100 + gamma)
+    out, _ = _run_and_check(wl, draft_rows=rows, requests=reqs)
+    assert np.all(out["ell"] == gamma)  # unbounded budget
+
+
+_LOAD_SWEEP_INPUTS = {}
+
+
+@pytest.mark.parametrize("mult", [1, 2, 4, 8])
+def test_load_sweep_sampled(mult):
+    """Load-sweep point: B=1024, gamma=8, V=129280, r=256, bf16, budget mult*B (four 256-row blocks)."""
+    wl = synth.load_sweep(1024 * mult)
+    if not _LOAD_SWEEP_INPUTS:  # the inputs do not depend on the budget
+        _LOAD_SWEEP_INPUTS["inp"] = synth.make_inputs(wl)
+    inp = _LOAD_SWEEP_INPUTS["inp"]
+    print(f"case {wl.describe()} seed={wl.philox_seed:#x}", flush=True)
+    out = run_step(inp, wl.budget, wl.philox_seed)
+    structural_checks(out, wl.gamma)
+    assert int(out["ell"].sum()) == min(wl.budget, wl.B * wl.gamma)
+    rows, reqs = _sample(wl, 200 + mult)
+    rep = check_step(inp, out, wl.budget, wl.philox_seed, draft_rows=rows, requests=reqs)
+    print("  ", rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep.draft_flips + rep.accept_flips + rep.final_flips <= MAX_FLIPS
+
+
 def test_run_to_run_determinism():
     wl = synth.tiny(B=64, gamma=5, V=8192, r=64, budget=200, dtype="bf16")
     inp = synth.make_inputs(wl)
