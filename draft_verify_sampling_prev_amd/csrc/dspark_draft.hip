@@ -138,10 +138,9 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
 // unrolled so every copy reads and fills fixed buffers):
 //   wait until Bm tile i has landed, barrier;
 //   load the L values of tile i+1 into registers, DMA Bm tile i+3;
-//   acc = L values of tile i, MFMAs over Bm tile i, then the epilogue (row
-//   max and sum of exp) of tile i-1, written to LDS staging.  (Measured on
-//   MI355X: running the two phases in opposite orders in the two halves of
-//   the workgroup was slower.)
+//   the epilogue (row max and sum of exp) of tile i-1, written to LDS
+//   staging, while tile i's L values arrive; then acc = L values of tile i
+//   and the MFMAs over Bm tile i.
 // Every iteration issues the same number of loads (past the last tile they
 // are dummies reading one location), so the wait for Bm tile i is a constant
 // count of outstanding loads per wave (wait_stage).
@@ -226,14 +225,20 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
         dma(i + 3, nxt);
         issue_fence();
         if (active) {
+            // The previous tile's epilogue first: it needs no memory, so it
+            // runs while this tile's L values are still arriving.  (Measured
+            // on MI355X: giving the two waves of a SIMD opposite phase orders
+            // was slower.)
+            if constexpr (decltype(has_prev)::value) {
+                epilogue(std::false_type{});
+                issue_fence();
+            }
             floatx4 acc[4][2];
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(row16_block(lc[bb], vb));
             tile_mma_vm<2, KS>(a, cur, nks, acc);
-            if constexpr (decltype(has_prev)::value)
-                epilogue(std::false_type{});  // previous tile; independent of the MFMAs above
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
@@ -371,17 +376,60 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
 // loads in flight at once; the partials are combined with wave scans (no
 // barriers, no LDS) by the same rule as locate(); the chosen tile is
 // recomputed by the wave alone from its own LDS copy of the Bm tile.
+// First tile of the next step's tile kernel, read ahead into L2.  Workgroup
+// b of this launch and workgroup b of the tile launch that follows it are
+// both placed on XCD b mod 8 (workgroups are dispatched to the XCDs
+// round-robin by index), so when the AG locate's second wave reads the 256
+// L rows and the 256 Bm rows of that workgroup's first tile (64 KB, by LDS
+// DMA into a kilobyte nothing reads), the tile kernel finds them in its XCD's
+// L2 instead of starting with a full HBM round trip.  Addresses are clamped
+// into the arrays as the tile kernel clamps them (rows past the batch read the
+// last row; columns stop at V - 8).
+__device__ __forceinline__ void prefetch_first_tile(const uint16_t* __restrict__ L, const uint16_t* __restrict__ Bm,
+                                                    int b, int B, int gamma, int V, int k_next, int nT, int nM,
+                                                    int S, char* sink)
+{
+    const int G = S * nM;
+    if (b >= G) return;
+    const int lid = xcd_logical_id(b, G);
+    const int mblk = lid % nM, slot = lid / nM;
+    int t0, ts, cnt;
+    slot_tiles(slot, S, nT, &t0, &ts, &cnt);
+    if (cnt <= 0) return;
+    const int lane = threadIdx.x & 63;
+    const int col = min(t0 * kTcols + 8 * (lane & 7), V - 8);
+#pragma unroll 4
+    for (int i = 0; i < kTileRows / 8; ++i) {
+        const int rb = min(mblk * kTileRows + 8 * i, B - 1);  // wave-uniform
+        const int row = min(mblk * kTileRows + 8 * i + (lane >> 3), B - 1);
+        dma16(L + ((size_t)rb * gamma + (k_next - 1)) * V,
+              (uint32_t)(((size_t)(row - rb) * gamma * V + col) * 2), sink);
+    }
+#pragma unroll 4
+    for (int i = 0; i < kAgRank / 8; ++i) dma16(Bm + (size_t)(8 * i) * V, (uint32_t)(((lane >> 3) * V + col) * 2), sink);
+    wait_all_mem();
+}
+
 template <int KS, int PER, bool AG>
-__global__ __launch_bounds__(64) void k_draft_locate_bf16(const uint16_t* __restrict__ L,
+__global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __restrict__ L,
                                                           const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ Bm,
                                                           const int32_t* __restrict__ x0, int32_t* tok,
                                                           float* __restrict__ p_out, double* __restrict__ lse_out,
                                                           const float2* __restrict__ part, uint16_t* __restrict__ ag,
-                                                          int B, int gamma, int V, int r, int k, int nT,
-                                                          uint64_t seed)
+                                                          int B, int gamma, int V, int r, int k, int nT, int nM_next,
+                                                          int S_next, uint64_t seed)
 {
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
+    // AG (not the last step): a second wave reads the next tile launch's
+    // first tile ahead; it shares nothing with the first wave.
+    if (threadIdx.x >= 64) {
+        if constexpr (AG) {
+            __shared__ __attribute__((aligned(1024))) char sink[1024];
+            prefetch_first_tile(L, Bm, blockIdx.x, B, gamma, V, k + 1, nT, nM_next, S_next, sink);
+        }
+        return;
+    }
     // With AG (rank 256): the A rows of the chosen tile's 64 columns, the
     // candidates for the sampled token, DMA'd alongside the Bm tile; the
     // sampled one is copied into `ag` in MFMA order for the next step's tile
@@ -472,20 +520,21 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     // rows in MFMA order when the rank is 256.
     const bool wave_locate = dtype == 1 && nT <= 64 * 64;
     const bool ag_path = wave_locate && r == kAgRank;
+    // bf16 tile grid: nM row blocks x S persistent slots.
+    const int nM = (B + kTileRows - 1) / kTileRows;
+    const int S = std::min(nT, std::max((cu_count() + nM - 1) / nM, (nT + kPartTiles - 1) / kPartTiles));
     prof_begin(K_DRAFT_TILES, s);
     if (dtype == 1) {
-        const int nM = (B + kTileRows - 1) / kTileRows;
-        const int S = std::min(nT, std::max((cu_count() + nM - 1) / nM, (nT + kPartTiles - 1) / kPartTiles));
         auto kern = (r + 31) / 32 == 8 ? k_draft_tiles_bf16<8> : k_draft_tiles_bf16<0>;
         hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok,
                            static_cast<const uint16_t*>(ag_path && k >= 2 ? ag : nullptr), B, gamma, V, r, k, nT, nM,
                            S, part);
     } else {
-        const int nM = (B + 255) / 256;
-        hipLaunchKernelGGL(k_draft_tiles_f32, dim3(nT * nM), dim3(kThreads), 0, s, static_cast<const float*>(L),
+        const int nM32 = (B + 255) / 256;
+        hipLaunchKernelGGL(k_draft_tiles_f32, dim3(nT * nM32), dim3(kThreads), 0, s, static_cast<const float*>(L),
                            static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, B, gamma, V, r, k,
-                           nT, nM, part);
+                           nT, nM32, part);
     }
     prof_end(K_DRAFT_TILES, s);
     prof_begin(K_DRAFT_LOCATE, s);
@@ -495,9 +544,9 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
                                 : k_draft_locate_bf16<0, 32, false>)
                           : (k8 ? (wag ? k_draft_locate_bf16<8, 64, true> : k_draft_locate_bf16<8, 64, false>)
                                 : k_draft_locate_bf16<0, 64, false>);
-        hipLaunchKernelGGL(kern, dim3(B), dim3(64), 0, s, static_cast<const uint16_t*>(L),
+        hipLaunchKernelGGL(kern, dim3(B), dim3(wag ? 128 : 64), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
-                           ag, B, gamma, V, r, k, nT, seed);
+                           ag, B, gamma, V, r, k, nT, nM, S, seed);
     } else if (dtype == 1) {
         hipLaunchKernelGGL(k_draft_locate<Bf16>, dim3(B), dim3(kThreads), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,

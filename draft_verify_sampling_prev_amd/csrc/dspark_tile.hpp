@@ -236,25 +236,37 @@ __device__ __forceinline__ void tile_mma_vm(const uint4 (&a)[NBB][8], const char
     int off[4];
     bm_lane_offsets(off);
     if constexpr (KS > 0) {
-        // The Bm^T fragments of k step ks+1 are read while the MFMAs of step ks run.
-        bf16x8 b[4], bn[4];
+        // The Bm^T fragments of k step ks+2 are read while the MFMAs of step
+        // ks run: two steps of MFMAs cover the LDS latency of a workgroup
+        // whose eight waves all read at once.
+        bf16x8 b[4], b1[4], bn[4];
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb) b[vb] = bm_frag(bufB, off, 0, vb);
+        if (KS > 1) {
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb) b1[vb] = bm_frag(bufB, off, 1, vb);
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) {
+            if (ks + 2 < KS) {
 #pragma unroll
-                for (int vb = 0; vb < 4; ++vb) bn[vb] = bm_frag(bufB, off, ks + 1, vb);
+                for (int vb = 0; vb < 4; ++vb) bn[vb] = bm_frag(bufB, off, ks + 2, vb);
             }
+            // Keep the reads of step ks+2 ahead of the MFMAs of step ks (the
+            // scheduler would otherwise sink each read next to its use);
+            // VALU, SALU and transcendental work may still move across.
+            __builtin_amdgcn_sched_barrier(0x0406);
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
                 for (int bb = 0; bb < NBB; ++bb)
                     acc[vb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         b[vb], __builtin_bit_cast(bf16x8, a[bb][ks]), acc[vb][bb], 0, 0, 0);
-            if (ks + 1 < KS) {
+            __builtin_amdgcn_sched_barrier(0x0406);
 #pragma unroll
-                for (int vb = 0; vb < 4; ++vb) b[vb] = bn[vb];
+            for (int vb = 0; vb < 4; ++vb) {
+                b[vb] = b1[vb];
+                b1[vb] = bn[vb];
             }
         }
     } else {
@@ -340,14 +352,56 @@ __device__ __forceinline__ void slot_tiles(int s, int S, int nT, int* t0, int* t
     *cnt = q + (s < rem ? 1 : 0);
 }
 
+// Butterfly steps across 16-lane rows without LDS: the gfx950 permlane swaps
+// exchange rows 0<->1 and 2<->3 (xor 16) or the wave halves (xor 32), so
+// every lane sees its own value and its partner's.  Both lanes of a pair get
+// op(a, b) of the same two values; for max and add the operand order does
+// not change the result, so the pair ends with identical bits.
+__device__ __forceinline__ void xor16_pair(float x, float* a, float* b)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    *a = __uint_as_float(p[0]);
+    *b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void xor32_pair(float x, float* a, float* b)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    *a = __uint_as_float(p[0]);
+    *b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor16_32(float s)
+{
+    float a, b;
+    xor16_pair(s, &a, &b);
+    xor32_pair(a + b, &a, &b);
+    return a + b;
+}
+// max of two floats as one v_max_f32 (fmaxf would first quiet the operands,
+// which the compiler cannot prove canonical after a lane swap; the values
+// here are logits or -inf, never NaN).
+__device__ __forceinline__ float vmax(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float max_xor16_32(float m)
+{
+    float a, b;
+    xor16_pair(m, &a, &b);
+    xor32_pair(vmax(a, b), &a, &b);
+    return vmax(a, b);
+}
+
 // Row-wise max and sum of exp over the 64 columns of a tile held as 16
 // values per lane (lanes c, c+16, c+32, c+48 hold one row).  With TAIL,
 // values of columns at or past ncol count as absent (without it the code has
 // no branch, so the compiler can interleave it with independent MFMAs).  All
 // four lanes of the row receive the same bits: the max m (-inf if no finite
-// value) and s = sum exp(f - m) (fp32, fixed order: within the lane in block
-// order, then the xor-16 and xor-32 butterflies, whose operand swaps do not
-// change a floating-point add or max).
+// value) and s = sum exp(f - m) (fp32, fixed order: per 4-column block in
+// column order, the four block sums pairwise, then the xor-16 and xor-32
+// butterflies).  Short dependency chains, and no LDS traffic, so the work
+// fills the issue slots between independent MFMAs.
 template <bool TAIL>
 __device__ __forceinline__ void row64_max_sum(floatx4 (&v)[4], int ncol, float* m_out, float* s_out)
 {
@@ -357,23 +411,21 @@ __device__ __forceinline__ void row64_max_sum(floatx4 (&v)[4], int ncol, float* 
         for (int vb = 0; vb < 4; ++vb)
             if (vm_col(G, vb) >= ncol) v[vb] = floatx4{ -INFINITY, -INFINITY, -INFINITY, -INFINITY };
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, v[vb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Three-input maxima, depth 3.
+    const float t0 = fmaxf(fmaxf(v[0][0], v[0][1]), v[0][2]), t1 = fmaxf(fmaxf(v[0][3], v[1][0]), v[1][1]);
+    const float t2 = fmaxf(fmaxf(v[1][2], v[1][3]), v[2][0]), t3 = fmaxf(fmaxf(v[2][1], v[2][2]), v[2][3]);
+    const float t4 = fmaxf(fmaxf(v[3][0], v[3][1]), v[3][2]);
+    const float mx = max_xor16_32(fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), v[3][3])));
     const float ml = row_mlog2(mx);
-    float s = 0.0f;
+    float sb[4];
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+    for (int vb = 0; vb < 4; ++vb) {
+        sb[vb] = softmax_w(v[vb][0], ml);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s += softmax_w(v[vb][i], ml);
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
+        for (int i = 1; i < 4; ++i) sb[vb] += softmax_w(v[vb][i], ml);
+    }
     *m_out = mx;
-    *s_out = s;
+    *s_out = sum_xor16_32((sb[0] + sb[1]) + (sb[2] + sb[3]));
 }
 
 }  // namespace dspark

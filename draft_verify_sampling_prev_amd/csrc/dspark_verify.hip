@@ -396,22 +396,22 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
         constexpr int NBB = decltype(nbb)::value;
 #pragma unroll
         for (int bb = 0; bb < NBB; ++bb) {
-            float sw = 0.0f, sp = 0.0f;
+            // Per 4-column block in column order, the block sums pairwise, then
+            // the xor-16 / xor-32 butterflies (short chains, no LDS).
+            float sw[4], sp[4];
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb) {
                 const floatx4 t = bf16x4_to_f32(row16_block(tv[bb], vb));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float ptv;
-                    sw += resid_weight(f[vb][bb][e], t[e], ld[bb], lt[bb], &ptv);
-                    sp += ptv;
+                    const float w = resid_weight(f[vb][bb][e], t[e], ld[bb], lt[bb], &ptv);
+                    sw[vb] = e == 0 ? w : sw[vb] + w;
+                    sp[vb] = e == 0 ? ptv : sp[vb] + ptv;
                 }
             }
-            sw += __shfl_xor(sw, 16, 64);
-            sw += __shfl_xor(sw, 32, 64);
-            sp += __shfl_xor(sp, 16, 64);
-            sp += __shfl_xor(sp, 32, 64);
-            stage[i][row_of(bb) + c] = pack_f2(sw, sp);
+            stage[i][row_of(bb) + c] = pack_f2(sum_xor16_32((sw[0] + sw[1]) + (sw[2] + sw[3])),
+                                               sum_xor16_32((sp[0] + sp[1]) + (sp[2] + sp[3])));
         }
     };
     // The vocabulary's tail tile: target values of columns at or past V
