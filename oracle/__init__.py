@@ -93,6 +93,11 @@ def _declare(L):
     L.orc_survival.restype = None
     L.orc_select.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int64, _P]
     L.orc_select.restype = ctypes.c_int
+    L.orc_select_objective.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int64, _P,
+                                       ctypes.POINTER(ctypes.c_int64)]
+    L.orc_select_objective.restype = ctypes.c_int
+    L.orc_select_threshold.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_float, _P]
+    L.orc_select_threshold.restype = None
     L.orc_accept_scan.argtypes = [_P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_int,
                                   _P, _P, _P]
     L.orc_accept_scan.restype = ctypes.c_int
@@ -215,6 +220,25 @@ def select(theta, budget: int) -> np.ndarray:
     B, gamma = th.shape
     ln = np.zeros(B, dtype=np.int32)
     _check(lib().orc_select(_ptr(th), B, gamma, ctypes.c_int64(int(budget)), _ptr(ln)), "select")
+    return ln
+
+
+def select_objective(theta, step_time, max_admit: int):
+    """Objective-based admission (greedy order, early stop); returns (len, admitted)."""
+    th, st = _f32(theta), _f32(step_time)
+    B, gamma = th.shape
+    ln = np.zeros(B, dtype=np.int32)
+    adm = ctypes.c_int64(0)
+    _check(lib().orc_select_objective(_ptr(th), B, gamma, _ptr(st), int(st.shape[0]), ctypes.c_int64(int(max_admit)),
+                                      _ptr(ln), ctypes.byref(adm)), "select_objective")
+    return ln, int(adm.value)
+
+
+def select_threshold(theta, tau: float) -> np.ndarray:
+    th = _f32(theta)
+    B, gamma = th.shape
+    ln = np.zeros(B, dtype=np.int32)
+    lib().orc_select_threshold(_ptr(th), B, gamma, ctypes.c_float(float(tau)), _ptr(ln))
     return ln
 
 

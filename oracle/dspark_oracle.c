@@ -312,6 +312,97 @@ int orc_select(const float* theta, int B, int gamma, int64_t budget, int32_t* le
     return rc;
 }
 
+/* Objective-based admission: the scheduler's greedy global order (the same
+ * order as orc_select) with incremental admission and early stopping
+ * (menfem.com note, Key Contributions, hardware-aware prefix scheduler;
+ * paperlayer.ai summary, section 5.2 and Appendix A).  Reading taken here:
+ * the objective after m admissions is the expected number of emitted tokens
+ * per unit of verification time,
+ *     J(m) = E(m) / t[B + m],   E(m) = B + sum of the m first Theta,
+ * (every request emits one token whatever happens, Theta_0 = 1; the batch
+ * verifies the admitted drafts plus one position per request), where t[n]
+ * is the engine's time for a verification batch of n tokens.  Candidates
+ * are admitted in order while J does not drop; the first candidate whose
+ * admission would make J strictly smaller stops the scan (early stopping),
+ * and at most max_admit are admitted.
+ * Arithmetic fixed here so that two implementations take the same decisions:
+ * Theta is clamped into [0, 1] (NaN counts as 0) and E is kept in integer
+ * units of 2^-36 (each term floor(Theta * 2^36), exact below 2^53); the test
+ * J(m+1) < J(m) is E(m+1) * t[B+m] < E(m) * t[B+m+1], both products in
+ * double from the exact E and the float t.  Requires n_time > B + min(max_admit, B*gamma).
+ * *admitted receives the number admitted; len[b] the leading run of admitted
+ * positions of row b (ORC_ERR_NOT_PREFIX if an admitted set is not a prefix). */
+int orc_select_objective(const float* theta, int B, int gamma, const float* step_time, int n_time,
+                         int64_t max_admit, int32_t* len, int64_t* admitted)
+{
+    if (B < 0 || gamma <= 0 || max_admit < 0) return ORC_ERR_ARG;
+    int64_t n = (int64_t)B * gamma;
+    int64_t cap = max_admit < n ? max_admit : n;
+    if ((int64_t)n_time <= (int64_t)B + cap) return ORC_ERR_ARG;
+    for (int b = 0; b < B; ++b) len[b] = 0;
+    *admitted = 0;
+    if (n == 0) return ORC_OK;
+    orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)n);
+    if (!c) return ORC_ERR_ALLOC;
+    for (int b = 0; b < B; ++b)
+        for (int k = 0; k < gamma; ++k) {
+            float t = theta[b * gamma + k];
+            if (isnan(t)) {
+                free(c);
+                return ORC_ERR_ARG;
+            }
+            c[b * gamma + k].theta = t;
+            c[b * gamma + k].b = b;
+            c[b * gamma + k].k = k;
+        }
+    qsort(c, (size_t)n, sizeof(orc_cand), orc_cand_cmp);
+    const double unit = 68719476736.0; /* 2^36 */
+    int64_t E = (int64_t)B * (int64_t)68719476736LL;
+    int64_t m = 0;
+    while (m < cap) {
+        float th = c[m].theta;
+        if (!(th > 0.0f)) th = 0.0f;
+        if (th > 1.0f) th = 1.0f;
+        int64_t q = (int64_t)floor((double)th * unit);
+        int64_t E1 = E + q;
+        double keep_new = (double)E1 * (double)step_time[B + m];
+        double keep_old = (double)E * (double)step_time[B + m + 1];
+        if (keep_new < keep_old) break; /* J(m+1) < J(m): stop */
+        E = E1;
+        ++m;
+    }
+    *admitted = m;
+    unsigned char* adm = (unsigned char*)calloc((size_t)n, 1);
+    if (!adm) {
+        free(c);
+        return ORC_ERR_ALLOC;
+    }
+    for (int64_t i = 0; i < m; ++i) adm[c[i].b * gamma + c[i].k] = 1;
+    int rc = ORC_OK;
+    for (int b = 0; b < B; ++b) {
+        int l = 0;
+        while (l < gamma && adm[b * gamma + l]) ++l;
+        for (int k = l; k < gamma; ++k)
+            if (adm[b * gamma + k]) rc = ORC_ERR_NOT_PREFIX;
+        len[b] = l;
+    }
+    free(adm);
+    free(c);
+    return rc;
+}
+
+/* Static-threshold admission (paperlayer.ai summary, section 4.3): a
+ * position is verified when its prefix survival is at least tau; len[b] is
+ * the leading run of positions with Theta >= tau (NaN stops the run). */
+void orc_select_threshold(const float* theta, int B, int gamma, float tau, int32_t* len)
+{
+    for (int b = 0; b < B; ++b) {
+        int l = 0;
+        while (l < gamma && theta[b * gamma + l] >= tau) ++l;
+        len[b] = l;
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Verification ([MF] Methodology: the k-th drafted token is kept with       */
 /* probability min(1, p_t(x_k)/p_d(x_k)) and the first rejection drops every */

@@ -47,6 +47,9 @@ int orc_markov_draft(const float* L, const float* A, const float* Bm, const int3
 
 void orc_survival(const float* z, const float* T, int B, int gamma, float* theta);
 int orc_select(const float* theta, int B, int gamma, int64_t budget, int32_t* len);
+int orc_select_objective(const float* theta, int B, int gamma, const float* step_time, int n_time,
+                         int64_t max_admit, int32_t* len, int64_t* admitted);
+void orc_select_threshold(const float* theta, int B, int gamma, float tau, int32_t* len);
 
 int orc_accept_scan(const float* T_b, const int32_t* tok_b, const float* pd_b, int ell, int V, uint64_t seed, int b,
                     double* pt, double* ratio, float* us);

@@ -142,3 +142,134 @@ def test_appendix_a_early_stop_reading():
         th = np.array([[a1, a1 * c2]], dtype=np.float32)
         assert oracle.select(th, 1).tolist() == [1]
         assert oracle.select(th, 0).tolist() == [0]
+
+
+# ----------------------------------------------------------------------------- objective-based admission
+UNIT = 2**36
+
+
+def _objective_brute(theta, t, max_admit):
+    """The admission rule written with exact rationals: candidates in the order
+    (Theta desc, request asc, position asc); admit while
+    E(m+1) / t[B+m+1] >= E(m) / t[B+m], E in units of 2^-36 (each term
+    floor(clamp(Theta) * 2^36)), every request contributing 1."""
+    from fractions import Fraction
+    B, gamma = theta.shape
+    order = sorted(((float(theta[b, k]), b, k) for b in range(B) for k in range(gamma)),
+                   key=lambda c: (-c[0], c[1], c[2]))
+    cap = min(max_admit, B * gamma)
+    E = B * UNIT
+    m = 0
+    while m < cap:
+        th = min(max(order[m][0], 0.0), 1.0)
+        E1 = E + int(Fraction(th) * UNIT)  # floor for non-negative values
+        if Fraction(E1) / Fraction(float(t[B + m + 1])) < Fraction(E) / Fraction(float(t[B + m])):
+            break
+        E = E1
+        m += 1
+    adm = np.zeros((B, gamma), dtype=bool)
+    for i in range(m):
+        adm[order[i][1], order[i][2]] = True
+    ln = np.array([next((k for k in range(gamma) if not adm[b, k]), gamma) for b in range(B)], dtype=np.int32)
+    return ln, m
+
+
+def test_objective_appendix_a_early_stop():
+    """Appendix A of the paperlayer.ai summary: without early stopping the
+    length chosen for the first draft depends on c_2 (length 2 when the
+    continuation is confident, 0 otherwise); with early stopping the scan ends
+    before c_2 matters.  The capacity curve is an instance chosen here (the
+    page gives none) with J(1) < J(0) and, for c_2 = 0.9, J(2) > J(0)."""
+    from fractions import Fraction
+    with open(os.path.join(os.path.dirname(__file__), "golden", "appendix_a.json")) as f:
+        fx = json.load(f)["facts_from_the_page"]
+    a1 = fx["first_position_acceptance_a1"]
+    t = np.array([0.0, 1.0, 1.9, 2.0], dtype=np.float32)  # t[n]: n = 1 + admitted (one request)
+    global_best = {}
+    for c2 in (fx["c2_high_confidence"], fx["c2_low_confidence"]):
+        th = np.array([[a1, np.float32(a1) * np.float32(c2)]], dtype=np.float32)
+        ln, m = oracle.select_objective(th, t, 2)
+        assert ln.tolist() == [0] and m == 0
+        # the search over every prefix length that the page shows to be biased
+        J = [(1 + sum(Fraction(float(x)) for x in th[0, :l])) / Fraction(float(t[1 + l])) for l in range(3)]
+        global_best[c2] = max(range(3), key=lambda l: J[l])
+    assert global_best == {fx["c2_high_confidence"]: 2, fx["c2_low_confidence"]: 0}
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_objective_matches_exact_rule(seed):
+    g = np.random.default_rng(100 + seed)
+    B, gamma = int(g.integers(1, 7)), int(g.integers(1, 6))
+    z = (g.standard_normal((B, gamma)) * 2).astype(np.float32)
+    if seed % 3 == 0:
+        z[:, :] = z[0, 0]  # equal survivals across requests
+    theta = oracle.survival(z, (1.0 + 0.2 * np.arange(1, gamma + 1)).astype(np.float32))
+    n = B + B * gamma + 1
+    kind = seed % 4
+    if kind == 0:    # concave: fixed cost plus a per-token cost
+        t = (3.0 + 0.05 * np.arange(n)).astype(np.float32)
+    elif kind == 1:  # irregular: steps every 4 tokens
+        t = (1.0 + 0.5 * (np.arange(n) // 4) + 0.01 * np.arange(n)).astype(np.float32)
+    elif kind == 2:  # random increasing
+        t = np.cumsum(g.uniform(0.01, 1.0, n)).astype(np.float32)
+    else:            # random, not monotone
+        t = g.uniform(0.5, 2.0, n).astype(np.float32)
+    for cap in (0, 1, B * gamma // 2, B * gamma, 10 * B * gamma):
+        ln, m = oracle.select_objective(theta, t, cap)
+        ref_ln, ref_m = _objective_brute(theta, t, cap)
+        assert m == ref_m and ln.tolist() == ref_ln.tolist(), (kind, cap)
+        assert int(ln.sum()) == m
+
+
+def test_objective_linear_profile_admits_only_certain_tokens():
+    """t[n] proportional to n: J(m) is the mean of 1 (per request) and the
+    admitted Theta, so a candidate with Theta < 1 lowers it; Theta = 1 keeps
+    it equal, which does not stop the scan."""
+    theta = np.array([[1.0, 1.0, 0.9], [1.0, 0.99, 0.5], [0.7, 0.6, 0.1]], dtype=np.float32)
+    t = (0.25 * np.arange(3 + 9 + 1)).astype(np.float32)
+    ln, m = oracle.select_objective(theta, t, 9)
+    assert ln.tolist() == [2, 1, 0] and m == 3
+
+
+@pytest.mark.parametrize("K", [0, 1, 5, 17, 40])
+def test_objective_flat_then_prohibitive_equals_budget(K):
+    """A profile flat up to B + K tokens and prohibitive after it admits the
+    K best candidates: the budget form with budget K (and a flat profile
+    with cap K too)."""
+    g = np.random.default_rng(7)
+    B, gamma = 8, 5
+    theta = oracle.survival((g.standard_normal((B, gamma)) * 2).astype(np.float32),
+                            np.ones(gamma, dtype=np.float32))
+    n = B + B * gamma + 1
+    t = np.where(np.arange(n) <= B + K, 1.0, 1e30).astype(np.float32)
+    ln, m = oracle.select_objective(theta, t, B * gamma)
+    assert ln.tolist() == oracle.select(theta, K).tolist() and m == min(K, B * gamma)
+    ln2, m2 = oracle.select_objective(theta, np.ones(n, dtype=np.float32), K)
+    assert ln2.tolist() == oracle.select(theta, K).tolist() and m2 == min(K, B * gamma)
+
+
+def test_objective_clamps_and_errors():
+    theta = np.array([[1.5, -0.25]], dtype=np.float32)  # given survivals outside [0, 1]
+    t = np.ones(4, dtype=np.float32)
+    ln, m = oracle.select_objective(theta, t, 2)
+    assert ln.tolist() == [2] and m == 2
+    with pytest.raises(RuntimeError):
+        oracle.select_objective(theta, np.ones(2, dtype=np.float32), 2)  # profile too short
+    with pytest.raises(RuntimeError):
+        oracle.select_objective(theta, t, -1)
+
+
+def test_threshold_leading_run():
+    g = np.random.default_rng(3)
+    theta = g.uniform(0, 1, (50, 6)).astype(np.float32)
+    theta[::7, 2] = np.nan
+    for tau in (0.0, 0.3, 0.5, 0.99, 1.0):
+        ln = oracle.select_threshold(theta, tau)
+        for b in range(50):
+            run = 0
+            while run < 6 and theta[b, run] >= tau:
+                run += 1
+            assert ln[b] == run
+    # non-increasing survivals: the run is the count of positions at or above tau
+    th2 = oracle.survival((g.standard_normal((20, 5))).astype(np.float32), np.ones(5, dtype=np.float32))
+    assert oracle.select_threshold(th2, 0.2).tolist() == (th2 >= np.float32(0.2)).sum(1).tolist()
