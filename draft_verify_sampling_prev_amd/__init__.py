@@ -10,6 +10,8 @@ from .binding import (  # noqa: F401
     DsparkError,
     dspark_markov_draft,
     dspark_schedule,
+    dspark_schedule_objective,
+    dspark_schedule_threshold,
     dspark_verify,
     dspark_workspace_size,
     dspark_version,
@@ -21,6 +23,8 @@ __all__ = [
     "DsparkError",
     "dspark_markov_draft",
     "dspark_schedule",
+    "dspark_schedule_objective",
+    "dspark_schedule_threshold",
     "dspark_verify",
     "dspark_workspace_size",
     "dspark_version",

@@ -59,6 +59,10 @@ def load_library():
                                       ctypes.c_size_t, _P]
     L.dspark_schedule.restype = _I
     L.dspark_schedule.argtypes = [_P, _P, _I, _I, ctypes.c_int64, _P, _P, _P]
+    L.dspark_schedule_objective.restype = _I
+    L.dspark_schedule_objective.argtypes = [_P, _P, _I, _I, _P, _I, ctypes.c_int64, _P, _P, _P]
+    L.dspark_schedule_threshold.restype = _I
+    L.dspark_schedule_threshold.argtypes = [_P, _P, _I, _I, ctypes.c_float, _P, _P, _P]
     L.dspark_verify.restype = _I
     L.dspark_verify.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P,
                                 _P, _P, ctypes.c_size_t, _P]
@@ -173,6 +177,55 @@ def dspark_schedule(z: Optional[torch.Tensor], temps: Optional[torch.Tensor], bu
     rc = load_library().dspark_schedule(_ptr(z), _ptr(temps), B, gamma, ctypes.c_int64(int(budget)), _ptr(survival),
                                         _ptr(out_len), _stream(dev, stream))
     _check(rc, "dspark_schedule")
+    return survival, out_len
+
+
+def _schedule_args(z, temps, survival, out_len, B, gamma):
+    ref = z if z is not None else survival
+    if ref is None:
+        raise DsparkError("either z or survival must be given")
+    dev = ref.device
+    if B is None or gamma is None:
+        B, gamma = ref.shape
+    if z is not None:
+        _dev(z, "z", dev, torch.float32, (B, gamma))
+        _dev(temps, "temps", dev, torch.float32, (gamma,))
+        if survival is None:
+            survival = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    _dev(survival, "survival", dev, torch.float32, (B, gamma))
+    if out_len is None:
+        out_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    return dev, B, gamma, survival, out_len
+
+
+def dspark_schedule_objective(z: Optional[torch.Tensor], temps: Optional[torch.Tensor], step_time: torch.Tensor,
+                              max_admit: int, survival: Optional[torch.Tensor] = None,
+                              out_len: Optional[torch.Tensor] = None, B: Optional[int] = None,
+                              gamma: Optional[int] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Survival product and objective-based admission against the engine
+    profile `step_time` (f32 [n_time], time of a batch of n tokens).
+    Returns (survival f32 [B][g], verify_len int32 [B])."""
+    dev, B, gamma, survival, out_len = _schedule_args(z, temps, survival, out_len, B, gamma)
+    if step_time.dim() != 1:
+        raise DsparkError("step_time must be one-dimensional")
+    _dev(step_time, "step_time", dev, torch.float32, (step_time.shape[0],))
+    rc = load_library().dspark_schedule_objective(_ptr(z), _ptr(temps), B, gamma, _ptr(step_time),
+                                                  int(step_time.shape[0]), ctypes.c_int64(int(max_admit)),
+                                                  _ptr(survival), _ptr(out_len), _stream(dev, stream))
+    _check(rc, "dspark_schedule_objective")
+    return survival, out_len
+
+
+def dspark_schedule_threshold(z: Optional[torch.Tensor], temps: Optional[torch.Tensor], tau: float,
+                              survival: Optional[torch.Tensor] = None, out_len: Optional[torch.Tensor] = None,
+                              B: Optional[int] = None, gamma: Optional[int] = None,
+                              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Survival product and static-threshold admission (leading run of Theta >= tau).
+    Returns (survival f32 [B][g], verify_len int32 [B])."""
+    dev, B, gamma, survival, out_len = _schedule_args(z, temps, survival, out_len, B, gamma)
+    rc = load_library().dspark_schedule_threshold(_ptr(z), _ptr(temps), B, gamma, ctypes.c_float(float(tau)),
+                                                  _ptr(survival), _ptr(out_len), _stream(dev, stream))
+    _check(rc, "dspark_schedule_threshold")
     return survival, out_len
 
 

@@ -187,6 +187,42 @@ int dspark_schedule(const float* z, const float* temps, int B, int gamma, int64_
                       "schedule launch");
 }
 
+int dspark_schedule_objective(const float* z, const float* temps, int B, int gamma, const float* step_time,
+                              int n_time, int64_t max_admit, float* survival, int32_t* verify_len, void* stream)
+{
+    g_err[0] = 0;
+    if (B < 0) return fail(DSPARK_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    if (gamma < 1 || gamma > kMaxGamma) return fail(DSPARK_ERR_UNSUPPORTED, "gamma must be in [1, %d] (got %d)", kMaxGamma, gamma);
+    if ((long long)B * gamma > kMaxCandidates)
+        return fail(DSPARK_ERR_UNSUPPORTED, "B*gamma must be <= %d", kMaxCandidates);
+    if (max_admit < 0) return fail(DSPARK_ERR_INVALID_ARG, "max_admit must be >= 0 (got %lld)", (long long)max_admit);
+    if (B == 0) return DSPARK_OK;
+    if (!survival || !verify_len || !step_time) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    if (z && !temps) return fail(DSPARK_ERR_INVALID_ARG, "temps must be given with z");
+    const int64_t n = (int64_t)B * gamma;
+    const int64_t cap = max_admit < n ? max_admit : n;
+    if ((int64_t)n_time <= (int64_t)B + cap)
+        return fail(DSPARK_ERR_INVALID_ARG, "step_time needs B + min(max_admit, B*gamma) + 1 = %lld entries (got %d)",
+                    (long long)(B + cap + 1), n_time);
+    return hip_status(launch_schedule_objective(z, temps, B, gamma, step_time, cap, survival, verify_len,
+                                                static_cast<hipStream_t>(stream)),
+                      "schedule_objective launch");
+}
+
+int dspark_schedule_threshold(const float* z, const float* temps, int B, int gamma, float tau, float* survival,
+                              int32_t* verify_len, void* stream)
+{
+    g_err[0] = 0;
+    if (B < 0) return fail(DSPARK_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+    if (gamma < 1 || gamma > kMaxGamma) return fail(DSPARK_ERR_UNSUPPORTED, "gamma must be in [1, %d] (got %d)", kMaxGamma, gamma);
+    if (B == 0) return DSPARK_OK;
+    if (!survival || !verify_len) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    if (z && !temps) return fail(DSPARK_ERR_INVALID_ARG, "temps must be given with z");
+    return hip_status(launch_schedule_threshold(z, temps, B, gamma, tau, survival, verify_len,
+                                                static_cast<hipStream_t>(stream)),
+                      "schedule_threshold launch");
+}
+
 int dspark_verify(int dtype, const void* Tgt, const void* L, const void* A, const void* Bm, const int32_t* x0,
                   const int32_t* draft_tok, const float* draft_p, const double* draft_lse, const int32_t* verify_len,
                   int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok, int32_t* n_out,

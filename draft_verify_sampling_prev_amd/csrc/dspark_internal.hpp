@@ -64,6 +64,10 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
 
 hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,
                            int32_t* len, hipStream_t s);
+hipError_t launch_schedule_objective(const float* z, const float* temps, int B, int gamma, const float* step_time,
+                                     int64_t cap, float* survival, int32_t* len, hipStream_t s);
+hipError_t launch_schedule_threshold(const float* z, const float* temps, int B, int gamma, float tau,
+                                     float* survival, int32_t* len, hipStream_t s);
 
 hipError_t launch_verify(int dtype, const void* Tg, const void* L, const void* A, const void* Bm, const int32_t* x0,
                          const int32_t* tok, const float* pd, const double* lse_d, const int32_t* len, int B,

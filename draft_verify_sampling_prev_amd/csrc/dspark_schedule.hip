@@ -16,6 +16,8 @@
 // it are admitted, and among keys equal to it the first ones in (request,
 // position) order.  Because each row's Theta is non-increasing, the admitted
 // set of a row is a prefix and its verify length is its admitted count.
+#include <limits.h>
+
 #include "dspark_device.hpp"
 #include "dspark_internal.hpp"
 
@@ -52,6 +54,35 @@ __device__ __forceinline__ int block_excl_scan_int(int v, int* wsum, int* total)
     return off + inc - v;
 }
 
+// Prefix survivals of all N = B*gamma candidates into vals[] (LDS, fp32 bit
+// patterns, index b*gamma + k-1): the inputs (z, or the given survivals) are
+// read with coalesced loads, then one thread per row runs the product, and
+// with z the results go out to surv with coalesced stores.  Ends with a
+// barrier.
+__device__ __forceinline__ void survival_lds(const float* __restrict__ z, const float* __restrict__ temps, int B,
+                                             int gamma, float* surv, uint32_t* vals, float* tsh)
+{
+    const int t = threadIdx.x, N = B * gamma;
+    const float* src = z ? z : surv;
+    for (int i = t; i < N; i += kSchedThreads) vals[i] = __float_as_uint(src[i]);
+    if (z && t < gamma) tsh[t] = temps[t];
+    __syncthreads();
+    if (z) {
+        for (int b = t; b < B; b += kSchedThreads) {
+            float th = 1.0f;
+            for (int kk = 0; kk < gamma; ++kk) {
+                const float q = __uint_as_float(vals[b * gamma + kk]) / tsh[kk];
+                const float c = 1.0f / (1.0f + expf(-q));
+                th = th * c;
+                vals[b * gamma + kk] = __float_as_uint(th);  // the row's own slots only
+            }
+        }
+        __syncthreads();
+        for (int i = t; i < N; i += kSchedThreads) surv[i] = __uint_as_float(vals[i]);
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(kSchedThreads) void k_schedule(const float* __restrict__ z,
                                                             const float* __restrict__ temps, int B, int gamma,
                                                             long long admit, float* surv, int32_t* __restrict__ len)
@@ -65,30 +96,9 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(const float* __restr
     const int t = threadIdx.x;
     const int N = B * gamma;
 
-    // Inputs (z, or the given survivals) into LDS with coalesced loads, and
-    // the temperatures; then one thread per row runs the product.
     __shared__ float tsh[kMaxGamma];
-    const float* src = z ? z : surv;
-    for (int i = t; i < N; i += kSchedThreads) keys[i] = __float_as_uint(src[i]);
-    if (z && t < gamma) tsh[t] = temps[t];
-    __syncthreads();
-    if (z) {
-        for (int b = t; b < B; b += kSchedThreads) {
-            float th = 1.0f;
-            for (int kk = 0; kk < gamma; ++kk) {
-                const float q = __uint_as_float(keys[b * gamma + kk]) / tsh[kk];
-                const float c = 1.0f / (1.0f + expf(-q));
-                th = th * c;
-                keys[b * gamma + kk] = __float_as_uint(th);  // the row's own slots only
-            }
-        }
-        __syncthreads();
-    }
-    for (int i = t; i < N; i += kSchedThreads) {
-        const float v = __uint_as_float(keys[i]);
-        if (z) surv[i] = v;
-        keys[i] = order_key(v);
-    }
+    survival_lds(z, temps, B, gamma, surv, keys, tsh);
+    for (int i = t; i < N; i += kSchedThreads) keys[i] = order_key(__uint_as_float(keys[i]));
     __syncthreads();
 
     if (admit <= 0 || admit >= N) {
@@ -167,6 +177,185 @@ __global__ __launch_bounds__(kSchedThreads) void k_schedule(const float* __restr
         for (int kk = 0; kk < gamma; ++kk) l += (int)keys[b * gamma + kk];
         len[b] = l;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Objective-based admission: the same greedy order, admitted one candidate
+// at a time while the expected number of emitted tokens per unit of
+// verification time does not drop, stopping at the first candidate that
+// would lower it (menfem.com note, hardware-aware prefix scheduler:
+// incremental batch admission with early stopping; paperlayer.ai summary,
+// section 5.2 (engine throughput profile) and Appendix A (early stopping)).
+//   J(m) = E(m) / t[B + m],  E(m) = B + (sum of the m first Theta),
+// t[n] the time of a verification batch of n tokens.  Arithmetic fixed so
+// the decision is reproducible: Theta clamped into [0, 1] (NaN -> 0), E in
+// integer units of 2^-36 (terms floor(Theta * 2^36), sums exact), and
+// "J(m+1) < J(m)" evaluated as E(m+1) * t[B+m] < E(m) * t[B+m+1] with both
+// products in double.
+//
+// One workgroup: the N keys ((order key of Theta) complemented, index) are
+// bitonic-sorted ascending in LDS (Theta desc, then index = request-major
+// order asc), each thread takes a contiguous run of ranks, the per-rank
+// terms are scanned across the workgroup (int64), every rank evaluates its
+// own stop test, and the first failing rank (capped at `cap`) is the number
+// admitted.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float key_to_float(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+constexpr double kThetaUnit = 68719476736.0;  // 2^36
+constexpr int kObjPerThread = kMaxCandidates / kSchedThreads;
+
+__global__ __launch_bounds__(kSchedThreads) void k_schedule_objective(const float* __restrict__ z,
+                                                                      const float* __restrict__ temps, int B,
+                                                                      int gamma, const float* __restrict__ step_time,
+                                                                      long long cap, float* surv,
+                                                                      int32_t* __restrict__ len)
+{
+    __shared__ unsigned long long skey[kMaxCandidates];  // 128 KB
+    __shared__ unsigned char adm[kMaxCandidates];
+    __shared__ long long wsum[kSchedThreads / 64];
+    __shared__ float tsh[kMaxGamma];
+    __shared__ int sh_stop;
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int N = B * gamma;
+    // Survivals into the upper half of skey (as 32-bit words), then the
+    // 64-bit sort keys over the whole array (values first held in registers).
+    uint32_t* vals = reinterpret_cast<uint32_t*>(skey) + kMaxCandidates;
+    survival_lds(z, temps, B, gamma, surv, vals, tsh);
+    int P = 2;
+    while (P < N) P <<= 1;
+    uint32_t kv[kObjPerThread];
+#pragma unroll
+    for (int j = 0; j < kObjPerThread; ++j) {
+        const int i = t + j * kSchedThreads;
+        kv[j] = i < N ? ~order_key(__uint_as_float(vals[i])) : 0xFFFFFFFFu;
+    }
+    for (int i = t; i < N; i += kSchedThreads) adm[i] = 0;
+    if (t == 0) sh_stop = (int)min(cap, (long long)N);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kObjPerThread; ++j) {
+        const int i = t + j * kSchedThreads;
+        if (i < P) skey[i] = i < N ? ((unsigned long long)kv[j] << 32) | (uint32_t)i : ~0ull;
+    }
+    __syncthreads();
+
+    // Bitonic sort, ascending.
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = t; i < P; i += kSchedThreads) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const unsigned long long a = skey[i], b = skey[ixj];
+                    if ((a > b) == ((i & k) == 0)) {
+                        skey[i] = b;
+                        skey[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // Ranks [r0, r1) of this thread: terms, their sum, the exclusive scan.
+    const int per = (N + kSchedThreads - 1) / kSchedThreads;
+    const int r0 = min(t * per, N), r1 = min(r0 + per, N);
+    long long local = 0;
+    for (int m = r0; m < r1; ++m) {
+        float th = key_to_float(~(uint32_t)(skey[m] >> 32));
+        th = fminf(fmaxf(th, 0.0f), 1.0f);  // NaN -> 0
+        local += (long long)floor((double)th * kThetaUnit);
+    }
+    long long inc = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const long long n = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += n;
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    long long excl = inc - local;
+    for (int i = 0; i < w; ++i) excl += wsum[i];
+
+    // Stop test of each rank m < cap: admitting rank m moves E(m) -> E(m+1).
+    const long long mcap = min(cap, (long long)N);
+    long long E = (long long)B * (long long)kThetaUnit + excl;
+    int first = INT_MAX;
+    for (int m = r0; m < r1 && m < mcap; ++m) {
+        float th = key_to_float(~(uint32_t)(skey[m] >> 32));
+        th = fminf(fmaxf(th, 0.0f), 1.0f);
+        const long long E1 = E + (long long)floor((double)th * kThetaUnit);
+        const double keep_new = (double)E1 * (double)step_time[B + m];
+        const double keep_old = (double)E * (double)step_time[B + m + 1];
+        if (keep_new < keep_old) {
+            first = m;
+            break;
+        }
+        E = E1;
+    }
+    if (first != INT_MAX) atomicMin(&sh_stop, first);
+    __syncthreads();
+    const int admit = sh_stop;
+    for (int m = t; m < admit; m += kSchedThreads) adm[(uint32_t)skey[m]] = 1;
+    __syncthreads();
+    for (int b = t; b < B; b += kSchedThreads) {
+        int l = 0;
+        while (l < gamma && adm[b * gamma + l]) ++l;
+        len[b] = l;
+    }
+}
+
+// Static threshold: verify_len[b] is the leading run of positions whose
+// survival is at least tau (paperlayer.ai summary, section 4.3).  One thread
+// per request; the survival product is the one of survival_lds.
+__global__ __launch_bounds__(256) void k_schedule_threshold(const float* __restrict__ z,
+                                                            const float* __restrict__ temps, int B, int gamma,
+                                                            float tau, float* surv, int32_t* __restrict__ len)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    float th = 1.0f;
+    int l = 0;
+    bool run = true;
+    for (int kk = 0; kk < gamma; ++kk) {
+        float v;
+        if (z) {
+            const float q = z[b * gamma + kk] / temps[kk];
+            const float c = 1.0f / (1.0f + expf(-q));
+            th = th * c;
+            v = th;
+            surv[b * gamma + kk] = v;
+        } else {
+            v = surv[b * gamma + kk];
+        }
+        run = run && v >= tau;
+        l += run ? 1 : 0;
+    }
+    len[b] = l;
+}
+
+hipError_t launch_schedule_objective(const float* z, const float* temps, int B, int gamma, const float* step_time,
+                                     int64_t cap, float* survival, int32_t* len, hipStream_t s)
+{
+    prof_begin(K_SCHEDULE, s);
+    hipLaunchKernelGGL(k_schedule_objective, dim3(1), dim3(kSchedThreads), 0, s, z, temps, B, gamma, step_time,
+                       (long long)cap, survival, len);
+    prof_end(K_SCHEDULE, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_schedule_threshold(const float* z, const float* temps, int B, int gamma, float tau,
+                                     float* survival, int32_t* len, hipStream_t s)
+{
+    prof_begin(K_SCHEDULE, s);
+    hipLaunchKernelGGL(k_schedule_threshold, dim3((B + 255) / 256), dim3(256), 0, s, z, temps, B, gamma, tau,
+                       survival, len);
+    prof_end(K_SCHEDULE, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,

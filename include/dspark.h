@@ -136,6 +136,46 @@ int dspark_schedule(const float* z, const float* temps, int B, int gamma, int64_
                     int32_t* verify_len, void* stream);
 
 /*
+ * dspark_schedule_objective -- objective-based admission: the scheduler's
+ * greedy global order with incremental batch admission and early stopping
+ * (menfem.com note, "Hardware-aware prefix scheduler"; paperlayer.ai summary,
+ * section 5.2: verification budget routed by an engine throughput profile,
+ * and Appendix A: early stopping keeps admission non-anticipating).
+ *
+ * Survivals as in dspark_schedule.  Candidates are taken in the order
+ * (Theta desc, b asc, k asc); with m admitted the objective is the expected
+ * number of emitted tokens per unit of verification time
+ *     J(m) = E(m) / step_time[B + m],   E(m) = B + sum of the m first Theta
+ * (each request emits one token in any case; the verification batch holds
+ * the admitted drafts plus one position per request).  Candidates are
+ * admitted while J does not drop; the first one whose admission would make
+ * J strictly smaller ends the scan, and at most max_admit are admitted.
+ * Reproducible arithmetic: Theta clamped into [0, 1]; E in integer units of
+ * 2^-36 (each term floor(Theta * 2^36)); the test J(m+1) < J(m) is
+ * E(m+1) * step_time[B+m] < E(m) * step_time[B+m+1] in double.
+ *
+ *   step_time  [n_time] f32 device array: time of a verification batch of n
+ *              tokens (any unit, > 0, finite); n_time must exceed
+ *              B + min(max_admit, B*gamma), else DSPARK_ERR_INVALID_ARG
+ *   max_admit  upper bound on admitted drafts (>= 0)
+ *   survival, verify_len, z, temps: as in dspark_schedule (given survivals
+ *              must not be NaN)
+ * One workgroup; B*gamma <= 16384.  Enqueues one kernel on `stream`.
+ */
+int dspark_schedule_objective(const float* z, const float* temps, int B, int gamma, const float* step_time,
+                              int n_time, int64_t max_admit, float* survival, int32_t* verify_len, void* stream);
+
+/*
+ * dspark_schedule_threshold -- static confidence threshold (paperlayer.ai
+ * summary, section 4.3: positions whose prefix survival falls below a fixed
+ * threshold are not verified).  verify_len[b] = the number of leading
+ * positions k = 1, 2, ... with Theta[b][k] >= tau (a NaN ends the run).
+ * Survivals as in dspark_schedule.  One thread per request.
+ */
+int dspark_schedule_threshold(const float* z, const float* temps, int B, int gamma, float tau, float* survival,
+                              int32_t* verify_len, void* stream);
+
+/*
  * dspark_verify -- exact rejection sampling (menfem.com note, Methodology:
  * token x_k is kept with probability min(1, p_t(x_k)/p_d(x_k)) and the first
  * rejection drops all later tokens; paperlayer.ai summary, section 2).

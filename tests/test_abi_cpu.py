@@ -39,7 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_python_binding_has_the_same_names():
-    for n in ("dspark_markov_draft", "dspark_schedule", "dspark_verify", "dspark_workspace_size", "dspark_version"):
+    for n in ("dspark_markov_draft", "dspark_schedule", "dspark_schedule_objective", "dspark_schedule_threshold",
+              "dspark_verify", "dspark_workspace_size", "dspark_version"):
         assert callable(getattr(dsp, n))
 
 
@@ -87,6 +88,32 @@ def test_schedule_argument_errors(lib):
     assert f(FAKE, FAKE, 4, 0, ctypes.c_int64(3), FAKE, FAKE, None) == UNSUPPORTED
     assert f(FAKE, FAKE, 4, 5, ctypes.c_int64(3), None, FAKE, None) == INVALID
     assert f(None, None, 0, 5, ctypes.c_int64(3), None, None, None) == OK
+
+
+def test_schedule_objective_argument_errors(lib):
+    f = lib.dspark_schedule_objective
+
+    def call(z=FAKE, temps=FAKE, B=4, gamma=5, st=FAKE, n_time=64, cap=3, surv=FAKE, ln=FAKE):
+        return f(z, temps, B, gamma, st, n_time, ctypes.c_int64(cap), surv, ln, None)
+
+    assert call(cap=-1) == INVALID
+    assert call(temps=None) == INVALID
+    assert call(st=None) == INVALID
+    assert call(surv=None) == INVALID
+    assert call(gamma=0) == UNSUPPORTED
+    assert call(B=5000, gamma=4) == UNSUPPORTED
+    assert call(n_time=7) == INVALID            # needs B + min(cap, B*gamma) + 1 = 8 entries
+    assert b"step_time" in lib.dspark_last_error()
+    assert call(n_time=24, cap=1000) == INVALID  # cap clamps to 20: needs 25
+    assert call(B=0, z=None, temps=None, st=None, surv=None, ln=None) == OK
+
+
+def test_schedule_threshold_argument_errors(lib):
+    f = lib.dspark_schedule_threshold
+    assert f(FAKE, None, 4, 5, ctypes.c_float(0.5), FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 4, 17, ctypes.c_float(0.5), FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, FAKE, 4, 5, ctypes.c_float(0.5), FAKE, None, None) == INVALID
+    assert f(None, None, 0, 5, ctypes.c_float(0.5), None, None, None) == OK
 
 
 def test_verify_argument_errors(lib):
