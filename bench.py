@@ -118,6 +118,10 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=160, help="requests in the oracle CPU-baseline sample (~10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="also time HIP-graph replay of the whole step")
+    ap.add_argument("--schedule", choices=("budget", "objective", "threshold"), default="budget",
+                    help="admission rule of the step: the budget (default, the headline), objective-based "
+                         "admission against a synthetic step-time profile capped at the budget, or a static threshold")
+    ap.add_argument("--tau", type=float, default=0.3, help="survival threshold for --schedule threshold")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -163,9 +167,22 @@ def main():
     K = args.steps
     n_out_all = torch.zeros((K + args.warmup + 1, B), dtype=torch.int32, device=dev)
 
+    # Synthetic engine profile for objective-based admission: a verification
+    # batch of n tokens takes 1 ms plus 1 us per token (a fixed cost of
+    # reading the weights plus a per-token cost).
+    prof = (1.0 + 0.001 * torch.arange(B + B * gamma + 1, dtype=torch.float64)).float().to(dev)
+
+    def schedule():
+        if args.schedule == "budget":
+            dsp.dspark_schedule(g.z, g.temps, wl.budget, survival=theta, out_len=ell)
+        elif args.schedule == "objective":
+            dsp.dspark_schedule_objective(g.z, g.temps, prof, wl.budget, survival=theta, out_len=ell)
+        else:
+            dsp.dspark_schedule_threshold(g.z, g.temps, args.tau, survival=theta, out_len=ell)
+
     def step(i: int, seed: int):
         dsp.dspark_markov_draft(g.L, g.A, g.Bm, g.x0, seed, ws=ws, out=(tok, p, lse))
-        dsp.dspark_schedule(g.z, g.temps, wl.budget, survival=theta, out_len=ell)
+        schedule()
         dsp.dspark_verify(g.T, g.L, g.A, g.Bm, g.x0, tok, p, lse, ell, seed, ws=ws,
                           out=(acc, out_tok, n_out_all[i], tp))
 
@@ -259,6 +276,9 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded; target N(0,4) logits, draft = target + position noise, Markov factors N(0,0.02^2))",
         "config": {"workload": wl.name, "B": B, "gamma": gamma, "V": V, "r": r, "budget": wl.budget,
+                   "schedule": args.schedule + (" (step time 1 ms + 1 us/token, capped at the budget)"
+                                                if args.schedule == "objective" else
+                                                f" (tau {args.tau})" if args.schedule == "threshold" else ""),
                    "emitted_per_step": round(emitted / K, 2), "verified_per_step": int(ell.sum().item()),
                    "accumulation": "fp32 MFMA, fp64 softmax masses"},
         "roofline": {"kernel": "draft Markov tiles (k_draft_tiles)", "bound": "hbm",
@@ -278,7 +298,7 @@ def main():
     }
     if graph:
         result["graph_replay"] = graph
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.schedule == "budget":
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, wl, base_seed, min(args.cpu_requests, B))
     print(json.dumps(result), flush=True)
