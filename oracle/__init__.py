@@ -91,6 +91,8 @@ def _declare(L):
     L.orc_markov_draft.restype = ctypes.c_int
     L.orc_survival.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, _P]
     L.orc_survival.restype = None
+    L.orc_markov_confidence.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]
+    L.orc_markov_confidence.restype = ctypes.c_int
     L.orc_select.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int64, _P]
     L.orc_select.restype = ctypes.c_int
     L.orc_select_objective.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int64, _P,
@@ -213,6 +215,17 @@ def survival(z, T) -> np.ndarray:
     th = np.zeros((B, gamma), dtype=np.float32)
     lib().orc_survival(_ptr(zz), _ptr(TT), B, gamma, _ptr(th))
     return th
+
+
+def markov_confidence(A, wc, x0, tok, z0) -> np.ndarray:
+    """z[b][k] = z0[b][k] + <A[x_{k-1}], wc> (x_0 = x0[b], x_{k-1} = tok[b][k-2])."""
+    AA, ww, xx, tt, zz = _f32(A), _f32(wc), _i32(x0), _i32(tok), _f32(z0)
+    V, r = AA.shape
+    B, gamma = zz.shape
+    z = np.zeros((B, gamma), dtype=np.float32)
+    _check(lib().orc_markov_confidence(_ptr(AA), _ptr(ww), _ptr(xx), _ptr(tt), _ptr(zz), B, gamma, V, r, _ptr(z)),
+           "markov_confidence")
+    return z
 
 
 def select(theta, budget: int) -> np.ndarray:

@@ -249,6 +249,29 @@ void orc_survival(const float* z, const float* T, int B, int gamma, float* theta
 }
 
 /* ------------------------------------------------------------------------ */
+/* Markov-conditioned confidence logit (paperlayer.ai summary, Appendix A: the */
+/* Markov confidence head sees the previously sampled token, so c_2 depends on */
+/* x_1; menfem.com note: the confidence head is linear).  Reading taken here:  */
+/* z[b][k] = z0[b][k] + <A[x_{k-1}], wc>, the backbone part z0 an input and    */
+/* the token part the dot product of the token's Markov code A[x] (the same    */
+/* rows the Markov head uses) with a weight vector wc[r]; x_0 = x0[b],         */
+/* x_{k-1} = tok[b][k-2].  Summed in double, rounded once to float.           */
+/* ------------------------------------------------------------------------ */
+int orc_markov_confidence(const float* A, const float* wc, const int32_t* x0, const int32_t* tok, const float* z0,
+                          int B, int gamma, int V, int r, float* z)
+{
+    for (int b = 0; b < B; ++b)
+        for (int k = 1; k <= gamma; ++k) {
+            int x = k == 1 ? x0[b] : tok[b * gamma + (k - 2)];
+            if (x < 0 || x >= V) return ORC_ERR_ARG;
+            double s = z0[b * gamma + (k - 1)];
+            for (int j = 0; j < r; ++j) s += (double)A[(size_t)x * r + j] * (double)wc[j];
+            z[b * gamma + (k - 1)] = (float)s;
+        }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Selection ([MF] "Hardware-aware prefix scheduler": candidates are sorted  */
 /* globally by cumulative survival and admitted greedily; here the budget   */
 /* form: admit the first min(budget, B*gamma) of the order (Theta desc,     */

@@ -273,3 +273,43 @@ def test_threshold_leading_run():
     # non-increasing survivals: the run is the count of positions at or above tau
     th2 = oracle.survival((g.standard_normal((20, 5))).astype(np.float32), np.ones(5, dtype=np.float32))
     assert oracle.select_threshold(th2, 0.2).tolist() == (th2 >= np.float32(0.2)).sum(1).tolist()
+
+
+# ----------------------------------------------------------------------------- Markov-conditioned confidence
+def test_markov_confidence_one_hot_codes_select_weights():
+    """With one-hot conditioning codes A[x] = e_{x mod r}, z[b][k] = z0[b][k] + wc[x_{k-1} mod r] exactly."""
+    V, r, B, gamma = 12, 8, 3, 4
+    A = np.zeros((V, r), dtype=np.float32)
+    A[np.arange(V), np.arange(V) % r] = 1.0
+    wc = np.arange(1, r + 1, dtype=np.float32) * 0.5
+    x0 = np.array([3, 11, 0], dtype=np.int32)
+    tok = np.array([[1, 2, 9, 4], [5, 5, 5, 5], [7, 0, 10, 6]], dtype=np.int32)
+    z0 = np.array([[0.25, -1.0, 2.0, 0.0], [1.5, 1.5, -0.5, 3.0], [0.0, 0.125, 0.0, -2.0]], dtype=np.float32)
+    z = oracle.markov_confidence(A, wc, x0, tok, z0)
+    prev = np.concatenate([x0[:, None], tok[:, :-1]], axis=1)
+    assert np.array_equal(z, z0 + wc[prev % r])
+
+
+def test_markov_confidence_integer_exact_and_depends_on_previous_token():
+    """Small-integer codes: the dot product is exact; z_k changes with x_{k-1}
+    and with nothing later (Appendix A: c_2 depends on x_1)."""
+    g = np.random.default_rng(5)
+    V, r, B, gamma = 50, 24, 4, 5
+    A = g.integers(-3, 4, (V, r)).astype(np.float32)
+    wc = g.integers(-2, 3, r).astype(np.float32)
+    x0 = g.integers(0, V, B).astype(np.int32)
+    tok = g.integers(0, V, (B, gamma)).astype(np.int32)
+    z0 = g.integers(-5, 6, (B, gamma)).astype(np.float32)
+    z = oracle.markov_confidence(A, wc, x0, tok, z0)
+    ref = np.empty((B, gamma), dtype=np.int64)
+    for b in range(B):
+        for k in range(gamma):
+            x = x0[b] if k == 0 else tok[b, k - 1]
+            ref[b, k] = int(z0[b, k]) + int(A[x].astype(np.int64) @ wc.astype(np.int64))
+    assert np.array_equal(z.astype(np.int64), ref)
+    tok2 = tok.copy()
+    tok2[:, 0] = (tok[:, 0] + 1) % V  # change x_1 only
+    z2 = oracle.markov_confidence(A, wc, x0, tok2, z0)
+    assert np.array_equal(z2[:, 0], z[:, 0]) and np.array_equal(z2[:, 2:], z[:, 2:])
+    moved = (A[tok[:, 0]] @ wc) != (A[tok2[:, 0]] @ wc)
+    assert np.array_equal(z2[:, 1] != z[:, 1], moved)
