@@ -122,6 +122,9 @@ def main():
                     help="admission rule of the step: the budget (default, the headline), objective-based "
                          "admission against a synthetic step-time profile capped at the budget, or a static threshold")
     ap.add_argument("--tau", type=float, default=0.3, help="survival threshold for --schedule threshold")
+    ap.add_argument("--confidence", action="store_true",
+                    help="draft with the fused Markov-conditioned confidence head (z = z0 + <A[x_prev], wc>, "
+                         "synthetic wc ~ N(0, 0.5^2)) and schedule on those z")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate HBM byte counters")
     args = ap.parse_args()
@@ -172,16 +175,24 @@ def main():
     # reading the weights plus a per-token cost).
     prof = (1.0 + 0.001 * torch.arange(B + B * gamma + 1, dtype=torch.float64)).float().to(dev)
 
+    # Confidence-head weights on the Markov code (synthetic), and its output.
+    wc = (torch.randn(r, generator=torch.Generator().manual_seed(wl.data_seed + 7)) * 0.5).to(g.L.dtype).to(dev)
+    zc = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    zs = zc if args.confidence else g.z
+
     def schedule():
         if args.schedule == "budget":
-            dsp.dspark_schedule(g.z, g.temps, wl.budget, survival=theta, out_len=ell)
+            dsp.dspark_schedule(zs, g.temps, wl.budget, survival=theta, out_len=ell)
         elif args.schedule == "objective":
-            dsp.dspark_schedule_objective(g.z, g.temps, prof, wl.budget, survival=theta, out_len=ell)
+            dsp.dspark_schedule_objective(zs, g.temps, prof, wl.budget, survival=theta, out_len=ell)
         else:
-            dsp.dspark_schedule_threshold(g.z, g.temps, args.tau, survival=theta, out_len=ell)
+            dsp.dspark_schedule_threshold(zs, g.temps, args.tau, survival=theta, out_len=ell)
 
     def step(i: int, seed: int):
-        dsp.dspark_markov_draft(g.L, g.A, g.Bm, g.x0, seed, ws=ws, out=(tok, p, lse))
+        if args.confidence:
+            dsp.dspark_markov_draft_conf(g.L, g.A, g.Bm, g.x0, seed, g.z, wc, ws=ws, out=(tok, p, lse, zc))
+        else:
+            dsp.dspark_markov_draft(g.L, g.A, g.Bm, g.x0, seed, ws=ws, out=(tok, p, lse))
         schedule()
         dsp.dspark_verify(g.T, g.L, g.A, g.Bm, g.x0, tok, p, lse, ell, seed, ws=ws,
                           out=(acc, out_tok, n_out_all[i], tp))
@@ -278,7 +289,8 @@ def main():
         "config": {"workload": wl.name, "B": B, "gamma": gamma, "V": V, "r": r, "budget": wl.budget,
                    "schedule": args.schedule + (" (step time 1 ms + 1 us/token, capped at the budget)"
                                                 if args.schedule == "objective" else
-                                                f" (tau {args.tau})" if args.schedule == "threshold" else ""),
+                                                f" (tau {args.tau})" if args.schedule == "threshold" else "")
+                   + (", z from the fused Markov-conditioned confidence head" if args.confidence else ""),
                    "emitted_per_step": round(emitted / K, 2), "verified_per_step": int(ell.sum().item()),
                    "accumulation": "fp32 MFMA, fp64 softmax masses"},
         "roofline": {"kernel": "draft Markov tiles (k_draft_tiles)", "bound": "hbm",
@@ -298,7 +310,7 @@ def main():
     }
     if graph:
         result["graph_replay"] = graph
-    if not args.no_cpu_baseline and args.schedule == "budget":
+    if not args.no_cpu_baseline and args.schedule == "budget" and not args.confidence:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, wl, base_seed, min(args.cpu_requests, B))
     print(json.dumps(result), flush=True)

@@ -9,6 +9,7 @@ library; the first call does, and raises if the library is missing.
 from .binding import (  # noqa: F401
     DsparkError,
     dspark_markov_draft,
+    dspark_markov_draft_conf,
     dspark_schedule,
     dspark_schedule_objective,
     dspark_schedule_threshold,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
 __all__ = [
     "DsparkError",
     "dspark_markov_draft",
+    "dspark_markov_draft_conf",
     "dspark_schedule",
     "dspark_schedule_objective",
     "dspark_schedule_threshold",

@@ -57,6 +57,9 @@ def load_library():
     L.dspark_markov_draft.restype = _I
     L.dspark_markov_draft.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]
+    L.dspark_markov_draft_conf.restype = _I
+    L.dspark_markov_draft_conf.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P,
+                                           _P, _P, ctypes.c_size_t, _P]
     L.dspark_schedule.restype = _I
     L.dspark_schedule.argtypes = [_P, _P, _I, _I, ctypes.c_int64, _P, _P, _P]
     L.dspark_schedule_objective.restype = _I
@@ -152,6 +155,38 @@ def dspark_markov_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: 
                                             _ptr(lse), _ptr(ws), ws.numel(), _stream(dev, stream))
     _check(rc, "dspark_markov_draft")
     return tok, p, lse
+
+
+def dspark_markov_draft_conf(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor, seed: int,
+                             z0: torch.Tensor, wc: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                             out: Optional[Tuple] = None, stream=None):
+    """Draft gamma tokens per request and the Markov-conditioned confidence
+    logits z[b][k-1] = z0[b][k-1] + <A[x_{k-1}], wc>.  Returns (draft_tok int32,
+    draft_p f32, draft_lse f64, z f32), each [B][g]."""
+    dev = L.device
+    _dev(L, "L", None)
+    B, gamma, V = L.shape
+    r = A.shape[1]
+    _dev(A, "A", dev, L.dtype, (V, r))
+    _dev(Bm, "Bm", dev, L.dtype, (r, V))
+    _dev(x0, "x0", dev, torch.int32, (B,))
+    _dev(z0, "z0", dev, torch.float32, (B, gamma))
+    _dev(wc, "wc", dev, L.dtype, (r,))
+    if out is None:
+        tok = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+        p = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, gamma), dtype=torch.float64, device=dev)
+        z = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    else:
+        tok, p, lse, z = out
+    if ws is None:
+        ws = workspace(B, gamma, V, r, dev)
+    rc = load_library().dspark_markov_draft_conf(_dtype_code(L), _ptr(L), _ptr(A), _ptr(Bm), _ptr(x0), B, gamma, V,
+                                                 r, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(z0), _ptr(wc),
+                                                 _ptr(tok), _ptr(p), _ptr(lse), _ptr(z), _ptr(ws), ws.numel(),
+                                                 _stream(dev, stream))
+    _check(rc, "dspark_markov_draft_conf")
+    return tok, p, lse, z
 
 
 def dspark_schedule(z: Optional[torch.Tensor], temps: Optional[torch.Tensor], budget: int,

@@ -144,11 +144,11 @@ size_t dspark_workspace_size(int B, int gamma, int V, int r)
     return ws_layout(B, gamma, V).total;
 }
 
-int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B, int gamma,
-                        int V, int r, uint64_t seed, int32_t* draft_tok, float* draft_p, double* draft_lse, void* ws,
-                        size_t ws_bytes, void* stream)
+static int markov_draft_impl(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
+                             int gamma, int V, int r, uint64_t seed, const float* z0, const void* wc,
+                             int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, void* ws,
+                             size_t ws_bytes, void* stream)
 {
-    g_err[0] = 0;
     if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
     int rc = check_common(B, gamma, V, r);
     if (rc) return rc;
@@ -163,10 +163,30 @@ int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm,
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int k = 1; k <= gamma; ++k) {
         hipError_t e = launch_draft_step(dtype, L, A, Bm, x0, B, gamma, V, r, k, seed, draft_tok, draft_p, draft_lse,
-                                         ws, lay, s);
+                                         z0, wc, z_out, ws, lay, s);
         if (e != hipSuccess) return hip_status(e, "draft launch");
     }
     return DSPARK_OK;
+}
+
+int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B, int gamma,
+                        int V, int r, uint64_t seed, int32_t* draft_tok, float* draft_p, double* draft_lse, void* ws,
+                        size_t ws_bytes, void* stream)
+{
+    g_err[0] = 0;
+    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, seed, nullptr, nullptr, draft_tok, draft_p,
+                             draft_lse, nullptr, ws, ws_bytes, stream);
+}
+
+int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
+                             int gamma, int V, int r, uint64_t seed, const float* z0, const void* wc,
+                             int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, void* ws,
+                             size_t ws_bytes, void* stream)
+{
+    g_err[0] = 0;
+    if (B > 0 && (!z0 || !wc || !z_out)) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, seed, z0, wc, draft_tok, draft_p, draft_lse, z_out,
+                             ws, ws_bytes, stream);
 }
 
 int dspark_schedule(const float* z, const float* temps, int B, int gamma, int64_t budget, float* survival,

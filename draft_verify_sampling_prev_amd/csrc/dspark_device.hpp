@@ -44,6 +44,36 @@ struct F32 {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Markov-conditioned confidence logit of one draft position (the linear
+// confidence head's token part; paperlayer.ai summary, Appendix A: the Markov
+// confidence head sees the previously sampled token):
+//     z[i] = z0[i] + <A[x], wc>.
+// One wave: lane l multiplies elements 4l .. 4l+3 (r <= 256, a multiple of 8)
+// in order with fused multiply-adds, the lane sums are added by the xor
+// butterflies 32, 16, ..., 1, and lane 0 stores.  z == nullptr: nothing.
+struct ConfOut {
+    const float* z0;
+    const void* wc;
+    float* z;
+};
+
+template <class DT>
+__device__ __forceinline__ void markov_confidence(const typename DT::T* __restrict__ A, const ConfOut& co, int x,
+                                                  int r, int i)
+{
+    const int lane = threadIdx.x & 63;
+    const auto* wc = static_cast<const typename DT::T*>(co.wc);
+    float s = 0.0f;
+    if (4 * lane < r) {
+        const typename DT::T* a = A + (size_t)x * r + 4 * lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s = __builtin_fmaf(DT::to_f32(a[j]), DT::to_f32(wc[4 * lane + j]), s);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (lane == 0) co.z[i] = co.z0[i] + s;
+}
+
 // ---------------------------------------------------------------------------
 // Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
 // 4-word S-box with multipliers 0xD2511F53 / 0xCD9E8D57 and a key advanced by

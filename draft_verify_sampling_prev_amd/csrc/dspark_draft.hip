@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
                                                            const int32_t* __restrict__ x0, int32_t* tok,
                                                            float* __restrict__ p_out, double* __restrict__ lse_out,
                                                            const float2* __restrict__ part, int B, int gamma, int V,
-                                                           int r, int k, int nT, uint64_t seed)
+                                                           int r, int k, int nT, uint64_t seed, ConfOut co)
 {
     typedef TileTraits<DT> TT;
     __shared__ __attribute__((aligned(1024))) char lds[TT::kLdsBytes];
@@ -334,6 +334,7 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
 
     const int n0 = loc.idx * TT::kCols;
     const int prev = cond_token(x0, tok, b, gamma, k, V);
+    if (co.z && (threadIdx.x >> 6) == 0) markov_confidence<DT>(A, co, prev, r, b * gamma + (k - 1));
     const auto* lrow = L + ((size_t)b * gamma + (k - 1)) * V;
     const float mt = pr[loc.idx].x;
     const double scale = tile_mass(mt, 1.0, M);
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
                                                           float* __restrict__ p_out, double* __restrict__ lse_out,
                                                           const float2* __restrict__ part, uint16_t* __restrict__ ag,
                                                           int B, int gamma, int V, int r, int k, int nT, int nM_next,
-                                                          int S_next, uint64_t seed)
+                                                          int S_next, uint64_t seed, ConfOut co)
 {
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
     // AG (not the last step): a second wave reads the next tile launch's
@@ -443,6 +444,7 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
     int i0;
     load_slices<PER>(pr, nT, make_float2(-INFINITY, 0.0f), q, &i0);
     const int prev = cond_token(x0, tok, b, gamma, k, V);
+    if (co.z) markov_confidence<Bf16>(A, co, prev, r, b * gamma + (k - 1));
     uint4 a[1][8];
     {
         const uint16_t* arow[1] = { A + (size_t)prev * r };
@@ -511,8 +513,10 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
 
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
                              int gamma, int V, int r, int k, uint64_t seed, int32_t* tok, float* p, double* lse,
-                             void* ws, const WsLayout& lay, hipStream_t s)
+                             const float* z0, const void* wc, float* z_out, void* ws, const WsLayout& lay,
+                             hipStream_t s)
 {
+    const ConfOut co{ z0, wc, z_out };
     float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.draft_part);
     uint16_t* ag = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.ag);
     const int nT = n_tiles(dtype, V);
@@ -546,15 +550,15 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
                                 : k_draft_locate_bf16<0, 64, false>);
         hipLaunchKernelGGL(kern, dim3(B), dim3(wag ? 128 : 64), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
-                           ag, B, gamma, V, r, k, nT, nM, S, seed);
+                           ag, B, gamma, V, r, k, nT, nM, S, seed, co);
     } else if (dtype == 1) {
         hipLaunchKernelGGL(k_draft_locate<Bf16>, dim3(B), dim3(kThreads), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
-                           B, gamma, V, r, k, nT, seed);
+                           B, gamma, V, r, k, nT, seed, co);
     } else
         hipLaunchKernelGGL(k_draft_locate<F32>, dim3(B), dim3(kThreads), 0, s, static_cast<const float*>(L),
                            static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, p, lse, part, B,
-                           gamma, V, r, k, nT, seed);
+                           gamma, V, r, k, nT, seed, co);
     prof_end(K_DRAFT_LOCATE, s);
     return hipGetLastError();
 }

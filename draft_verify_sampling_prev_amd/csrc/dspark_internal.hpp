@@ -58,9 +58,12 @@ void prof_begin(int id, hipStream_t s);
 void prof_end(int id, hipStream_t s);
 
 // Launchers (return hipGetLastError()).
+// z0/wc/z_out (all null, or all set): the Markov-conditioned confidence
+// logit z_out[b][k-1] = z0[b][k-1] + <A[x_{k-1}], wc>, computed by the locate.
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0,
                              int B, int gamma, int V, int r, int k, uint64_t seed, int32_t* tok, float* p,
-                             double* lse, void* ws, const WsLayout& lay, hipStream_t s);
+                             double* lse, const float* z0, const void* wc, float* z_out, void* ws,
+                             const WsLayout& lay, hipStream_t s);
 
 hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,
                            int32_t* len, hipStream_t s);

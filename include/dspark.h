@@ -108,6 +108,29 @@ int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm,
                         size_t ws_bytes, void* stream);
 
 /*
+ * dspark_markov_draft_conf -- dspark_markov_draft plus the Markov-conditioned
+ * confidence logits, fused into the draft steps (paperlayer.ai summary,
+ * Appendix A: the Markov confidence head sees the previously sampled token,
+ * so the survival of position 2 depends on x_1; menfem.com note: the
+ * confidence head is linear).  Draft outputs are exactly those of
+ * dspark_markov_draft; in addition, for k = 1..gamma,
+ *     z_out[b][k-1] = z0[b][k-1] + sum_j A[x_{k-1}][j] * wc[j]   (fp32)
+ * (x_0 = x0[b]), the token part being the conditioning code of the token the
+ * step conditions on (the same rows of A the Markov head uses) dotted with
+ * the head's weight vector.  z_out feeds dspark_schedule* as z.
+ *
+ *   z0     [B][gamma] f32   backbone part of the confidence logit (input)
+ *   wc     [r] (dtype)      confidence weights on the Markov code
+ *   z_out  [B][gamma] f32   out
+ * Other arguments, limits and errors as dspark_markov_draft (z0, wc, z_out
+ * must be non-null when B > 0).
+ */
+int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
+                             int gamma, int V, int r, uint64_t seed, const float* z0, const void* wc,
+                             int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * dspark_schedule -- confidence-scheduled verify lengths (paperlayer.ai
  * summary, section 3.2; menfem.com note, "Hardware-aware prefix scheduler";
  * llm-wiki.hwlabs.dev: prefix survival = probability that positions 1..i are

@@ -39,7 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_python_binding_has_the_same_names():
-    for n in ("dspark_markov_draft", "dspark_schedule", "dspark_schedule_objective", "dspark_schedule_threshold",
+    for n in ("dspark_markov_draft", "dspark_markov_draft_conf", "dspark_schedule", "dspark_schedule_objective",
+              "dspark_schedule_threshold",
               "dspark_verify", "dspark_workspace_size", "dspark_version"):
         assert callable(getattr(dsp, n))
 
@@ -79,6 +80,20 @@ def test_draft_argument_errors(lib):
     assert b"workspace" in lib.dspark_last_error()
     # B == 0 is a no-op, even with null pointers
     assert _draft(lib, B=0, ptr=None, L=None) == OK
+
+
+def test_draft_conf_argument_errors(lib):
+    f = lib.dspark_markov_draft_conf
+
+    def call(z0=FAKE, wc=FAKE, z=FAKE, B=4, dtype=1):
+        return f(dtype, FAKE, FAKE, FAKE, FAKE, B, 5, 1024, 16, ctypes.c_uint64(1), z0, wc, FAKE, FAKE, FAKE, z, FAKE,
+                 1 << 30, None)
+
+    assert call(z0=None) == INVALID
+    assert call(wc=None) == INVALID
+    assert call(z=None) == INVALID
+    assert call(dtype=5) == UNSUPPORTED
+    assert call(B=0, z0=None, wc=None, z=None) == OK
 
 
 def test_schedule_argument_errors(lib):
