@@ -444,11 +444,19 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
     int i0;
     load_slices<PER>(pr, nT, make_float2(-INFINITY, 0.0f), q, &i0);
     const int prev = cond_token(x0, tok, b, gamma, k, V);
-    if (co.z) markov_confidence<Bf16>(A, co, prev, r, b * gamma + (k - 1));
     uint4 a[1][8];
     {
         const uint16_t* arow[1] = { A + (size_t)prev * r };
         load_a_frags<1>(arow, r, a);
+    }
+    // Confidence weights in the A operand's order (lane group G holds
+    // k = 32ks + 8G .. +7), for the Markov-conditioned confidence logit.
+    uint4 wcf[8];
+    if (co.z) {
+        const uint16_t* wc = static_cast<const uint16_t*>(co.wc);
+        const int kq8 = 8 * (lane >> 4);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) wcf[ks] = ld16(wc + min(32 * ks + kq8, r - 8));
     }
     float mloc = -INFINITY;
 #pragma unroll
@@ -489,6 +497,18 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
     };
     row_tile_vm_wave<KS, AG ? 32 : 0>(L + ((size_t)b * gamma + (k - 1)) * V, a, Bm, V, r, n0, lds, f,
                                       dma_candidates);
+    if (co.z) {
+        // z = z0 + <A[prev], wc> from the A operand already in registers
+        // (pieces past r are zero): 64 products per lane in (k step, element)
+        // order, then the four lane groups by the xor-16 / xor-32 butterflies.
+        float sdot = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sdot = __builtin_fmaf(Bf16::get(a[0][ks], e), Bf16::get(wcf[ks], e), sdot);
+        sdot = sum_xor16_32(sdot);
+        if (lane == 0) co.z[b * gamma + (k - 1)] = co.z0[b * gamma + (k - 1)] + sdot;
+    }
     const double scale = tile_mass(mt, 1.0, M);
     const float ml = row_mlog2(mt);
     double wsel;
