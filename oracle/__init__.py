@@ -91,6 +91,8 @@ def _declare(L):
     L.orc_markov_draft.restype = ctypes.c_int
     L.orc_survival.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, _P]
     L.orc_survival.restype = None
+    L.orc_rnn_state.argtypes = [_P, _P, _P, ctypes.c_int, _P]
+    L.orc_rnn_state.restype = None
     L.orc_markov_confidence.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]
     L.orc_markov_confidence.restype = ctypes.c_int
     L.orc_select.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int64, _P]
@@ -215,6 +217,15 @@ def survival(z, T) -> np.ndarray:
     th = np.zeros((B, gamma), dtype=np.float32)
     lib().orc_survival(_ptr(zz), _ptr(TT), B, gamma, _ptr(th))
     return th
+
+
+def rnn_state(Wt, h_prev, a) -> np.ndarray:
+    """One RNN-head update in double: tanh(Wt^T h_prev + a) (Wt[j][i] multiplies h_prev[j] into output i)."""
+    W, h, aa = _f32(Wt), _f32(h_prev), _f32(a)
+    r = aa.shape[0]
+    out = np.zeros(r, dtype=np.float64)
+    lib().orc_rnn_state(_ptr(W), _ptr(h), _ptr(aa), r, _ptr(out))
+    return out
 
 
 def markov_confidence(A, wc, x0, tok, z0) -> np.ndarray:

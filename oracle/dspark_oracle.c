@@ -249,6 +249,24 @@ void orc_survival(const float* z, const float* T, int B, int gamma, float* theta
 }
 
 /* ------------------------------------------------------------------------ */
+/* RNN sequential head (menfem.com note, Key Contributions: the second head    */
+/* variant keeps the whole in-block prefix in a recurrent state instead of    */
+/* the first-order Markov dependency).  Reading taken here: a state          */
+/* h_k = tanh(W h_{k-1} + A[x_{k-1}]), h_0 = 0, replaces A[x_{k-1}] in the    */
+/* bias, Delta_k = h_k . Bm.  Wt is W transposed: Wt[j][i] multiplies         */
+/* h_{k-1}[j] into output i.  This computes one update in double:            */
+/* out[i] = tanh(sum_j Wt[j][i] h_prev[j] + a[i]).                           */
+/* ------------------------------------------------------------------------ */
+void orc_rnn_state(const float* Wt, const float* h_prev, const float* a, int r, double* out)
+{
+    for (int i = 0; i < r; ++i) {
+        double s = a[i];
+        for (int j = 0; j < r; ++j) s += (double)Wt[(size_t)j * r + i] * (double)h_prev[j];
+        out[i] = tanh(s);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Markov-conditioned confidence logit (paperlayer.ai summary, Appendix A: the */
 /* Markov confidence head sees the previously sampled token, so c_2 depends on */
 /* x_1; menfem.com note: the confidence head is linear).  Reading taken here:  */

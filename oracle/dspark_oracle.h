@@ -46,6 +46,7 @@ int orc_markov_draft(const float* L, const float* A, const float* Bm, const int3
                      int r, uint64_t seed, int32_t* tok, float* p, double* lse);
 
 void orc_survival(const float* z, const float* T, int B, int gamma, float* theta);
+void orc_rnn_state(const float* Wt, const float* h_prev, const float* a, int r, double* out);
 int orc_markov_confidence(const float* A, const float* wc, const int32_t* x0, const int32_t* tok, const float* z0,
                           int B, int gamma, int V, int r, float* z);
 int orc_select(const float* theta, int B, int gamma, int64_t budget, int32_t* len);

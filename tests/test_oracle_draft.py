@@ -145,3 +145,37 @@ def test_logsumexp_matches_library():
     row = (g.standard_normal(129280) * 2).astype(np.float32)
     ref = torch.logsumexp(torch.from_numpy(row).double(), 0).item()
     assert oracle.logsumexp(row) == pytest.approx(ref, rel=1e-14)
+
+
+# ----------------------------------------------------------------------------- RNN head state update
+def test_rnn_state_zero_weights_is_tanh_of_code():
+    a = np.array([0.0, 0.5, -1.25, 3.0], dtype=np.float32)
+    out = oracle.rnn_state(np.zeros((4, 4), dtype=np.float32), np.ones(4, dtype=np.float32), a)
+    # tanh(0) = 0 exactly; tanh is odd; |tanh(x)| < 1; tanh(x) ~ x - x^3/3 near 0
+    assert out[0] == 0.0 and abs(out[1] - (0.5 - 0.5**3 / 3 + 2 * 0.5**5 / 15)) < 0.5**7 * 17 / 315 + 1e-12
+    assert np.array_equal(oracle.rnn_state(np.zeros((4, 4), np.float32), np.ones(4, np.float32), -a), -out)
+    assert np.all(np.abs(out) < 1.0)
+
+
+def test_rnn_state_one_hot_state_selects_a_column_of_w():
+    """h_prev = e_j: the pre-activation is W[:, j] + a = Wt[j, :] + a (a transposed W would give Wt[:, j])."""
+    g = np.random.default_rng(11)
+    r = 6
+    Wt = g.integers(-2, 3, (r, r)).astype(np.float32)
+    a = g.integers(-1, 2, r).astype(np.float32)
+    for j in range(r):
+        h = np.zeros(r, dtype=np.float32)
+        h[j] = 1.0
+        out = oracle.rnn_state(Wt, h, a)
+        pre = Wt[j].astype(np.float64) + a
+        assert np.array_equal(np.round(np.arctanh(np.clip(out, -1 + 1e-15, 1 - 1e-15)), 9), np.round(pre, 9))
+
+
+def test_rnn_state_diagonal_weights_act_elementwise():
+    d = np.array([0.5, -2.0, 1.0, 0.0], dtype=np.float32)
+    h = np.array([1.0, 0.25, -0.5, 7.0], dtype=np.float32)
+    a = np.array([0.0, 0.5, 0.5, -0.25], dtype=np.float32)
+    out = oracle.rnn_state(np.diag(d), h, a)
+    pre = d.astype(np.float64) * h + a
+    # tanh(x) = (e^{2x} - 1) / (e^{2x} + 1)
+    assert np.allclose(out, (np.exp(2 * pre) - 1) / (np.exp(2 * pre) + 1), rtol=0, atol=1e-15)
