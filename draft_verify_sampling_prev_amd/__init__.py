@@ -10,6 +10,8 @@ from .binding import (  # noqa: F401
     DsparkError,
     dspark_markov_draft,
     dspark_markov_draft_conf,
+    dspark_rnn_draft,
+    dspark_rnn_verify,
     dspark_schedule,
     dspark_schedule_objective,
     dspark_schedule_threshold,
@@ -24,6 +26,8 @@ __all__ = [
     "DsparkError",
     "dspark_markov_draft",
     "dspark_markov_draft_conf",
+    "dspark_rnn_draft",
+    "dspark_rnn_verify",
     "dspark_schedule",
     "dspark_schedule_objective",
     "dspark_schedule_threshold",

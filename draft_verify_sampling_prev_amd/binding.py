@@ -60,6 +60,12 @@ def load_library():
     L.dspark_markov_draft_conf.restype = _I
     L.dspark_markov_draft_conf.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P,
                                            _P, _P, ctypes.c_size_t, _P]
+    L.dspark_rnn_draft.restype = _I
+    L.dspark_rnn_draft.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P,
+                                   ctypes.c_size_t, _P]
+    L.dspark_rnn_verify.restype = _I
+    L.dspark_rnn_verify.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P,
+                                    _P, _P, ctypes.c_size_t, _P]
     L.dspark_schedule.restype = _I
     L.dspark_schedule.argtypes = [_P, _P, _I, _I, ctypes.c_int64, _P, _P, _P]
     L.dspark_schedule_objective.restype = _I
@@ -189,6 +195,35 @@ def dspark_markov_draft_conf(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
     return tok, p, lse, z
 
 
+def dspark_rnn_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, Wt: torch.Tensor, x0: torch.Tensor, seed: int,
+                     ws: Optional[torch.Tensor] = None, out: Optional[Tuple] = None, stream=None):
+    """Draft gamma tokens per request with the RNN head.  Returns (draft_tok int32 [B][g], draft_p f32,
+    draft_lse f64, H [B][g][r] in the logits' dtype)."""
+    dev = L.device
+    _dev(L, "L", None)
+    B, gamma, V = L.shape
+    r = A.shape[1]
+    _dev(A, "A", dev, L.dtype, (V, r))
+    _dev(Bm, "Bm", dev, L.dtype, (r, V))
+    _dev(Wt, "Wt", dev, L.dtype, (r, r))
+    _dev(x0, "x0", dev, torch.int32, (B,))
+    if out is None:
+        tok = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+        p = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, gamma), dtype=torch.float64, device=dev)
+        H = torch.empty((B, gamma, r), dtype=L.dtype, device=dev)
+    else:
+        tok, p, lse, H = out
+    _dev(H, "H", dev, L.dtype, (B, gamma, r))
+    if ws is None:
+        ws = workspace(B, gamma, V, r, dev)
+    rc = load_library().dspark_rnn_draft(_dtype_code(L), _ptr(L), _ptr(A), _ptr(Bm), _ptr(Wt), _ptr(x0), B, gamma, V,
+                                         r, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(tok), _ptr(p), _ptr(lse),
+                                         _ptr(H), _ptr(ws), ws.numel(), _stream(dev, stream))
+    _check(rc, "dspark_rnn_draft")
+    return tok, p, lse, H
+
+
 def dspark_schedule(z: Optional[torch.Tensor], temps: Optional[torch.Tensor], budget: int,
                     survival: Optional[torch.Tensor] = None, out_len: Optional[torch.Tensor] = None,
                     B: Optional[int] = None, gamma: Optional[int] = None,
@@ -296,6 +331,40 @@ def dspark_verify(Tgt: torch.Tensor, L: torch.Tensor, A: torch.Tensor, Bm: torch
                                       ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(acc), _ptr(out_tok),
                                       _ptr(n_out), _ptr(tp), _ptr(ws), ws.numel(), _stream(dev, stream))
     _check(rc, "dspark_verify")
+    return acc, out_tok, n_out, tp
+
+
+def dspark_rnn_verify(Tgt: torch.Tensor, L: torch.Tensor, H: torch.Tensor, Bm: torch.Tensor, draft_tok: torch.Tensor,
+                      draft_p: torch.Tensor, draft_lse: torch.Tensor, verify_len: torch.Tensor, seed: int,
+                      ws: Optional[torch.Tensor] = None, out: Optional[Tuple] = None, want_target_p: bool = True,
+                      stream=None):
+    """Verification of an RNN-head draft (the residual rebuilds draft rows from the states H [B][g][r]).
+    Returns (accepted int32 [B], out_tok int32 [B][g+1], n_out int32 [B], target_p f32 [B][g] or None)."""
+    dev = L.device
+    _dev(L, "L", None)
+    B, gamma, V = L.shape
+    r = H.shape[2]
+    _dev(Tgt, "Tgt", dev, L.dtype, (B, gamma + 1, V))
+    _dev(H, "H", dev, L.dtype, (B, gamma, r))
+    _dev(Bm, "Bm", dev, L.dtype, (r, V))
+    _dev(draft_tok, "draft_tok", dev, torch.int32, (B, gamma))
+    _dev(draft_p, "draft_p", dev, torch.float32, (B, gamma))
+    _dev(draft_lse, "draft_lse", dev, torch.float64, (B, gamma))
+    _dev(verify_len, "verify_len", dev, torch.int32, (B,))
+    if out is None:
+        acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        out_tok = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+        n_out = torch.empty((B,), dtype=torch.int32, device=dev)
+        tp = torch.empty((B, gamma), dtype=torch.float32, device=dev) if want_target_p else None
+    else:
+        acc, out_tok, n_out, tp = out
+    if ws is None:
+        ws = workspace(B, gamma, V, r, dev)
+    rc = load_library().dspark_rnn_verify(_dtype_code(L), _ptr(Tgt), _ptr(L), _ptr(H), _ptr(Bm), _ptr(draft_tok),
+                                          _ptr(draft_p), _ptr(draft_lse), _ptr(verify_len), B, gamma, V, r,
+                                          ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(acc), _ptr(out_tok),
+                                          _ptr(n_out), _ptr(tp), _ptr(ws), ws.numel(), _stream(dev, stream))
+    _check(rc, "dspark_rnn_verify")
     return acc, out_tok, n_out, tp
 
 

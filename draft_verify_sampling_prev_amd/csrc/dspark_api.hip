@@ -146,8 +146,8 @@ size_t dspark_workspace_size(int B, int gamma, int V, int r)
 
 static int markov_draft_impl(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
                              int gamma, int V, int r, uint64_t seed, const float* z0, const void* wc,
-                             int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, void* ws,
-                             size_t ws_bytes, void* stream)
+                             int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, const void* Wt,
+                             void* H, void* ws, size_t ws_bytes, void* stream)
 {
     if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
     int rc = check_common(B, gamma, V, r);
@@ -163,7 +163,7 @@ static int markov_draft_impl(int dtype, const void* L, const void* A, const void
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int k = 1; k <= gamma; ++k) {
         hipError_t e = launch_draft_step(dtype, L, A, Bm, x0, B, gamma, V, r, k, seed, draft_tok, draft_p, draft_lse,
-                                         z0, wc, z_out, ws, lay, s);
+                                         z0, wc, z_out, Wt, H, ws, lay, s);
         if (e != hipSuccess) return hip_status(e, "draft launch");
     }
     return DSPARK_OK;
@@ -175,7 +175,7 @@ int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm,
 {
     g_err[0] = 0;
     return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, seed, nullptr, nullptr, draft_tok, draft_p,
-                             draft_lse, nullptr, ws, ws_bytes, stream);
+                             draft_lse, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
@@ -186,7 +186,18 @@ int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void
     g_err[0] = 0;
     if (B > 0 && (!z0 || !wc || !z_out)) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
     return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, seed, z0, wc, draft_tok, draft_p, draft_lse, z_out,
-                             ws, ws_bytes, stream);
+                             nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int dspark_rnn_draft(int dtype, const void* L, const void* A, const void* Bm, const void* Wt, const int32_t* x0, int B,
+                     int gamma, int V, int r, uint64_t seed, int32_t* draft_tok, float* draft_p, double* draft_lse,
+                     void* H, void* ws, size_t ws_bytes, void* stream)
+{
+    g_err[0] = 0;
+    if (B > 0 && (!Wt || !H)) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    if (B > 0 && !aligned16(H)) return fail(DSPARK_ERR_INVALID_ARG, "H must be 16-byte aligned");
+    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, seed, nullptr, nullptr, draft_tok, draft_p,
+                             draft_lse, nullptr, Wt, H, ws, ws_bytes, stream);
 }
 
 int dspark_schedule(const float* z, const float* temps, int B, int gamma, int64_t budget, float* survival,
@@ -243,28 +254,49 @@ int dspark_schedule_threshold(const float* z, const float* temps, int B, int gam
                       "schedule_threshold launch");
 }
 
+static int verify_impl(int dtype, const void* Tgt, const void* L, const void* A, const void* Bm, const int32_t* x0,
+                       const int32_t* draft_tok, const float* draft_p, const double* draft_lse,
+                       const int32_t* verify_len, int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted,
+                       int32_t* out_tok, int32_t* n_out, float* target_p, const void* H, void* ws, size_t ws_bytes,
+                       void* stream)
+{
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    int rc = check_common(B, gamma, V, r);
+    if (rc) return rc;
+    if (B == 0) return DSPARK_OK;
+    if (!Tgt || !L || !A || !Bm || (!x0 && !H) || !draft_tok || !draft_p || !draft_lse || !verify_len || !accepted ||
+        !out_tok || !n_out || !ws)
+        return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(Tgt) || !aligned16(L) || !aligned16(A) || !aligned16(Bm))
+        return fail(DSPARK_ERR_INVALID_ARG, "Tgt, L, A (or H) and Bm must be 16-byte aligned");
+    const WsLayout lay = ws_layout(B, gamma, V);
+    if (ws_bytes < lay.total)
+        return fail(DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, lay.total);
+    return hip_status(launch_verify(dtype, Tgt, L, A, Bm, x0, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r,
+                                    seed, accepted, out_tok, n_out, target_p, H, ws, lay,
+                                    static_cast<hipStream_t>(stream)),
+                      "verify launch");
+}
+
 int dspark_verify(int dtype, const void* Tgt, const void* L, const void* A, const void* Bm, const int32_t* x0,
                   const int32_t* draft_tok, const float* draft_p, const double* draft_lse, const int32_t* verify_len,
                   int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok, int32_t* n_out,
                   float* target_p, void* ws, size_t ws_bytes, void* stream)
 {
     g_err[0] = 0;
-    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
-    int rc = check_common(B, gamma, V, r);
-    if (rc) return rc;
-    if (B == 0) return DSPARK_OK;
-    if (!Tgt || !L || !A || !Bm || !x0 || !draft_tok || !draft_p || !draft_lse || !verify_len || !accepted ||
-        !out_tok || !n_out || !ws)
-        return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
-    if (!aligned16(Tgt) || !aligned16(L) || !aligned16(A) || !aligned16(Bm))
-        return fail(DSPARK_ERR_INVALID_ARG, "Tgt, L, A and Bm must be 16-byte aligned");
-    const WsLayout lay = ws_layout(B, gamma, V);
-    if (ws_bytes < lay.total)
-        return fail(DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, lay.total);
-    return hip_status(launch_verify(dtype, Tgt, L, A, Bm, x0, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r,
-                                    seed, accepted, out_tok, n_out, target_p, ws, lay,
-                                    static_cast<hipStream_t>(stream)),
-                      "verify launch");
+    return verify_impl(dtype, Tgt, L, A, Bm, x0, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r, seed,
+                       accepted, out_tok, n_out, target_p, nullptr, ws, ws_bytes, stream);
+}
+
+int dspark_rnn_verify(int dtype, const void* Tgt, const void* L, const void* H, const void* Bm,
+                      const int32_t* draft_tok, const float* draft_p, const double* draft_lse,
+                      const int32_t* verify_len, int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted,
+                      int32_t* out_tok, int32_t* n_out, float* target_p, void* ws, size_t ws_bytes, void* stream)
+{
+    g_err[0] = 0;
+    if (B > 0 && !H) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    return verify_impl(dtype, Tgt, L, H, Bm, nullptr, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r, seed,
+                       accepted, out_tok, n_out, target_p, H, ws, ws_bytes, stream);
 }
 
 int dspark_profile_start(int max_launches, unsigned kernel_mask)

@@ -91,8 +91,8 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
                                                               const float* __restrict__ A,
                                                               const float* __restrict__ Bm,
                                                               const int32_t* __restrict__ x0, const int32_t* tok,
-                                                              int B, int gamma, int V, int r, int k, int nT, int nM,
-                                                              float2* __restrict__ part)
+                                                              const float* __restrict__ H, int B, int gamma, int V,
+                                                              int r, int k, int nT, int nM, float2* __restrict__ part)
 {
     __shared__ __attribute__((aligned(16))) char lds[markov_lds_bytes<F32>()];
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
         const int ra = min(mw0 + 16 * mb + (lane & 15), B - 1);
-        arow[mb] = A + (size_t)cond_token(x0, tok, ra, gamma, k, V) * r;
+        arow[mb] = H ? H + ((size_t)ra * gamma + (k - 1)) * r : A + (size_t)cond_token(x0, tok, ra, gamma, k, V) * r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = mw0 + 16 * mb + 4 * (lane >> 4) + i;
@@ -153,8 +153,9 @@ constexpr int kPartTiles = 12;  // tiles per slot whose partials fit the LDS sta
 template <int KS>
 __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
-    const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const uint16_t* __restrict__ ag, int B,
-    int gamma, int V, int r, int k, int nT, int nM, int S, float2* __restrict__ part)
+    const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const uint16_t* __restrict__ ag,
+    const uint16_t* __restrict__ H, int B, int gamma, int V, int r, int k, int nT, int nM, int S,
+    float2* __restrict__ part)
 {
     constexpr int NW = kTileWaves, R = kTileRows;
     __shared__ __attribute__((aligned(1024))) char s0[kBmTileBytes];
@@ -275,7 +276,12 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) tk[bb] = cond_token_raw(x0, tok, min(mw + 16 * bb + c, B - 1), gamma, k);
         first_tile();
-        const uint16_t* arow[2] = { A + (size_t)clamp_token(tk[0], V) * r, A + (size_t)clamp_token(tk[1], V) * r };
+        // The operand rows: A[x] (Markov head) or the rows' RNN states.
+        const uint16_t* arow[2];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+            arow[bb] = H ? H + ((size_t)min(mw + 16 * bb + c, B - 1) * gamma + (k - 1)) * r
+                         : A + (size_t)clamp_token(tk[bb], V) * r;
         load_a_frags<2>(arow, r, a);
     }
     issue_fence();
@@ -313,8 +319,9 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
                                                            const typename DT::T* __restrict__ Bm,
                                                            const int32_t* __restrict__ x0, int32_t* tok,
                                                            float* __restrict__ p_out, double* __restrict__ lse_out,
-                                                           const float2* __restrict__ part, int B, int gamma, int V,
-                                                           int r, int k, int nT, uint64_t seed, ConfOut co)
+                                                           const float2* __restrict__ part,
+                                                           const typename DT::T* __restrict__ H, int B, int gamma,
+                                                           int V, int r, int k, int nT, uint64_t seed, ConfOut co)
 {
     typedef TileTraits<DT> TT;
     __shared__ __attribute__((aligned(1024))) char lds[TT::kLdsBytes];
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
     int j;
     if constexpr (std::is_same<DT, Bf16>::value) {
         floatx4 f[4];
-        row_tile_vm(lrow, A, Bm, prev, V, r, n0, lds, f);
+        row_tile_vm(lrow, H ? H + ((size_t)b * gamma + (k - 1)) * r : A, Bm, H ? 0 : prev, V, r, n0, lds, f);
         if ((threadIdx.x >> 6) != 0) return;
         j = scan_vm_tile(
             n0, b, scale, loc.cprev, loc.tau,
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
             &wsel);
     } else {
         float f[TT::kNB];
-        row_tile_f(lrow, A, Bm, prev, V, r, n0, lds, f);
+        row_tile_f(lrow, H ? H + ((size_t)b * gamma + (k - 1)) * r : A, Bm, H ? 0 : prev, V, r, n0, lds, f);
         if ((threadIdx.x >> 6) != 0) return;
         const int l16 = threadIdx.x & 15;
         double w[TT::kNB];
@@ -418,8 +425,9 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
                                                           const int32_t* __restrict__ x0, int32_t* tok,
                                                           float* __restrict__ p_out, double* __restrict__ lse_out,
                                                           const float2* __restrict__ part, uint16_t* __restrict__ ag,
-                                                          int B, int gamma, int V, int r, int k, int nT, int nM_next,
-                                                          int S_next, uint64_t seed, ConfOut co)
+                                                          const uint16_t* __restrict__ H, int B, int gamma, int V,
+                                                          int r, int k, int nT, int nM_next, int S_next,
+                                                          uint64_t seed, ConfOut co)
 {
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
     // AG (not the last step): a second wave reads the next tile launch's
@@ -446,7 +454,7 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
     const int prev = cond_token(x0, tok, b, gamma, k, V);
     uint4 a[1][8];
     {
-        const uint16_t* arow[1] = { A + (size_t)prev * r };
+        const uint16_t* arow[1] = { H ? H + ((size_t)b * gamma + (k - 1)) * r : A + (size_t)prev * r };
         load_a_frags<1>(arow, r, a);
     }
     // Confidence weights in the A operand's order (lane group G holds
@@ -531,19 +539,82 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
     }
 }
 
+// ---------------------------------------------------------------------------
+// RNN sequential head (menfem.com note, Key Contributions: the head variant
+// that keeps the whole in-block prefix in a recurrent state instead of the
+// first-order Markov dependency).  Before draft step k:
+//     h_k = tanh(W h_{k-1} + A[x_{k-1}]),  h_0 = 0,
+// stored as row (b, k-1) of H in the element type; it replaces A[x_{k-1}] as
+// the operand of the rank-r bias.  Wt is W transposed (Wt[j][i] multiplies
+// h_{k-1}[j] into output i), so for a fixed j the lanes read consecutive
+// outputs.  One 64-thread workgroup per request; lane l owns outputs
+// l + 64q; the pre-activation starts from A[x][i] and adds the products in j
+// order (fp32 FMA), then fp32 tanh and a round to the element type.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t store_elem(Bf16, float f) { return f32_to_bf16_rne(f); }
+__device__ __forceinline__ float store_elem(F32, float f) { return f; }
+
+template <class DT>
+__global__ __launch_bounds__(64) void k_rnn_state(const typename DT::T* __restrict__ A,
+                                                  const typename DT::T* __restrict__ Wt,
+                                                  const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
+                                                  typename DT::T* H, int B, int gamma, int V, int r, int k)
+{
+    __shared__ float hp[kMaxRank];
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int x = cond_token(x0, tok, b, gamma, k, V);
+    const typename DT::T* arow = A + (size_t)x * r;
+    typename DT::T* hout = H + ((size_t)b * gamma + (k - 1)) * r;
+    if (k >= 2) {
+        const typename DT::T* hprev = H + ((size_t)b * gamma + (k - 2)) * r;
+        for (int j = lane; j < r; j += 64) hp[j] = DT::to_f32(hprev[j]);
+    }
+    __syncthreads();
+    float s[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] = 64 * q + lane < r ? DT::to_f32(arow[64 * q + lane]) : 0.0f;
+    if (k >= 2) {
+        for (int j = 0; j < r; ++j) {
+            const float h = hp[j];
+            const typename DT::T* wrow = Wt + (size_t)j * r;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (64 * q + lane < r) s[q] = __builtin_fmaf(DT::to_f32(wrow[64 * q + lane]), h, s[q]);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (64 * q + lane < r) hout[64 * q + lane] = store_elem(DT{}, tanhf(s[q]));
+}
+
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
                              int gamma, int V, int r, int k, uint64_t seed, int32_t* tok, float* p, double* lse,
-                             const float* z0, const void* wc, float* z_out, void* ws, const WsLayout& lay,
-                             hipStream_t s)
+                             const float* z0, const void* wc, float* z_out, const void* Wt, void* H, void* ws,
+                             const WsLayout& lay, hipStream_t s)
 {
     const ConfOut co{ z0, wc, z_out };
+    if (H) {  // RNN head: this step's operand rows
+        if (dtype == 1)
+            hipLaunchKernelGGL(k_rnn_state<Bf16>, dim3(B), dim3(64), 0, s, static_cast<const uint16_t*>(A),
+                               static_cast<const uint16_t*>(Wt), x0, tok, static_cast<uint16_t*>(H), B, gamma, V, r, k);
+        else
+            hipLaunchKernelGGL(k_rnn_state<F32>, dim3(B), dim3(64), 0, s, static_cast<const float*>(A),
+                               static_cast<const float*>(Wt), x0, tok, static_cast<float*>(H), B, gamma, V, r, k);
+    }
     float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.draft_part);
     uint16_t* ag = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.ag);
     const int nT = n_tiles(dtype, V);
     // The one-wave locate (bf16, up to 4096 tiles) hands the next step its A
     // rows in MFMA order when the rank is 256.
     const bool wave_locate = dtype == 1 && nT <= 64 * 64;
-    const bool ag_path = wave_locate && r == kAgRank;
+    const bool ag_path = wave_locate && r == kAgRank && !H;  // (RNN head: the next operand is the state, not A[x])
     // bf16 tile grid: nM row blocks x S persistent slots.
     const int nM = (B + kTileRows - 1) / kTileRows;
     const int S = std::min(nT, std::max((cu_count() + nM - 1) / nM, (nT + kPartTiles - 1) / kPartTiles));
@@ -552,13 +623,13 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
         auto kern = (r + 31) / 32 == 8 ? k_draft_tiles_bf16<8> : k_draft_tiles_bf16<0>;
         hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok,
-                           static_cast<const uint16_t*>(ag_path && k >= 2 ? ag : nullptr), B, gamma, V, r, k, nT, nM,
-                           S, part);
+                           static_cast<const uint16_t*>(ag_path && k >= 2 ? ag : nullptr),
+                           static_cast<const uint16_t*>(H), B, gamma, V, r, k, nT, nM, S, part);
     } else {
         const int nM32 = (B + 255) / 256;
         hipLaunchKernelGGL(k_draft_tiles_f32, dim3(nT * nM32), dim3(kThreads), 0, s, static_cast<const float*>(L),
-                           static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, B, gamma, V, r, k,
-                           nT, nM32, part);
+                           static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok,
+                           static_cast<const float*>(H), B, gamma, V, r, k, nT, nM32, part);
     }
     prof_end(K_DRAFT_TILES, s);
     prof_begin(K_DRAFT_LOCATE, s);
@@ -570,15 +641,15 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
                                 : k_draft_locate_bf16<0, 64, false>);
         hipLaunchKernelGGL(kern, dim3(B), dim3(wag ? 128 : 64), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
-                           ag, B, gamma, V, r, k, nT, nM, S, seed, co);
+                           ag, static_cast<const uint16_t*>(H), B, gamma, V, r, k, nT, nM, S, seed, co);
     } else if (dtype == 1) {
         hipLaunchKernelGGL(k_draft_locate<Bf16>, dim3(B), dim3(kThreads), 0, s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
-                           B, gamma, V, r, k, nT, seed, co);
+                           static_cast<const uint16_t*>(H), B, gamma, V, r, k, nT, seed, co);
     } else
         hipLaunchKernelGGL(k_draft_locate<F32>, dim3(B), dim3(kThreads), 0, s, static_cast<const float*>(L),
-                           static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, p, lse, part, B,
-                           gamma, V, r, k, nT, seed, co);
+                           static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, p, lse, part,
+                           static_cast<const float*>(H), B, gamma, V, r, k, nT, seed, co);
     prof_end(K_DRAFT_LOCATE, s);
     return hipGetLastError();
 }

@@ -60,10 +60,13 @@ void prof_end(int id, hipStream_t s);
 // Launchers (return hipGetLastError()).
 // z0/wc/z_out (all null, or all set): the Markov-conditioned confidence
 // logit z_out[b][k-1] = z0[b][k-1] + <A[x_{k-1}], wc>, computed by the locate.
+// Wt/H (both null, or both set): the RNN head -- the step first writes the
+// state h_k = tanh(W h_{k-1} + A[x_{k-1}]) into row (b, k-1) of H, which
+// then replaces A[x_{k-1}] as the operand.
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0,
                              int B, int gamma, int V, int r, int k, uint64_t seed, int32_t* tok, float* p,
-                             double* lse, const float* z0, const void* wc, float* z_out, void* ws,
-                             const WsLayout& lay, hipStream_t s);
+                             double* lse, const float* z0, const void* wc, float* z_out, const void* Wt, void* H,
+                             void* ws, const WsLayout& lay, hipStream_t s);
 
 hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,
                            int32_t* len, hipStream_t s);
@@ -75,6 +78,6 @@ hipError_t launch_schedule_threshold(const float* z, const float* temps, int B, 
 hipError_t launch_verify(int dtype, const void* Tg, const void* L, const void* A, const void* Bm, const int32_t* x0,
                          const int32_t* tok, const float* pd, const double* lse_d, const int32_t* len, int B,
                          int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok,
-                         int32_t* n_out, float* target_p, void* ws, const WsLayout& lay, hipStream_t s);
+                         int32_t* n_out, float* target_p, const void* H, void* ws, const WsLayout& lay, hipStream_t s);
 
 }  // namespace dspark

@@ -171,7 +171,7 @@ constexpr int kAcceptThreads = 1024;
 __global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restrict__ pd, const int32_t* __restrict__ len,
                                                            const double* __restrict__ pt,
                                                            const int32_t* __restrict__ x0,
-                                                           const int32_t* __restrict__ tok, int B, int gamma,
+                                                           const int32_t* __restrict__ tok, int B, int gamma, int rnn,
                                                            uint64_t seed, int32_t* __restrict__ accepted,
                                                            int32_t* __restrict__ n_out, float* __restrict__ target_p,
                                                            int32_t* __restrict__ resid_idx,
@@ -225,7 +225,9 @@ __global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restri
             resid_idx[b] = rej ? idx : -1;
             if (rej) {
                 const int ks = accepted_b + 1;
-                const int xprev = ks == 1 ? x0[b] : tok[(size_t)b * gamma + ks - 2];
+                // operand row of the rejected position's draft logits: A[x_{ks-1}],
+                // or with the RNN head the state row (b, ks-1)
+                const int xprev = rnn ? b * gamma + ks - 1 : ks == 1 ? x0[b] : tok[(size_t)b * gamma + ks - 2];
                 resid_list[idx] = make_int4(b, ks, xprev, 0);
             }
         }
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
     const float* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ accepted,
     const int4* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int B, int gamma, int V, int r, int nT,
-    int nM, float2* __restrict__ rpart)
+    int nM, int nA, float2* __restrict__ rpart)
 {
     __shared__ __attribute__((aligned(16))) char lds[markov_lds_bytes<F32>()];
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -285,12 +287,12 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
     floatx4 acc[4][8];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-        const ResidRow ra = resid_row(resid_list, min(mw0 + 16 * mb + (lane & 15), cnt - 1), B, gamma, V);
+        const ResidRow ra = resid_row(resid_list, min(mw0 + 16 * mb + (lane & 15), cnt - 1), B, gamma, nA);
         arow[mb] = A + (size_t)ra.x * r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = mw0 + 16 * mb + 4 * (lane >> 4) + i;
-            const ResidRow rr = resid_row(resid_list, min(row, cnt - 1), B, gamma, V);
+            const ResidRow rr = resid_row(resid_list, min(row, cnt - 1), B, gamma, nA);
             const float* lrow = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = mw0 + 16 * mb + 4 * (lane >> 4) + i;
-            const ResidRow rr = resid_row(resid_list, min(row, cnt - 1), B, gamma, V);
+            const ResidRow rr = resid_row(resid_list, min(row, cnt - 1), B, gamma, nA);
             const float* trow = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
             const float ld = lse_log2(lse_d[(size_t)rr.b * gamma + rr.ks - 1]);
             const float lt = lse_log2(lse_t[(size_t)rr.b * gamma + rr.ks - 1]);
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ accepted,
     const int4* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int B, int gamma, int V, int r, int nT,
-    int nM, int S, float2* __restrict__ rpart)
+    int nM, int S, int nA, float2* __restrict__ rpart)
 {
     constexpr int NW = kTileWaves, R = kTileRows;
     __shared__ __attribute__((aligned(1024))) char s0[kBmTileBytes];
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     issue_fence();
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-        const ResidRow rr = resid_decode(rec[bb], B, gamma, V);
+        const ResidRow rr = resid_decode(rec[bb], B, gamma, nA);
         arow[bb] = A + (size_t)rr.x * r;
         lrow[bb] = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
         trow[bb] = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void k_final(
     const typename DT::T* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ len,
     const int32_t* __restrict__ accepted, const int32_t* __restrict__ resid_idx, const float2* __restrict__ rpart,
-    const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC,
+    const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rnn,
     uint64_t seed, int32_t* __restrict__ out_tok)
 {
     typedef typename DT::T T;
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void k_final(
         const int n0 = loc.idx * TT::kCols;
         const T* trow = Tg + ((size_t)b * (gamma + 1) + (ks - 1)) * V;
         const T* lrow = L + ((size_t)b * gamma + (ks - 1)) * V;
-        const int prev = cond_token_v(x0, tok, b, gamma, ks, V);
+        const int prev = rnn ? b * gamma + ks - 1 : cond_token_v(x0, tok, b, gamma, ks, V);
         const float ld = lse_log2(lse_d[(size_t)b * gamma + ks - 1]);
         const float lt = lse_log2(lse_t[(size_t)b * gamma + ks - 1]);
         auto weight = [&](float fv, float tv) {
@@ -666,7 +668,7 @@ __global__ __launch_bounds__(64) void k_final_bf16(
     const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ len,
     const int32_t* __restrict__ accepted, const int32_t* __restrict__ resid_idx, const float2* __restrict__ rpart,
-    const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC,
+    const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rnn,
     uint64_t seed, int32_t* __restrict__ out_tok)
 {
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
@@ -685,7 +687,7 @@ __global__ __launch_bounds__(64) void k_final_bf16(
         load_slices<PER>(rpart + (size_t)m * nT, nT, make_float2(0.0f, 0.0f), q, &i0);
         uint4 af[1][8];
         {
-            const uint16_t* arow[1] = { A + (size_t)cond_token_v(x0, tok, b, gamma, ks, V) * r };
+            const uint16_t* arow[1] = { A + (size_t)(rnn ? b * gamma + ks - 1 : cond_token_v(x0, tok, b, gamma, ks, V)) * r };
             load_a_frags<1>(arow, r, af);
         }
         float sw = 0.0f;
@@ -802,8 +804,11 @@ template <class DT>
 static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, const void* Bm_, const int32_t* x0,
                            const int32_t* tok, const float* pd, const double* lse_d, const int32_t* len, int B,
                            int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok,
-                           int32_t* n_out, float* target_p, void* ws, const WsLayout& lay, hipStream_t s)
+                           int32_t* n_out, float* target_p, const void* H, void* ws, const WsLayout& lay, hipStream_t s)
 {
+    // RNN head: the operand rows are the draft's states H[b][k-1] (row b*gamma + k-1) instead of A[x].
+    const int rnn = H ? 1 : 0, nA = H ? B * gamma : V;
+    if (H) A_ = H;
     typedef typename DT::T T;
     const T* Tg = static_cast<const T*>(Tg_);
     const T* L = static_cast<const T*>(L_);
@@ -829,8 +834,8 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
                        gamma, V, nC, lse_t, ptw);
     prof_end(K_TARGET_PARTIALS, s);
     prof_begin(K_ACCEPT, s);
-    hipLaunchKernelGGL(k_accept, dim3(1), dim3(kAcceptThreads), 0, s, pd, len, ptw, x0, tok, B, gamma, seed, accepted,
-                       n_out, target_p, ridx, rlist, rcnt);
+    hipLaunchKernelGGL(k_accept, dim3(1), dim3(kAcceptThreads), 0, s, pd, len, ptw, x0, tok, B, gamma, rnn, seed,
+                       accepted, n_out, target_p, ridx, rlist, rcnt);
     prof_end(K_ACCEPT, s);
     prof_begin(K_RESID_TILES, s);
     if (std::is_same<DT, Bf16>::value) {
@@ -840,13 +845,13 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
         hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s,
                            reinterpret_cast<const uint16_t*>(Tg), reinterpret_cast<const uint16_t*>(L),
                            reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(Bm), x0, tok,
-                           lse_d, lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, S, rpart);
+                           lse_d, lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, S, nA, rpart);
     } else {
         const int nM = (B + 255) / 256;
         hipLaunchKernelGGL(k_resid_tiles_f32, dim3(nT * nM), dim3(kThreads), 0, s,
                            reinterpret_cast<const float*>(Tg), reinterpret_cast<const float*>(L),
                            reinterpret_cast<const float*>(A), reinterpret_cast<const float*>(Bm), x0, tok, lse_d,
-                           lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, rpart);
+                           lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, nA, rpart);
     }
     prof_end(K_RESID_TILES, s);
     prof_begin(K_BONUS_PARTIALS, s);
@@ -861,10 +866,10 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
         hipLaunchKernelGGL(kern, dim3(B), dim3(64), 0, s, reinterpret_cast<const uint16_t*>(Tg),
                            reinterpret_cast<const uint16_t*>(L), reinterpret_cast<const uint16_t*>(A),
                            reinterpret_cast<const uint16_t*>(Bm), x0, tok, lse_d, lse_t, len, accepted, ridx, rpart, bm,
-                           bsum, gamma, V, r, nT, nC, seed, out_tok);
+                           bsum, gamma, V, r, nT, nC, rnn, seed, out_tok);
     } else {
         hipLaunchKernelGGL(k_final<DT>, dim3(B), dim3(kThreads), 0, s, Tg, L, A, Bm, x0, tok, lse_d, lse_t, len,
-                           accepted, ridx, rpart, bm, bsum, gamma, V, r, nT, nC, seed, out_tok);
+                           accepted, ridx, rpart, bm, bsum, gamma, V, r, nT, nC, rnn, seed, out_tok);
     }
     prof_end(K_FINAL, s);
     return hipGetLastError();
@@ -873,13 +878,14 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
 hipError_t launch_verify(int dtype, const void* Tg, const void* L, const void* A, const void* Bm, const int32_t* x0,
                          const int32_t* tok, const float* pd, const double* lse_d, const int32_t* len, int B,
                          int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok,
-                         int32_t* n_out, float* target_p, void* ws, const WsLayout& lay, hipStream_t s)
+                         int32_t* n_out, float* target_p, const void* H, void* ws, const WsLayout& lay,
+                         hipStream_t s)
 {
     if (dtype == 1)
         return verify_t<Bf16>(Tg, L, A, Bm, x0, tok, pd, lse_d, len, B, gamma, V, r, seed, accepted, out_tok, n_out,
-                              target_p, ws, lay, s);
+                              target_p, H, ws, lay, s);
     return verify_t<F32>(Tg, L, A, Bm, x0, tok, pd, lse_d, len, B, gamma, V, r, seed, accepted, out_tok, n_out,
-                         target_p, ws, lay, s);
+                         target_p, H, ws, lay, s);
 }
 
 }  // namespace dspark

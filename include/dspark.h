@@ -68,6 +68,17 @@ enum {
 const char* dspark_version(void);
 
 /* Message for the last non-OK return on this thread ("" if none). */
+/*
+ * dspark_rnn_verify -- dspark_verify for a draft made by dspark_rnn_draft:
+ * the residual at a rejected position k rebuilds the draft logits from the
+ * state H[b][k-1] (f = L[b][k-1] + h_k . Bm) instead of A[x_{k-1}]; there is
+ * no x0.  Everything else as dspark_verify.
+ */
+int dspark_rnn_verify(int dtype, const void* Tgt, const void* L, const void* H, const void* Bm,
+                      const int32_t* draft_tok, const float* draft_p, const double* draft_lse,
+                      const int32_t* verify_len, int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted,
+                      int32_t* out_tok, int32_t* n_out, float* target_p, void* ws, size_t ws_bytes, void* stream);
+
 const char* dspark_last_error(void);
 
 /*
@@ -129,6 +140,26 @@ int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void
                              int gamma, int V, int r, uint64_t seed, const float* z0, const void* wc,
                              int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * dspark_rnn_draft -- the draft steps with the RNN sequential head instead of
+ * the Markov head (menfem.com note, Key Contributions: the head variant that
+ * keeps the whole in-block prefix history in a recurrent state).  Before
+ * draft step k the state
+ *     h_k = tanh(W h_{k-1} + A[x_{k-1}]),  h_0 = 0  (fp32, then rounded to dtype)
+ * is written to H[b][k-1][:], and it replaces A[x_{k-1}] in the bias:
+ *     f = L[b][k-1][:] + h_k . Bm,   x_k = inverse-CDF sample of softmax(f).
+ * Everything else (sampling, p_d, lse_d, limits, errors) as
+ * dspark_markov_draft.
+ *
+ *   Wt  [r][r] (dtype)        W transposed: Wt[j][i] multiplies h_{k-1}[j]
+ *                             into output i
+ *   H   [B][gamma][r] (dtype) out: the states, 16-byte aligned; the verifier
+ *                             needs them (dspark_rnn_verify)
+ */
+int dspark_rnn_draft(int dtype, const void* L, const void* A, const void* Bm, const void* Wt, const int32_t* x0, int B,
+                     int gamma, int V, int r, uint64_t seed, int32_t* draft_tok, float* draft_p, double* draft_lse,
+                     void* H, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dspark_schedule -- confidence-scheduled verify lengths (paperlayer.ai

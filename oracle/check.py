@@ -20,7 +20,7 @@ from typing import Iterable, List, Optional, Tuple
 
 import numpy as np
 
-from . import accept_scan, draft_row, final_token, select, survival, uniform
+from . import accept_scan, draft_row, final_token, rnn_state, select, survival, uniform
 
 FLIP_TOL = 1e-5
 P_RTOL = 1e-5       # probabilities, relative
@@ -57,13 +57,18 @@ def _sample_flip_allowed(o_tok: int, y: int, o: dict) -> bool:
     return u - o["cdf_through"] < FLIP_TOL
 
 
-def check_draft(L, A, Bm, x0, seed, tok, p, lse, rep: Report, rows: Optional[Iterable[Tuple[int, int]]] = None):
-    """L [B][g][V] f32, tok/p/lse GPU outputs [B][g].  rows: (b, k) pairs with k 1-based; default all."""
+def check_draft(L, A, Bm, x0, seed, tok, p, lse, rep: Report, rows: Optional[Iterable[Tuple[int, int]]] = None,
+                states=None):
+    """L [B][g][V] f32, tok/p/lse GPU outputs [B][g].  rows: (b, k) pairs with k 1-based; default all.
+    states [B][g][r] (RNN head): the operand of (b, k) is states[b][k-1] instead of A[x_{k-1}]."""
     B, gamma, V = L.shape
     if rows is None:
         rows = [(b, k) for b in range(B) for k in range(1, gamma + 1)]
     for b, k in rows:
-        prev = int(x0[b]) if k == 1 else int(tok[b, k - 2])
+        if states is not None:
+            A, prev = states[b], k - 1
+        else:
+            prev = int(x0[b]) if k == 1 else int(tok[b, k - 2])
         y = int(tok[b, k - 1])
         if not (0 <= y < V):
             rep.fail(f"draft b={b} k={k}: token {y} out of range")
@@ -82,6 +87,30 @@ def check_draft(L, A, Bm, x0, seed, tok, p, lse, rep: Report, rows: Optional[Ite
             rep.fail(f"draft b={b} k={k}: p_d gpu {float(p[b, k - 1]):.9g} oracle {o['p']:.9g}")
         if abs(float(lse[b, k - 1]) - o["lse"]) > LSE_ATOL:
             rep.fail(f"draft b={b} k={k}: lse gpu {float(lse[b, k - 1]):.9g} oracle {o['lse']:.9g}")
+
+
+def check_rnn_states(A, Wt, x0, tok, H_gpu, rep: Report, elem: str = "bf16",
+                     rows: Optional[Iterable[Tuple[int, int]]] = None):
+    """RNN-head states, teacher-forced: H_gpu[b][k-1] (widened to float) against
+    tanh(W H_gpu[b][k-2] + A[x_{k-1}]) (h_0 = 0) from the oracle in double.  The GPU sums in fp32 and rounds
+    each state to its element type, so the bound is half an ulp of that type (2^-8 relative for bf16, 2^-24
+    for fp32), plus the fp32 error of the sum (tanh' <= 1) and a few fp32 ulps for tanh."""
+    B, gamma, r = H_gpu.shape
+    half_ulp = 2.0 ** -8 if elem == "bf16" else 2.0 ** -24
+    if rows is None:
+        rows = [(b, k) for b in range(B) for k in range(1, gamma + 1)]
+    for b, k in rows:
+        x = int(x0[b]) if k == 1 else int(tok[b, k - 2])
+        h_prev = np.zeros(r, dtype=np.float32) if k == 1 else H_gpu[b, k - 2].astype(np.float32)
+        ref = rnn_state(Wt, h_prev, A[x])
+        pre_mag = np.abs(A[x].astype(np.float64)) + np.abs(Wt.astype(np.float64)).T @ np.abs(h_prev.astype(np.float64))
+        got = H_gpu[b, k - 1].astype(np.float64)
+        tol = half_ulp * np.abs(ref) + 2.0 ** -24 * (r + 4) * pre_mag + 2.0 ** -21
+        rep.checked += r
+        bad = np.abs(got - ref) > tol
+        if bad.any():
+            i = int(np.argmax(bad))
+            rep.fail(f"rnn state b={b} k={k} i={i}: gpu {got[i]:.9g} oracle {ref[i]:.9g} (tol {tol[i]:.3g})")
 
 
 def check_survival(z, temps, theta_gpu, rep: Report):
@@ -104,8 +133,9 @@ def check_select(theta_gpu, budget, len_gpu, rep: Report):
 
 
 def check_verify(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_out, target_p, rep: Report,
-                 requests: Optional[Iterable[int]] = None):
-    """Teacher-forced on the GPU's draft outputs, verify lengths and accepted counts."""
+                 requests: Optional[Iterable[int]] = None, states=None):
+    """Teacher-forced on the GPU's draft outputs, verify lengths and accepted counts.
+    states [B][g][r] (RNN head): residual draft rows use states[b][k-1] as the operand."""
     B, gamma, V = L.shape
     if requests is None:
         requests = range(B)
@@ -147,7 +177,11 @@ def check_verify(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_out, targe
         if not (0 <= y < V):
             rep.fail(f"verify b={b}: final token {y} out of range")
             continue
-        o = final_token(T[b], L[b], A, Bm, int(x0[b]), tok[b], l, a_g, seed, b, query=y)
+        if states is not None:  # operand rows states[b][0..g-1], addressed as "tokens" 0..g-1
+            o = final_token(T[b], L[b], states[b], Bm, 0, np.arange(1, gamma + 1, dtype=np.int32), l, a_g, seed, b,
+                            query=y)
+        else:
+            o = final_token(T[b], L[b], A, Bm, int(x0[b]), tok[b], l, a_g, seed, b, query=y)
         if o["tok"] != y:
             if _sample_flip_allowed(o["tok"], y, o):
                 rep.final_flips += 1

@@ -39,7 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_python_binding_has_the_same_names():
-    for n in ("dspark_markov_draft", "dspark_markov_draft_conf", "dspark_schedule", "dspark_schedule_objective",
+    for n in ("dspark_markov_draft", "dspark_markov_draft_conf", "dspark_rnn_draft", "dspark_rnn_verify",
+              "dspark_schedule", "dspark_schedule_objective",
               "dspark_schedule_threshold",
               "dspark_verify", "dspark_workspace_size", "dspark_version"):
         assert callable(getattr(dsp, n))
@@ -94,6 +95,30 @@ def test_draft_conf_argument_errors(lib):
     assert call(z=None) == INVALID
     assert call(dtype=5) == UNSUPPORTED
     assert call(B=0, z0=None, wc=None, z=None) == OK
+
+
+def test_rnn_argument_errors(lib):
+    fd = lib.dspark_rnn_draft
+
+    def draft(Wt=FAKE, H=FAKE, B=4, dtype=1):
+        return fd(dtype, FAKE, FAKE, FAKE, Wt, FAKE, B, 5, 1024, 16, ctypes.c_uint64(1), FAKE, FAKE, FAKE, H, FAKE,
+                  1 << 30, None)
+
+    assert draft(Wt=None) == INVALID
+    assert draft(H=None) == INVALID
+    assert draft(H=MISALIGNED) == INVALID
+    assert draft(dtype=9) == UNSUPPORTED
+    assert draft(B=0, Wt=None, H=None) == OK
+    fv = lib.dspark_rnn_verify
+
+    def verify(H=FAKE, B=4, ws_bytes=1 << 30):
+        return fv(1, FAKE, FAKE, H, FAKE, FAKE, FAKE, FAKE, FAKE, B, 5, 1024, 16, ctypes.c_uint64(1), FAKE, FAKE, FAKE,
+                  None, FAKE, ws_bytes, None)
+
+    assert verify(H=None) == INVALID
+    assert verify(H=MISALIGNED) == INVALID
+    assert verify(ws_bytes=0) == WORKSPACE
+    assert verify(B=0, H=None) == OK
 
 
 def test_schedule_argument_errors(lib):
