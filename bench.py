@@ -122,6 +122,9 @@ def main():
                     help="admission rule of the step: the budget (default, the headline), objective-based "
                          "admission against a synthetic step-time profile capped at the budget, or a static threshold")
     ap.add_argument("--tau", type=float, default=0.3, help="survival threshold for --schedule threshold")
+    ap.add_argument("--head", choices=("markov", "rnn"), default="markov",
+                    help="sequential head of the draft: the Markov head (default, the headline) or the RNN head "
+                         "(h_k = tanh(W h_{k-1} + A[x_{k-1}]), synthetic W ~ N(0, 1/r))")
     ap.add_argument("--confidence", action="store_true",
                     help="draft with the fused Markov-conditioned confidence head (z = z0 + <A[x_prev], wc>, "
                          "synthetic wc ~ N(0, 0.5^2)) and schedule on those z")
@@ -188,7 +191,16 @@ def main():
         else:
             dsp.dspark_schedule_threshold(zs, g.temps, args.tau, survival=theta, out_len=ell)
 
+    Wt = (torch.randn((r, r), generator=torch.Generator().manual_seed(wl.data_seed + 3)) / r ** 0.5).to(g.L.dtype).to(dev)
+    Hst = torch.empty((B, gamma, r), dtype=g.L.dtype, device=dev)
+
     def step(i: int, seed: int):
+        if args.head == "rnn":
+            dsp.dspark_rnn_draft(g.L, g.A, g.Bm, Wt, g.x0, seed, ws=ws, out=(tok, p, lse, Hst))
+            schedule()
+            dsp.dspark_rnn_verify(g.T, g.L, Hst, g.Bm, tok, p, lse, ell, seed, ws=ws,
+                                  out=(acc, out_tok, n_out_all[i], tp))
+            return
         if args.confidence:
             dsp.dspark_markov_draft_conf(g.L, g.A, g.Bm, g.x0, seed, g.z, wc, ws=ws, out=(tok, p, lse, zc))
         else:
@@ -290,7 +302,8 @@ def main():
                    "schedule": args.schedule + (" (step time 1 ms + 1 us/token, capped at the budget)"
                                                 if args.schedule == "objective" else
                                                 f" (tau {args.tau})" if args.schedule == "threshold" else "")
-                   + (", z from the fused Markov-conditioned confidence head" if args.confidence else ""),
+                   + (", z from the fused Markov-conditioned confidence head" if args.confidence else "")
+                   + (", RNN sequential head" if args.head == "rnn" else ""),
                    "emitted_per_step": round(emitted / K, 2), "verified_per_step": int(ell.sum().item()),
                    "accumulation": "fp32 MFMA, fp64 softmax masses"},
         "roofline": {"kernel": "draft Markov tiles (k_draft_tiles)", "bound": "hbm",
@@ -310,7 +323,7 @@ def main():
     }
     if graph:
         result["graph_replay"] = graph
-    if not args.no_cpu_baseline and args.schedule == "budget" and not args.confidence:
+    if not args.no_cpu_baseline and args.schedule == "budget" and not args.confidence and args.head == "markov":
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, wl, base_seed, min(args.cpu_requests, B))
     print(json.dumps(result), flush=True)

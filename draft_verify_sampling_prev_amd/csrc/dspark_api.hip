@@ -195,7 +195,7 @@ int dspark_rnn_draft(int dtype, const void* L, const void* A, const void* Bm, co
 {
     g_err[0] = 0;
     if (B > 0 && (!Wt || !H)) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
-    if (B > 0 && !aligned16(H)) return fail(DSPARK_ERR_INVALID_ARG, "H must be 16-byte aligned");
+    if (B > 0 && (!aligned16(H) || !aligned16(Wt))) return fail(DSPARK_ERR_INVALID_ARG, "H and Wt must be 16-byte aligned");
     return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, seed, nullptr, nullptr, draft_tok, draft_p,
                              draft_lse, nullptr, Wt, H, ws, ws_bytes, stream);
 }

@@ -547,9 +547,10 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
 // stored as row (b, k-1) of H in the element type; it replaces A[x_{k-1}] as
 // the operand of the rank-r bias.  Wt is W transposed (Wt[j][i] multiplies
 // h_{k-1}[j] into output i), so for a fixed j the lanes read consecutive
-// outputs.  One 64-thread workgroup per request; lane l owns outputs
-// l + 64q; the pre-activation starts from A[x][i] and adds the products in j
-// order (fp32 FMA), then fp32 tanh and a round to the element type.
+// outputs with 16-byte loads.  One workgroup of r threads per request: the
+// products are summed in fp32 over kPer slices of j (thread (g, slice)
+// covers kPer consecutive outputs), the slices added in order to A[x][i],
+// then fp32 tanh and a round to the element type.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
@@ -562,36 +563,49 @@ __device__ __forceinline__ uint16_t store_elem(Bf16, float f) { return f32_to_bf
 __device__ __forceinline__ float store_elem(F32, float f) { return f; }
 
 template <class DT>
-__global__ __launch_bounds__(64) void k_rnn_state(const typename DT::T* __restrict__ A,
-                                                  const typename DT::T* __restrict__ Wt,
-                                                  const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
-                                                  typename DT::T* H, int B, int gamma, int V, int r, int k)
+__global__ __launch_bounds__(kMaxRank) void k_rnn_state(const typename DT::T* __restrict__ A,
+                                                        const typename DT::T* __restrict__ Wt,
+                                                        const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
+                                                        typename DT::T* H, int B, int gamma, int V, int r, int k)
 {
+    typedef typename DT::T T;
+    constexpr int kPer = 16 / sizeof(T);  // outputs per 16-byte load of a row of Wt
     __shared__ float hp[kMaxRank];
-    const int b = blockIdx.x, lane = threadIdx.x;
+    __shared__ float part[kPer][kMaxRank];
+    const int b = blockIdx.x, t = threadIdx.x;
     const int x = cond_token(x0, tok, b, gamma, k, V);
-    const typename DT::T* arow = A + (size_t)x * r;
-    typename DT::T* hout = H + ((size_t)b * gamma + (k - 1)) * r;
-    if (k >= 2) {
-        const typename DT::T* hprev = H + ((size_t)b * gamma + (k - 2)) * r;
-        for (int j = lane; j < r; j += 64) hp[j] = DT::to_f32(hprev[j]);
-    }
+    const T* arow = A + (size_t)x * r;
+    T* hout = H + ((size_t)b * gamma + (k - 1)) * r;
+    if (k >= 2 && t < r) hp[t] = DT::to_f32(H[((size_t)b * gamma + (k - 2)) * r + t]);
     __syncthreads();
-    float s[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s[q] = 64 * q + lane < r ? DT::to_f32(arow[64 * q + lane]) : 0.0f;
     if (k >= 2) {
-        for (int j = 0; j < r; ++j) {
-            const float h = hp[j];
-            const typename DT::T* wrow = Wt + (size_t)j * r;
+        // Thread t: outputs kPer*g .. +kPer-1 (g = t mod r/kPer) over the
+        // slice jj = t / (r/kPer) of j, one 16-byte load of Wt per j.
+        const int ng = r / kPer, g = t % ng, jj = t / ng, per = r / kPer;
+        float s[kPer];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (64 * q + lane < r) s[q] = __builtin_fmaf(DT::to_f32(wrow[64 * q + lane]), h, s[q]);
+        for (int e = 0; e < kPer; ++e) s[e] = 0.0f;
+        if (t < r) {
+#pragma unroll 8
+            for (int j = jj * per; j < (jj + 1) * per; ++j) {
+                const uint4 w = ld16(Wt + (size_t)j * r + kPer * g);
+                const float h = hp[j];
+#pragma unroll
+                for (int e = 0; e < kPer; ++e) s[e] = __builtin_fmaf(DT::get(w, e), h, s[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) part[jj][kPer * g + e] = s[e];
         }
+        __syncthreads();
     }
+    if (t < r) {
+        float pre = DT::to_f32(arow[t]);
+        if (k >= 2) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (64 * q + lane < r) hout[64 * q + lane] = store_elem(DT{}, tanhf(s[q]));
+            for (int q = 0; q < kPer; ++q) pre += part[q][t];
+        }
+        hout[t] = store_elem(DT{}, tanhf(pre));
+    }
 }
 
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
@@ -602,10 +616,10 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     const ConfOut co{ z0, wc, z_out };
     if (H) {  // RNN head: this step's operand rows
         if (dtype == 1)
-            hipLaunchKernelGGL(k_rnn_state<Bf16>, dim3(B), dim3(64), 0, s, static_cast<const uint16_t*>(A),
+            hipLaunchKernelGGL(k_rnn_state<Bf16>, dim3(B), dim3(kMaxRank), 0, s, static_cast<const uint16_t*>(A),
                                static_cast<const uint16_t*>(Wt), x0, tok, static_cast<uint16_t*>(H), B, gamma, V, r, k);
         else
-            hipLaunchKernelGGL(k_rnn_state<F32>, dim3(B), dim3(64), 0, s, static_cast<const float*>(A),
+            hipLaunchKernelGGL(k_rnn_state<F32>, dim3(B), dim3(kMaxRank), 0, s, static_cast<const float*>(A),
                                static_cast<const float*>(Wt), x0, tok, static_cast<float*>(H), B, gamma, V, r, k);
     }
     float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.draft_part);

@@ -153,7 +153,7 @@ int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void
  * dspark_markov_draft.
  *
  *   Wt  [r][r] (dtype)        W transposed: Wt[j][i] multiplies h_{k-1}[j]
- *                             into output i
+ *                             into output i; 16-byte aligned
  *   H   [B][gamma][r] (dtype) out: the states, 16-byte aligned; the verifier
  *                             needs them (dspark_rnn_verify)
  */

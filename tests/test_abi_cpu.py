@@ -107,6 +107,7 @@ def test_rnn_argument_errors(lib):
     assert draft(Wt=None) == INVALID
     assert draft(H=None) == INVALID
     assert draft(H=MISALIGNED) == INVALID
+    assert draft(Wt=MISALIGNED) == INVALID
     assert draft(dtype=9) == UNSUPPORTED
     assert draft(B=0, Wt=None, H=None) == OK
     fv = lib.dspark_rnn_verify
