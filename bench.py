@@ -133,7 +133,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU (request-sharded) path "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the multi-GPU (request-sharded) path "
                                    "is a design, not an implementation", "n_gpus": args.gpus}))
         sys.exit(2)
 
