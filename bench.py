@@ -55,16 +55,20 @@ def draft_tiles_bytes_flops(wl) -> tuple:
     return byts, flops
 
 
+# The draft tile kernel's translation unit: the source and every header it includes.
+DRAFT_TILE_SOURCES = ("dspark_device.hpp", "dspark_draft.hip", "dspark_internal.hpp", "dspark_locate.hpp",
+                      "dspark_markov.hpp", "dspark_tile.hpp")
+
+
 def kernel_source_digest() -> str:
-    """SHA-256 over the HIP sources and headers of the library (file names and contents, sorted)."""
+    """SHA-256 over the sources the draft tile kernel is compiled from (file names and contents, in order)."""
     import hashlib
     d = os.path.join(ROOT, "draft_verify_sampling_prev_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(name.encode())
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(f.read())
+    for name in DRAFT_TILE_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 

@@ -13,9 +13,10 @@
 // device, so the sequence can be captured in a HIP graph):
 //   k_row_partials (target)  grid = chunks x (B*gamma): row (b,k) with
 //                            k <= ell_b -> chunk max and sum of exp (fp64).
-//   k_target_lse             one wave per row: lse_t and p_t(x_k).
-//   k_accept                 one workgroup: accept draws per request; compacts
-//                            the requests with a rejection.
+//   k_lse_accept             one wave per request: lse_t and p_t(x_k) of its
+//                            verified rows, accept draws, first rejection;
+//                            appends the requests with a rejection to the
+//                            residual list.
 //   k_resid_tiles            Markov MFMA tiles of the rejected draft rows
 //                            fused with the target row: per tile sums of
 //                            max(0, p_t - p_d) and of p_t.
@@ -74,11 +75,13 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T*
                                                            const int32_t* __restrict__ len,
                                                            const int32_t* __restrict__ accepted, int B, int gamma,
                                                            int V, int nC, int bonus, float* __restrict__ om,
-                                                           double* __restrict__ os)
+                                                           double* __restrict__ os, int32_t* __restrict__ clear_count)
 {
     __shared__ BlockScratch bs;
     const int c = blockIdx.x;
     const int row = blockIdx.y;
+    // The residual-list counter of the accept kernel, which runs next on the stream.
+    if (clear_count && c == 0 && row == 0 && threadIdx.x == 0) *clear_count = 0;
     int b, trow;
     if (!bonus) {
         b = row / gamma;
@@ -131,115 +134,119 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T*
 }
 
 // ---------------------------------------------------------------------------
-// Target log-normaliser and p_t(x_k) of every verified row: one wave per row.
+// Target log-normalisers, p_t(x_k) and the accept scan: one wave per request.
+//
+// Lane c holds chunk c's (max, sum of exp) partials of every verified row
+// (all loads issued before the first reduction); per row the wave reduces
+// them to the log-normaliser, lane kk keeps row kk's, loads T[b][kk][x_kk]
+// and draws its accept uniform, and a ballot gives the first rejection.  A
+// request with a rejection takes the next slot of the residual list with an
+// atomic add on the counter that the target row pass cleared: the list is
+// compact but in no fixed order, and nothing downstream depends on the order
+// (every row's residual tile results depend only on the row).
 // ---------------------------------------------------------------------------
+constexpr int kAcceptWaves = 4;
+
 template <class DT>
-__global__ __launch_bounds__(kThreads) void k_target_lse(const typename DT::T* __restrict__ Tg,
-                                                         const int32_t* __restrict__ tok,
-                                                         const int32_t* __restrict__ len,
-                                                         const float* __restrict__ tgm,
-                                                         const double* __restrict__ tgs, int B, int gamma, int V,
-                                                         int nC, double* __restrict__ lse_t, double* __restrict__ pt)
+__global__ __launch_bounds__(64 * kAcceptWaves) void k_lse_accept(
+    const typename DT::T* __restrict__ Tg, const float* __restrict__ pd, const int32_t* __restrict__ len,
+    const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const float* __restrict__ tgm,
+    const double* __restrict__ tgs, int B, int gamma, int V, int nC, int rnn, uint64_t seed,
+    int32_t* __restrict__ accepted, int32_t* __restrict__ n_out, float* __restrict__ target_p,
+    double* __restrict__ lse_t, int32_t* __restrict__ resid_idx, int4* __restrict__ resid_list,
+    int32_t* __restrict__ resid_count)
 {
-    const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int b = blockIdx.x * kAcceptWaves + (int)(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (row >= B * gamma) return;
-    const int b = row / gamma, kk = row - b * gamma;
-    if (kk >= clamp_len(len[b], gamma)) return;
-    const float* m = tgm + (size_t)row * nC;
-    const double* s = tgs + (size_t)row * nC;
-    float M = -INFINITY;
-    for (int c = lane; c < nC; c += 64) M = fmaxf(M, m[c]);
-    M = wave_max(M);
-    double S = 0.0;
-    for (int c = lane; c < nC; c += 64) S += tile_mass(m[c], s[c], M);
-    S = wave_sum(S);
-    if (lane == 0) {
-        const double lse = (double)M + log(S);
-        lse_t[row] = lse;
-        const int x = clamp_tok(tok[row], V);
-        const double tx = (double)DT::to_f32(Tg[((size_t)b * (gamma + 1) + kk) * V + x]);
-        pt[row] = exp(tx - lse);
+    if (b >= B) return;
+    const size_t row0 = (size_t)b * gamma;
+    // Every load of rows k < gamma is issued before the length arrives (all
+    // in bounds; rows past ell_b are loaded and ignored), so the chain is
+    // {length, partials, p_d, tokens} -> T[x_k] -> residual slot.
+    float pdk = 1.0f;
+    int xk = 0;
+    if (lane < gamma) {
+        pdk = pd[row0 + lane];
+        xk = clamp_tok(tok[row0 + lane], V);
     }
-}
-
-// ---------------------------------------------------------------------------
-// Accept scan: one workgroup of 1024 threads, one request per thread.
-// ---------------------------------------------------------------------------
-constexpr int kAcceptThreads = 1024;
-
-__global__ __launch_bounds__(kAcceptThreads) void k_accept(const float* __restrict__ pd, const int32_t* __restrict__ len,
-                                                           const double* __restrict__ pt,
-                                                           const int32_t* __restrict__ x0,
-                                                           const int32_t* __restrict__ tok, int B, int gamma, int rnn,
-                                                           uint64_t seed, int32_t* __restrict__ accepted,
-                                                           int32_t* __restrict__ n_out, float* __restrict__ target_p,
-                                                           int32_t* __restrict__ resid_idx,
-                                                           int4* __restrict__ resid_list,
-                                                           int32_t* __restrict__ resid_count)
-{
-    __shared__ int wsum[kAcceptThreads / 64];
-    __shared__ int base;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    if (t == 0) base = 0;
-    __syncthreads();
-    for (int b0 = 0; b0 < B; b0 += kAcceptThreads) {
-        const int b = b0 + t;
-        int rej = 0, accepted_b = 0;
-        if (b < B) {
-            const int l = clamp_len(len[b], gamma);
-            int a = l;
-            for (int kk = 0; kk < gamma; ++kk) {
-                const size_t row = (size_t)b * gamma + kk;
-                if (kk < l) {
-                    const double ptk = pt[row];
-                    const double ratio = ptk / (double)pd[row];
-                    const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)(kk + 1), 1u);
-                    if (a == l && !(u < (float)ratio)) a = kk;
-                    if (target_p) target_p[row] = (float)ptk;
-                } else if (target_p) {
-                    target_p[row] = 0.0f;
+    const int l = clamp_len(len[b], gamma);
+    // Row kk's log-normaliser: M = max of the chunk maxima, S = sum over
+    // chunks of s_c exp(m_c - M), lse = M + ln S.  Lane kk keeps (M, S) of row kk.
+    float Mk = 0.0f;
+    double Sk = 1.0;
+    if (nC <= 64) {
+        float mv[kMaxGamma];
+        double sv[kMaxGamma];
+#pragma unroll
+        for (int kk = 0; kk < kMaxGamma; ++kk) {
+            mv[kk] = -INFINITY;
+            sv[kk] = 0.0;
+            if (kk < gamma && lane < nC) {
+                mv[kk] = tgm[(row0 + kk) * nC + lane];
+                sv[kk] = tgs[(row0 + kk) * nC + lane];
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < kMaxGamma; ++kk) {
+            if (kk < l) {
+                const float M = wave_max(mv[kk]);
+                const double S = wave_sum(tile_mass(mv[kk], sv[kk], M));
+                if (lane == kk) {
+                    Mk = M;
+                    Sk = S;
                 }
             }
-            accepted[b] = a;
-            accepted_b = a;
-            n_out[b] = a + 1;
-            rej = a < l;
         }
-        int inc = rej;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int n = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += n;
-        }
-        __syncthreads();
-        if (lane == 63) wsum[w] = inc;
-        __syncthreads();
-        int off = base, tot = 0;
-        for (int i = 0; i < kAcceptThreads / 64; ++i) {
-            if (i < w) off += wsum[i];
-            tot += wsum[i];
-        }
-        const int idx = off + inc - rej;
-        if (b < B) {
-            resid_idx[b] = rej ? idx : -1;
-            if (rej) {
-                const int ks = accepted_b + 1;
-                // operand row of the rejected position's draft logits: A[x_{ks-1}],
-                // or with the RNN head the state row (b, ks-1)
-                const int xprev = rnn ? b * gamma + ks - 1 : ks == 1 ? x0[b] : tok[(size_t)b * gamma + ks - 2];
-                resid_list[idx] = make_int4(b, ks, xprev, 0);
+    } else {
+        for (int kk = 0; kk < l; ++kk) {
+            const float* m = tgm + (row0 + kk) * nC;
+            const double* s = tgs + (row0 + kk) * nC;
+            float M = -INFINITY;
+            for (int c = lane; c < nC; c += 64) M = fmaxf(M, m[c]);
+            M = wave_max(M);
+            double S = 0.0;
+            for (int c = lane; c < nC; c += 64) S += tile_mass(m[c], s[c], M);
+            S = wave_sum(S);
+            if (lane == kk) {
+                Mk = M;
+                Sk = S;
             }
         }
-        __syncthreads();
-        if (t == 0) base += tot;
-        __syncthreads();
     }
-    if (t == 0) *resid_count = base;
+    bool reject = false;
+    if (lane < l) {
+        const double lse = (double)Mk + log(Sk);
+        lse_t[row0 + lane] = lse;
+        const double tx = (double)DT::to_f32(Tg[((size_t)b * (gamma + 1) + lane) * V + xk]);
+        const double ptk = exp(tx - lse);
+        const double ratio = ptk / (double)pdk;
+        const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)(lane + 1), 1u);
+        reject = !(u < (float)ratio);
+        if (target_p) target_p[row0 + lane] = (float)ptk;
+    } else if (target_p && lane < gamma) {
+        target_p[row0 + lane] = 0.0f;
+    }
+    const uint64_t rej = __ballot(reject);
+    const int a = rej ? __builtin_ctzll(rej) : l;
+    if (lane == 0) {
+        accepted[b] = a;
+        n_out[b] = a + 1;
+        if (a < l) {
+            const int ks = a + 1;
+            // operand row of the rejected position's draft logits: A[x_{ks-1}],
+            // or with the RNN head the state row (b, ks-1)
+            const int xprev = rnn ? b * gamma + ks - 1 : ks == 1 ? x0[b] : tok[row0 + ks - 2];
+            const int idx = atomicAdd(resid_count, 1);
+            resid_idx[b] = idx;
+            resid_list[idx] = make_int4(b, ks, xprev, 0);
+        } else {
+            resid_idx[b] = -1;
+        }
+    }
 }
 
 // Row m of the compacted residual list: request b at its first rejected
-// position ks, conditioned on token x (x_{ks-1}), as written by k_accept.
+// position ks, conditioned on token x (x_{ks-1}), as written by k_lse_accept.
 // Every field is clamped into range, so a row read past the count (stale
 // workspace) still addresses valid memory; such rows are never reported.
 struct ResidRow {
@@ -818,7 +825,6 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     float* tgm = reinterpret_cast<float*>(w + lay.tgt_m);
     double* tgs = reinterpret_cast<double*>(w + lay.tgt_s);
     double* lse_t = reinterpret_cast<double*>(w + lay.lse_t);
-    double* ptw = reinterpret_cast<double*>(w + lay.pt);
     int32_t* ridx = reinterpret_cast<int32_t*>(w + lay.resid_idx);
     int4* rlist = reinterpret_cast<int4*>(w + lay.resid_list);
     int32_t* rcnt = reinterpret_cast<int32_t*>(w + lay.resid_count);
@@ -829,13 +835,12 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
 
     prof_begin(K_TARGET_PARTIALS, s);
     hipLaunchKernelGGL(k_row_partials<DT>, dim3(nC, B * gamma), dim3(kThreads), 0, s, Tg, len, accepted, B, gamma, V,
-                       nC, 0, tgm, tgs);
-    hipLaunchKernelGGL(k_target_lse<DT>, dim3((B * gamma + 3) / 4), dim3(kThreads), 0, s, Tg, tok, len, tgm, tgs, B,
-                       gamma, V, nC, lse_t, ptw);
+                       nC, 0, tgm, tgs, rcnt);
     prof_end(K_TARGET_PARTIALS, s);
     prof_begin(K_ACCEPT, s);
-    hipLaunchKernelGGL(k_accept, dim3(1), dim3(kAcceptThreads), 0, s, pd, len, ptw, x0, tok, B, gamma, rnn, seed,
-                       accepted, n_out, target_p, ridx, rlist, rcnt);
+    hipLaunchKernelGGL(k_lse_accept<DT>, dim3((B + kAcceptWaves - 1) / kAcceptWaves), dim3(64 * kAcceptWaves), 0, s,
+                       Tg, pd, len, x0, tok, tgm, tgs, B, gamma, V, nC, rnn, seed, accepted, n_out, target_p, lse_t,
+                       ridx, rlist, rcnt);
     prof_end(K_ACCEPT, s);
     prof_begin(K_RESID_TILES, s);
     if (std::is_same<DT, Bf16>::value) {
@@ -856,7 +861,7 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     prof_end(K_RESID_TILES, s);
     prof_begin(K_BONUS_PARTIALS, s);
     hipLaunchKernelGGL(k_row_partials<DT>, dim3(nC, B), dim3(kThreads), 0, s, Tg, len, accepted, B, gamma, V, nC, 1,
-                       bm, bsum);
+                       bm, bsum, (int32_t*)nullptr);
     prof_end(K_BONUS_PARTIALS, s);
     prof_begin(K_FINAL, s);
     if (std::is_same<DT, Bf16>::value && nT <= 64 * 64 && nC <= 64 * 4) {
