@@ -75,6 +75,14 @@ def test_many_vocab_chunks_and_row_blocks():
     _run_and_check(wl, draft_rows=rows, requests=range(0, 600, 7))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_long_vocabulary_generic_paths(dtype):
+    # V = 600000: 74 target chunks (> 64, the accept kernel's per-lane chunk loop)
+    # and 9375 bf16 tiles (> 64 * 64, the workgroup locate and final kernels).
+    wl = synth.tiny(B=3, gamma=2, V=600000, r=16, budget=4, dtype=dtype)
+    _run_and_check(wl)
+
+
 def test_zero_markov_factors_reduce_to_plain_softmax():
     wl = synth.tiny(B=8, gamma=3, V=4096, r=32, budget=12, dtype="bf16")
     inp = synth.make_inputs(wl)
