@@ -60,6 +60,46 @@ DRAFT_TILE_SOURCES = ("dspark_device.hpp", "dspark_draft.hip", "dspark_internal.
                       "dspark_markov.hpp", "dspark_tile.hpp")
 
 
+def vocab_passes(wl, kern: dict, adm: float, rej: float) -> dict:
+    """HBM fraction of the vocabulary passes and MFMA fraction of the rank-r contraction, per step.
+
+    Algorithmic bytes (the method's minimum, s bytes per element): draft tiles, per launch the step's L rows,
+    Bm, the A rows, the partials and tokens; target rows, s*V per verified draft (adm per step); residual tiles,
+    Bm plus the target row and the draft-L row of each request with a rejection (rej per step); bonus rows,
+    s*V per request without one.  Flops: 2*r*V per draft row and per residual row.  Times are the per-kernel
+    averages of the event-bracketed pass (each includes its dispatch gap)."""
+    s = 2 if wl.dtype == "bf16" else 4
+    B, V, r, gamma = wl.B, wl.V, wl.r, wl.gamma
+    tile_b, _ = draft_tiles_bytes_flops(wl)
+    per_launch = {"draft_tiles": tile_b, "target_partials": s * V * adm,
+                  "resid_tiles": s * (r * V + 2 * rej * V), "bonus_partials": s * V * (B - rej)}
+    out = {}
+    tot_b = tot_us = 0.0
+    for name, byts in per_launch.items():
+        if name not in kern:
+            continue
+        us, n = kern[name]["avg_us"], kern[name]["launches_per_step"]
+        gbs = byts / (us * 1e-6) / 1e9
+        out[name] = {"bytes_per_launch": int(byts), "avg_us": us, "launches_per_step": n, "GB/s": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        tot_b += byts * n
+        tot_us += us * n
+    if tot_us > 0:
+        gbs = tot_b / (tot_us * 1e-6) / 1e9
+        out["all"] = {"bytes_per_step": int(tot_b), "us_per_step": round(tot_us, 2), "GB/s": round(gbs, 1),
+                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if "draft_tiles" in kern and "resid_tiles" in kern:
+        flops = 2.0 * r * V * (gamma * B + rej)
+        us = kern["draft_tiles"]["avg_us"] * kern["draft_tiles"]["launches_per_step"] + kern["resid_tiles"]["avg_us"]
+        tf = flops / (us * 1e-6) / 1e12
+        peak = BF16_MFMA_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+        out["markov_mfma"] = {"flops_per_step": flops, "us_per_step": round(us, 2), "TFLOP/s": round(tf, 1),
+                              "frac": round(tf / peak, 4)}
+    out["verified_per_step"] = adm
+    out["rejections_per_step"] = rej
+    return out
+
+
 def kernel_source_digest() -> str:
     """SHA-256 over the sources the draft tile kernel is compiled from (file names and contents, in order)."""
     import hashlib
@@ -252,15 +292,20 @@ def main():
 
     # Per-kernel averages (separate pass, all kernels bracketed) for context.
     kern = {}
+    n_adm = torch.zeros((), dtype=torch.int64, device=dev)  # verified drafts over the 10 steps
+    n_rej = torch.zeros((), dtype=torch.int64, device=dev)  # requests with a rejection over the 10 steps
     binding.profile_start(max_launches=10 * (2 * gamma + 6) + 16)
     for i in range(10):
         step(K + args.warmup, base_seed + 5000 + i)
+        n_adm += ell.sum()
+        n_rej += (acc < ell).sum()
     torch.cuda.synchronize()
     binding.profile_stop()
     for name in binding.KERNELS:
         t, n = binding.profile_query(name)
         if n:
             kern[name] = {"avg_us": round(1000.0 * t / n, 2), "launches_per_step": n // 10}
+    vocab = vocab_passes(wl, kern, n_adm.item() / 10.0, n_rej.item() / 10.0)
 
     graph = None
     if args.graph:
@@ -323,6 +368,7 @@ def main():
                      "mfma_frac": round(flops / avg_s / 1e12 / (BF16_MFMA_PEAK_TFLOPS if wl.dtype == "bf16"
                                                                else FP32_MFMA_PEAK_TFLOPS), 4)},
         "kernels": kern,
+        "vocab_passes": vocab,
         "wall_s_timed": round(t_wall, 3),
     }
     if graph:
