@@ -169,7 +169,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     int t0, ts, cnt;
     slot_tiles(slot, S, nT, &t0, &ts, &cnt);
     if (cnt <= 0) return;  // uniform
-    const int w = wave_id(), lane = threadIdx.x & 63, G = lane >> 4, c = lane & 15;
+    const int w = wave_id(), lane = threadIdx.x & 63, c = lane & 15;
     const int m0 = mblk * R;
     const int mw = m0 + 32 * w;  // first row of this wave
     const bool active = mw < B;

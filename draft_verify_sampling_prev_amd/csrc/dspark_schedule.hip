@@ -209,7 +209,6 @@ __device__ __forceinline__ float key_to_float(uint32_t key)
 }
 
 constexpr double kThetaUnit = 68719476736.0;  // 2^36
-constexpr int kObjPerThread = kMaxCandidates / kSchedThreads;
 
 // Bitonic sort of P keys held in registers: thread t keeps E = P / 1024 keys
 // (at least one; threads past P / E hold none) at indices
