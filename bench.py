@@ -369,6 +369,7 @@ def main():
                                                                else FP32_MFMA_PEAK_TFLOPS), 4)},
         "kernels": kern,
         "vocab_passes": vocab,
+        "verify_len_histogram": torch.bincount(ell.long().cpu(), minlength=gamma + 1).tolist(),
         "wall_s_timed": round(t_wall, 3),
     }
     if graph:

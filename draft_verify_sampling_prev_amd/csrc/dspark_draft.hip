@@ -185,7 +185,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) load_row16(lrow[bb], (t0 + i * ts) * kTcols, V, dummy, lv[bb]);
     };
-    auto dma = [&](int i, char* buf) { dma_bm_tile<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf); };
+    const BmDmaLanes<NW> dml = bm_dma_lanes<NW>(V, r);
+    auto dma = [&](int i, char* buf) { dma_bm_tile_pre<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf, dml); };
 
     floatx4 fprev[4][2];
     int prev = -1;  // local index of the tile held in fprev

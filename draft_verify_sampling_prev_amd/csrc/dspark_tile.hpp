@@ -103,6 +103,54 @@ __device__ __forceinline__ void dma_bm_tile(const uint16_t* __restrict__ Bm, int
     }
 }
 
+// dma_bm_tile for a pipeline that stages many tiles: the lane-dependent
+// part of every DMA offset is computed once (BmDmaLanes) and a tile adds only
+// its column clamp.  With c the lane's 16-byte chunk and k, kb its row and the
+// wave-uniform base row of block blk,
+//   voff = ((k - kb) V + min(n0 + 8c, V - 8) - n0) * 2
+//        = 2 (k - kb) V + 2 min(8c, V - 8 - n0),
+// the same addresses as dma_bm_tile.
+template <int NW>
+struct BmDmaLanes {
+    uint32_t kv[32 / NW];  // 2 (k - kb) V
+    int c8[32 / NW];       // 8c
+    long long kbv[32 / NW];  // kb V, wave-uniform
+};
+template <int NW>
+__device__ __forceinline__ BmDmaLanes<NW> bm_dma_lanes(int V, int r)
+{
+    BmDmaLanes<NW> d;
+    const int w = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < 32 / NW; ++t) {
+        const int blk = w + NW * t;
+        const int kb = min(8 * blk, r - 1);
+        const int k = min(8 * blk + (lane >> 3), r - 1);
+        d.kv[t] = (uint32_t)((k - kb) * V * 2);
+        d.kbv[t] = (long long)kb * V;
+        d.c8[t] = 8 * ((lane & 7) ^ swz_k(8 * blk + (lane >> 3)));
+    }
+    return d;
+}
+template <int NW>
+__device__ __forceinline__ void dma_bm_tile_pre(const uint16_t* __restrict__ Bm, int V, int r, int n0, bool dummy,
+                                                char* buf, const BmDmaLanes<NW>& d)
+{
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    dummy = __builtin_amdgcn_readfirstlane((int)dummy) != 0;
+    const int w = wave_id();
+    const int lim = V - 8 - n0;
+#pragma unroll
+    for (int t = 0; t < 32 / NW; ++t) {
+        const int blk = w + NW * t;
+        // Row kb of the block (wave-uniform), or Bm itself for a dummy: a
+        // select, not a branch.
+        const uint16_t* base = Bm + (dummy ? 0ll : d.kbv[t] + n0);
+        const uint32_t voff = dummy ? 0u : d.kv[t] + 2u * (uint32_t)min(d.c8[t], lim);
+        dma16(base, voff, buf + blk * 1024);
+    }
+}
+
 __device__ __forceinline__ v4s tr_read(const char* buf, int off)
 {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off));

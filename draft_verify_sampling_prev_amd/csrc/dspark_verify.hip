@@ -396,7 +396,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
             load_row16(trow[bb], (t0 + i * ts) * kTcols, V, dummy, tv[bb]);
         }
     };
-    auto dma = [&](int i, char* buf) { dma_bm_tile<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf); };
+    const BmDmaLanes<NW> dml = bm_dma_lanes<NW>(V, r);
+    auto dma = [&](int i, char* buf) { dma_bm_tile_pre<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf, dml); };
 
     // Row sums of tile i from its logits f (accumulators) and target values,
     // for the first NBB batch blocks.  Every lane of a row ends with the same
