@@ -370,6 +370,9 @@ def main():
         "kernels": kern,
         "vocab_passes": vocab,
         "verify_len_histogram": torch.bincount(ell.long().cpu(), minlength=gamma + 1).tolist(),
+        "secondary": {"drafted_tokens_per_s": round(B * gamma / (ms_step / 1000.0), 1),
+                      "verified_tokens_per_s": round(vocab["verified_per_step"] / (ms_step / 1000.0), 1),
+                      "mean_emitted_per_request": round(emitted / K / B, 4)},
         "wall_s_timed": round(t_wall, 3),
     }
     if graph:
