@@ -80,7 +80,6 @@ template <int NB>
 __device__ __forceinline__ int scan_tile_weights(const double (&w)[NB], double scale, double cprev, double tau,
                                                  double* w_sel)
 {
-    const int lane = threadIdx.x & 63;
     double carry = 0.0;
     int jhit = -1, jlast = -1;
     double whit = 0.0, wlast = 0.0;
