@@ -632,7 +632,7 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     const bool ag_path = wave_locate && r == kAgRank && !H;  // (RNN head: the next operand is the state, not A[x])
     // bf16 tile grid: nM row blocks x S persistent slots.
     const int nM = (B + kTileRows - 1) / kTileRows;
-    const int S = std::min(nT, std::max((cu_count() + nM - 1) / nM, (nT + kPartTiles - 1) / kPartTiles));
+    const int S = tile_slots(nT, nM, cu_count(), kPartTiles);
     prof_begin(K_DRAFT_TILES, s);
     if (dtype == 1) {
         auto kern = (r + 31) / 32 == 8 ? k_draft_tiles_bf16<8> : k_draft_tiles_bf16<0>;

@@ -50,6 +50,19 @@ enum KernelId {
     K_FINAL,
     K_COUNT
 };
+// Persistent slots per row block of a tile pass over nT tiles with nM row
+// blocks (one workgroup per compute unit at a time): the fewest slots that
+// keep every slot within max_tiles tiles (its partial staging) and make the
+// grid S * nM a whole number of rounds over the compute units, so that no
+// round runs on a fraction of the chip.
+inline int tile_slots(int nT, int nM, int cus, int max_tiles)
+{
+    const int per_round = cus / nM > 0 ? cus / nM : 1;
+    const int need = (nT + max_tiles - 1) / max_tiles;
+    const int rounds = (need + per_round - 1) / per_round;
+    return nT < per_round * rounds ? nT : per_round * rounds;
+}
+
 // Compute units of the current device (cached per device).
 int cu_count();
 

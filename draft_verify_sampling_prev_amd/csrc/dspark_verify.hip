@@ -846,7 +846,7 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     prof_begin(K_RESID_TILES, s);
     if (std::is_same<DT, Bf16>::value) {
         const int nM = (B + kTileRows - 1) / kTileRows;
-        const int S = std::min(nT, std::max((cu_count() + nM - 1) / nM, (nT + kResPartTiles - 1) / kResPartTiles));
+        const int S = tile_slots(nT, nM, cu_count(), kResPartTiles);
         auto kern = (r + 31) / 32 == 8 ? k_resid_tiles_bf16<8> : k_resid_tiles_bf16<0>;
         hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s,
                            reinterpret_cast<const uint16_t*>(Tg), reinterpret_cast<const uint16_t*>(L),
