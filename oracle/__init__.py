@@ -19,7 +19,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dspark_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# DSPARK_ORACLE_LIB selects another build of the same source (the sanitizer
+# build of the CPU tests); it is then loaded as given, never rebuilt.
+_LIB_OVERRIDE = os.environ.get("DSPARK_ORACLE_LIB")
+_LIB = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 
 ORC_OK = 0
 
@@ -40,16 +43,19 @@ class RowOut(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
-def build() -> str:
-    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
-    tmp = _LIB + ".tmp"
-    cmd = [
-        "gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-        "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm",
-    ]
+GCC_FLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra",
+             "-pthread"]
+
+
+def build(out: str = None, extra=()) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction) into `out`
+    (default: the in-tree liboracle.so); `extra` adds flags (e.g. sanitizers)."""
+    out = out or os.path.join(_HERE, "liboracle.so")
+    tmp = out + ".tmp"
+    cmd = ["gcc", *GCC_FLAGS, *extra, _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -58,7 +64,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _LIB_OVERRIDE and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
         _lib = ctypes.CDLL(_LIB)
         _declare(_lib)
@@ -112,6 +118,10 @@ def _declare(L):
     L.orc_verify.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                              ctypes.c_int, ctypes.c_uint64, _P, _P, _P, _P]
     L.orc_verify.restype = ctypes.c_int
+    L.orc_markov_draft_mt.argtypes = L.orc_markov_draft.argtypes + [ctypes.c_int]
+    L.orc_markov_draft_mt.restype = ctypes.c_int
+    L.orc_verify_mt.argtypes = L.orc_verify.argtypes + [ctypes.c_int]
+    L.orc_verify_mt.restype = ctypes.c_int
 
 
 def _f32(a):
@@ -197,16 +207,21 @@ def draft_row(L_row, A, Bm, prev: int, u: float, query: int = -1) -> dict:
     return o.as_dict()
 
 
-def markov_draft(L, A, Bm, x0, seed: int):
-    """Free-running draft.  L [B][gamma][V], A [V][r], Bm [r][V], x0 [B]."""
+def markov_draft(L, A, Bm, x0, seed: int, threads: int = 1):
+    """Free-running draft.  L [B][gamma][V], A [V][r], Bm [r][V], x0 [B].
+    threads > 1 splits the requests over that many POSIX threads (same results)."""
     Ll, Aa, Bb, xx = _f32(L), _f32(A), _f32(Bm), _i32(x0)
     B, gamma, V = Ll.shape
     r = Aa.shape[1]
     tok = np.zeros((B, gamma), dtype=np.int32)
     p = np.zeros((B, gamma), dtype=np.float32)
     lse = np.zeros((B, gamma), dtype=np.float64)
-    _check(lib().orc_markov_draft(_ptr(Ll), _ptr(Aa), _ptr(Bb), _ptr(xx), B, gamma, V, r, ctypes.c_uint64(seed),
-                                  _ptr(tok), _ptr(p), _ptr(lse)), "markov_draft")
+    args = (_ptr(Ll), _ptr(Aa), _ptr(Bb), _ptr(xx), B, gamma, V, r, ctypes.c_uint64(seed), _ptr(tok), _ptr(p),
+            _ptr(lse))
+    if threads > 1:
+        _check(lib().orc_markov_draft_mt(*args, int(threads)), "markov_draft_mt")
+    else:
+        _check(lib().orc_markov_draft(*args), "markov_draft")
     return tok, p, lse
 
 
@@ -292,8 +307,9 @@ def final_token(T_b, L_b, A, Bm, x0_b: int, tok_b, ell: int, a: int, seed: int, 
     return o.as_dict()
 
 
-def verify(T, L, A, Bm, x0, tok, pd, ell, seed: int):
-    """Full verification.  T [B][gamma+1][V], L [B][gamma][V]."""
+def verify(T, L, A, Bm, x0, tok, pd, ell, seed: int, threads: int = 1):
+    """Full verification.  T [B][gamma+1][V], L [B][gamma][V].
+    threads > 1 splits the requests over that many POSIX threads (same results)."""
     TT, Ll, Aa, Bb = _f32(T), _f32(L), _f32(A), _f32(Bm)
     xx, tt, pp, ll = _i32(x0), _i32(tok), _f32(pd), _i32(ell)
     B, gamma, V = Ll.shape
@@ -302,6 +318,10 @@ def verify(T, L, A, Bm, x0, tok, pd, ell, seed: int):
     out = np.zeros((B, gamma + 1), dtype=np.int32)
     n_out = np.zeros(B, dtype=np.int32)
     tp = np.zeros((B, gamma), dtype=np.float32)
-    _check(lib().orc_verify(_ptr(TT), _ptr(Ll), _ptr(Aa), _ptr(Bb), _ptr(xx), _ptr(tt), _ptr(pp), _ptr(ll), B, gamma,
-                            V, r, ctypes.c_uint64(seed), _ptr(acc), _ptr(out), _ptr(n_out), _ptr(tp)), "verify")
+    args = (_ptr(TT), _ptr(Ll), _ptr(Aa), _ptr(Bb), _ptr(xx), _ptr(tt), _ptr(pp), _ptr(ll), B, gamma, V, r,
+            ctypes.c_uint64(seed), _ptr(acc), _ptr(out), _ptr(n_out), _ptr(tp))
+    if threads > 1:
+        _check(lib().orc_verify_mt(*args, int(threads)), "verify_mt")
+    else:
+        _check(lib().orc_verify(*args), "verify")
     return acc, out, n_out, tp

@@ -15,7 +15,9 @@ Anything else is a hard failure.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
+import os
 from typing import Iterable, List, Optional, Tuple
 
 import numpy as np
@@ -30,7 +32,8 @@ THETA_RTOL = 1e-5   # survivals, relative
 
 @dataclasses.dataclass
 class Report:
-    checked: int = 0
+    checked: int = 0     # values compared (decisions, probabilities, states, survivals, lengths)
+    decisions: int = 0   # sampling and accept decisions compared (the events a flip can occur in)
     draft_flips: int = 0
     accept_flips: int = 0
     final_flips: int = 0
@@ -43,10 +46,42 @@ class Report:
     def ok(self) -> bool:
         return not self.failures
 
+    @property
+    def flips(self) -> int:
+        return self.draft_flips + self.accept_flips + self.final_flips
+
+    def merge(self, other: "Report"):
+        self.checked += other.checked
+        self.decisions += other.decisions
+        self.draft_flips += other.draft_flips
+        self.accept_flips += other.accept_flips
+        self.final_flips += other.final_flips
+        for f in other.failures:
+            self.fail(f)
+
     def summary(self) -> str:
-        return (f"checked={self.checked} draft_flips={self.draft_flips} accept_flips={self.accept_flips} "
-                f"final_flips={self.final_flips} failures={len(self.failures)}"
+        return (f"checked={self.checked} decisions={self.decisions} draft_flips={self.draft_flips} "
+                f"accept_flips={self.accept_flips} final_flips={self.final_flips} failures={len(self.failures)}"
                 + ("" if self.ok() else "\n  " + "\n  ".join(self.failures[:10])))
+
+
+def default_threads() -> int:
+    """Host threads for the oracle side of a check (the oracle's C calls release the GIL)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _parallel(fn, items: list, rep: Report, threads: int):
+    """Run fn(chunk, report) over contiguous chunks of items on a thread pool and merge the reports in order."""
+    if threads <= 1 or len(items) < 2 * threads:
+        fn(items, rep)
+        return
+    n = threads * 4
+    chunks = [items[len(items) * i // n: len(items) * (i + 1) // n] for i in range(n)]
+    reps = [Report() for _ in chunks]
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda cr: fn(cr[0], cr[1]), zip(chunks, reps)))
+    for r in reps:
+        rep.merge(r)
 
 
 def _sample_flip_allowed(o_tok: int, y: int, o: dict) -> bool:
@@ -58,12 +93,19 @@ def _sample_flip_allowed(o_tok: int, y: int, o: dict) -> bool:
 
 
 def check_draft(L, A, Bm, x0, seed, tok, p, lse, rep: Report, rows: Optional[Iterable[Tuple[int, int]]] = None,
-                states=None):
+                states=None, threads: int = 1):
     """L [B][g][V] f32, tok/p/lse GPU outputs [B][g].  rows: (b, k) pairs with k 1-based; default all.
-    states [B][g][r] (RNN head): the operand of (b, k) is states[b][k-1] instead of A[x_{k-1}]."""
+    states [B][g][r] (RNN head): the operand of (b, k) is states[b][k-1] instead of A[x_{k-1}].
+    threads > 1 spreads the rows over a thread pool."""
     B, gamma, V = L.shape
     if rows is None:
         rows = [(b, k) for b in range(B) for k in range(1, gamma + 1)]
+    _parallel(lambda part, r: _check_draft_rows(L, A, Bm, x0, seed, tok, p, lse, r, part, states), list(rows), rep,
+              threads)
+
+
+def _check_draft_rows(L, A, Bm, x0, seed, tok, p, lse, rep: Report, rows, states):
+    V = L.shape[2]
     for b, k in rows:
         if states is not None:
             A, prev = states[b], k - 1
@@ -76,6 +118,7 @@ def check_draft(L, A, Bm, x0, seed, tok, p, lse, rep: Report, rows: Optional[Ite
         u = uniform(seed, b, k, 0)
         o = draft_row(L[b, k - 1], A, Bm, prev, u, query=y)
         rep.checked += 1
+        rep.decisions += 1
         if o["tok"] != y:
             if _sample_flip_allowed(o["tok"], y, o):
                 rep.draft_flips += 1
@@ -133,12 +176,21 @@ def check_select(theta_gpu, budget, len_gpu, rep: Report):
 
 
 def check_verify(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_out, target_p, rep: Report,
-                 requests: Optional[Iterable[int]] = None, states=None):
+                 requests: Optional[Iterable[int]] = None, states=None, threads: int = 1):
     """Teacher-forced on the GPU's draft outputs, verify lengths and accepted counts.
-    states [B][g][r] (RNN head): residual draft rows use states[b][k-1] as the operand."""
-    B, gamma, V = L.shape
+    states [B][g][r] (RNN head): residual draft rows use states[b][k-1] as the operand.
+    threads > 1 spreads the requests over a thread pool."""
+    B = L.shape[0]
     if requests is None:
         requests = range(B)
+    _parallel(lambda part, r: _check_verify_requests(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_out,
+                                                     target_p, r, part, states), [int(b) for b in requests], rep,
+              threads)
+
+
+def _check_verify_requests(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_out, target_p, rep: Report,
+                           requests, states):
+    B, gamma, V = L.shape
     for b in requests:
         b = int(b)
         l = int(ell[b])
@@ -157,6 +209,7 @@ def check_verify(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_out, targe
                     rep.fail(f"verify b={b} k={k + 1}: p_t beyond the verify length is {float(target_p[b, k])}")
         # GPU decisions: accept at positions < a_g, reject at a_g (if a_g < l)
         for k in range(min(a_g + 1, l)):
+            rep.decisions += 1
             gpu_acc = k < a_g
             orc_acc = bool(us[k] < np.float32(ratio[k]))
             if gpu_acc != orc_acc:
@@ -182,6 +235,7 @@ def check_verify(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_out, targe
                             query=y)
         else:
             o = final_token(T[b], L[b], A, Bm, int(x0[b]), tok[b], l, a_g, seed, b, query=y)
+        rep.decisions += 1
         if o["tok"] != y:
             if _sample_flip_allowed(o["tok"], y, o):
                 rep.final_flips += 1

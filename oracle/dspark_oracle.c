@@ -43,6 +43,7 @@
  *   - a degenerate residual (all max(0, p_t - p_d) == 0) falls back to p_t.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -204,13 +205,14 @@ int orc_draft_row(const float* L_row, const float* A, const float* Bm, int V, in
     return ORC_OK;
 }
 
-/* gamma sequential draft steps for every request ([PL] 3.1: the sequential  */
-/* stage samples left to right, each position conditioned on the token just */
-/* sampled; x_0 is the last committed token).                                */
-int orc_markov_draft(const float* L, const float* A, const float* Bm, const int32_t* x0, int B, int gamma, int V,
-                     int r, uint64_t seed, int32_t* tok, float* p, double* lse)
+/* gamma sequential draft steps for requests b0..b1-1 ([PL] 3.1: the        */
+/* sequential stage samples left to right, each position conditioned on the */
+/* token just sampled; x_0 is the last committed token).  Arrays are the    */
+/* whole batch; b is the request index of the random-number counter.         */
+static int orc_markov_draft_range(const float* L, const float* A, const float* Bm, const int32_t* x0, int b0, int b1,
+                                  int gamma, int V, int r, uint64_t seed, int32_t* tok, float* p, double* lse)
 {
-    for (int b = 0; b < B; ++b) {
+    for (int b = b0; b < b1; ++b) {
         int prev = x0[b];
         for (int k = 1; k <= gamma; ++k) {
             orc_row_out o;
@@ -225,6 +227,12 @@ int orc_markov_draft(const float* L, const float* A, const float* Bm, const int3
         }
     }
     return ORC_OK;
+}
+
+int orc_markov_draft(const float* L, const float* A, const float* Bm, const int32_t* x0, int B, int gamma, int V,
+                     int r, uint64_t seed, int32_t* tok, float* p, double* lse)
+{
+    return orc_markov_draft_range(L, A, Bm, x0, 0, B, gamma, V, r, seed, tok, p, lse);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -542,13 +550,15 @@ int orc_final_token(const float* T_b, const float* L_b, const float* A, const fl
     return rc;
 }
 
-int orc_verify(const float* T, const float* L, const float* A, const float* Bm, const int32_t* x0,
-               const int32_t* tok, const float* pd, const int32_t* len, int B, int gamma, int V, int r, uint64_t seed,
-               int32_t* accepted, int32_t* out_tok, int32_t* n_out, float* target_p)
+/* Verification of requests b0..b1-1 (whole-batch arrays). */
+static int orc_verify_range(const float* T, const float* L, const float* A, const float* Bm, const int32_t* x0,
+                            const int32_t* tok, const float* pd, const int32_t* len, int b0, int b1, int gamma, int V,
+                            int r, uint64_t seed, int32_t* accepted, int32_t* out_tok, int32_t* n_out,
+                            float* target_p)
 {
     double* pt = (double*)malloc(sizeof(double) * (size_t)(gamma > 0 ? gamma : 1));
     if (!pt) return ORC_ERR_ALLOC;
-    for (int b = 0; b < B; ++b) {
+    for (int b = b0; b < b1; ++b) {
         int ell = len[b];
         if (ell < 0 || ell > gamma) {
             free(pt);
@@ -578,4 +588,100 @@ int orc_verify(const float* T, const float* L, const float* A, const float* Bm, 
     }
     free(pt);
     return ORC_OK;
+}
+
+int orc_verify(const float* T, const float* L, const float* A, const float* Bm, const int32_t* x0,
+               const int32_t* tok, const float* pd, const int32_t* len, int B, int gamma, int V, int r, uint64_t seed,
+               int32_t* accepted, int32_t* out_tok, int32_t* n_out, float* target_p)
+{
+    return orc_verify_range(T, L, A, Bm, x0, tok, pd, len, 0, B, gamma, V, r, seed, accepted, out_tok, n_out,
+                            target_p);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The same two calls with the requests split into contiguous ranges over   */
+/* POSIX threads (requests are independent in the draft and the verify;     */
+/* only the selection couples them).  Each thread runs the sequential code  */
+/* above on its own range, so the results are those of the one-thread call */
+/* bit for bit.  nthreads < 1 means 1.                                      */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const float *T, *L, *A, *Bm, *pd;
+    const int32_t *x0, *tok, *len;
+    int b0, b1, gamma, V, r;
+    uint64_t seed;
+    int32_t *tok_out, *accepted, *out_tok, *n_out;
+    float *p, *target_p;
+    double* lse;
+    int rc;
+} orc_job;
+
+static void* orc_draft_job(void* arg)
+{
+    orc_job* j = (orc_job*)arg;
+    j->rc = orc_markov_draft_range(j->L, j->A, j->Bm, j->x0, j->b0, j->b1, j->gamma, j->V, j->r, j->seed, j->tok_out,
+                                   j->p, j->lse);
+    return NULL;
+}
+
+static void* orc_verify_job(void* arg)
+{
+    orc_job* j = (orc_job*)arg;
+    j->rc = orc_verify_range(j->T, j->L, j->A, j->Bm, j->x0, j->tok, j->pd, j->len, j->b0, j->b1, j->gamma, j->V,
+                             j->r, j->seed, j->accepted, j->out_tok, j->n_out, j->target_p);
+    return NULL;
+}
+
+static int orc_run_jobs(orc_job* proto, int B, int nthreads, void* (*fn)(void*))
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > B) nthreads = B > 0 ? B : 1;
+    orc_job* jobs = (orc_job*)malloc(sizeof(orc_job) * (size_t)nthreads);
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    unsigned char* running = (unsigned char*)calloc((size_t)nthreads, 1);
+    if (!jobs || !th || !running) {
+        free(jobs);
+        free(th);
+        free(running);
+        return ORC_ERR_ALLOC;
+    }
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = *proto;
+        jobs[i].b0 = (int)((int64_t)B * i / nthreads);
+        jobs[i].b1 = (int)((int64_t)B * (i + 1) / nthreads);
+        jobs[i].rc = ORC_OK;
+        /* the last range runs on the calling thread, as does any whose thread fails to start */
+        if (i + 1 < nthreads && pthread_create(&th[i], NULL, fn, &jobs[i]) == 0) running[i] = 1;
+        else fn(&jobs[i]);
+    }
+    for (int i = 0; i < nthreads; ++i)
+        if (running[i]) pthread_join(th[i], NULL);
+    int rc = ORC_OK;
+    for (int i = 0; i < nthreads; ++i)
+        if (jobs[i].rc != ORC_OK && rc == ORC_OK) rc = jobs[i].rc;
+    free(jobs);
+    free(th);
+    free(running);
+    return rc;
+}
+
+int orc_markov_draft_mt(const float* L, const float* A, const float* Bm, const int32_t* x0, int B, int gamma, int V,
+                        int r, uint64_t seed, int32_t* tok, float* p, double* lse, int nthreads)
+{
+    orc_job j;
+    memset(&j, 0, sizeof(j));
+    j.L = L; j.A = A; j.Bm = Bm; j.x0 = x0; j.gamma = gamma; j.V = V; j.r = r; j.seed = seed;
+    j.tok_out = tok; j.p = p; j.lse = lse;
+    return orc_run_jobs(&j, B, nthreads, orc_draft_job);
+}
+
+int orc_verify_mt(const float* T, const float* L, const float* A, const float* Bm, const int32_t* x0,
+                  const int32_t* tok, const float* pd, const int32_t* len, int B, int gamma, int V, int r,
+                  uint64_t seed, int32_t* accepted, int32_t* out_tok, int32_t* n_out, float* target_p, int nthreads)
+{
+    orc_job j;
+    memset(&j, 0, sizeof(j));
+    j.T = T; j.L = L; j.A = A; j.Bm = Bm; j.x0 = x0; j.tok = tok; j.pd = pd; j.len = len; j.gamma = gamma; j.V = V;
+    j.r = r; j.seed = seed; j.accepted = accepted; j.out_tok = out_tok; j.n_out = n_out; j.target_p = target_p;
+    return orc_run_jobs(&j, B, nthreads, orc_verify_job);
 }

@@ -63,6 +63,14 @@ int orc_verify(const float* T, const float* L, const float* A, const float* Bm, 
                const int32_t* tok, const float* pd, const int32_t* len, int B, int gamma, int V, int r, uint64_t seed,
                int32_t* accepted, int32_t* out_tok, int32_t* n_out, float* target_p);
 
+/* orc_markov_draft / orc_verify with the requests split over nthreads POSIX
+ * threads; results identical to the one-thread calls. */
+int orc_markov_draft_mt(const float* L, const float* A, const float* Bm, const int32_t* x0, int B, int gamma, int V,
+                        int r, uint64_t seed, int32_t* tok, float* p, double* lse, int nthreads);
+int orc_verify_mt(const float* T, const float* L, const float* A, const float* Bm, const int32_t* x0,
+                  const int32_t* tok, const float* pd, const int32_t* len, int B, int gamma, int V, int r,
+                  uint64_t seed, int32_t* accepted, int32_t* out_tok, int32_t* n_out, float* target_p, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,15 +28,17 @@ def run_step(inp, budget: int, seed: int, dev=None):
                 out_tok=host(out_tok), n_out=host(n_out), tp=host(tp))
 
 
-def check_step(inp, out, budget: int, seed: int, draft_rows=None, requests=None) -> check.Report:
+def check_step(inp, out, budget: int, seed: int, draft_rows=None, requests=None, threads: int = 1) -> check.Report:
+    """Teacher-forced oracle check of one step: draft_rows / requests None = every row / request;
+    threads > 1 spreads the oracle over host threads."""
     T, L, A, Bm = f32(inp.T), f32(inp.L), f32(inp.A), f32(inp.Bm)
     x0 = inp.x0.numpy()
     rep = check.Report()
-    check.check_draft(L, A, Bm, x0, seed, out["tok"], out["p"], out["lse"], rep, rows=draft_rows)
+    check.check_draft(L, A, Bm, x0, seed, out["tok"], out["p"], out["lse"], rep, rows=draft_rows, threads=threads)
     check.check_survival(inp.z.numpy(), inp.temps.numpy(), out["theta"], rep)
     check.check_select(out["theta"], budget, out["ell"], rep)
     check.check_verify(T, L, A, Bm, x0, out["tok"], out["p"], out["ell"], seed, out["acc"], out["out_tok"],
-                       out["n_out"], out["tp"], rep, requests=requests)
+                       out["n_out"], out["tp"], rep, requests=requests, threads=threads)
     return rep
 
 

@@ -259,18 +259,30 @@ def test_objective_clamps_and_errors():
         oracle.select_objective(theta, t, -1)
 
 
-def test_threshold_leading_run():
+def test_threshold_constructed_cases():
+    """Static-threshold admission (paperlayer.ai summary, section 4.3) on rows whose answers are fixed in
+    advance: a survival equal to tau is verified (>=), a NaN ends the run, and on non-monotone given
+    survivals only the leading run counts (later positions above tau stay unverified)."""
+    nan = np.float32(np.nan)
+    f = np.float32
+    below = np.nextafter(f(0.3), f(0))  # the largest float32 under 0.3
+    theta = np.array([
+        [0.9, 0.5, 0.3, 0.1],       # 0.3 == tau counts: 3
+        [0.3, 0.3, 0.2, 0.2],       # ties at tau: 2
+        [0.8, nan, 0.9, 0.9],       # NaN mid-row ends the run: 1
+        [nan, 1.0, 1.0, 1.0],       # NaN first: 0
+        [below, below, 0.0, 0.0],   # one ulp under tau: 0
+        [0.5, 0.2, 0.6, 0.7],       # not monotone: only the leading run, 1
+        [1.0, 1.0, 1.0, 1.0],       # 4
+        [-0.0, 0.0, -0.0, 0.0],     # signed zeros: 0 (and all 4 at tau = 0)
+    ], dtype=np.float32)
+    assert oracle.select_threshold(theta, f(0.3)).tolist() == [3, 2, 1, 0, 0, 1, 4, 0]
+    assert oracle.select_threshold(theta, f(0.0)).tolist() == [4, 4, 1, 0, 4, 4, 4, 4]
+    assert oracle.select_threshold(theta, f(1.0)).tolist() == [0, 0, 0, 0, 0, 0, 4, 0]
+    assert oracle.select_threshold(theta, below).tolist() == [3, 2, 1, 0, 2, 1, 4, 0]
+    assert oracle.select_threshold(theta, nan).tolist() == [0] * 8  # no comparison with NaN holds
+    # monotone survivals: the run is the number of positions at or above tau
     g = np.random.default_rng(3)
-    theta = g.uniform(0, 1, (50, 6)).astype(np.float32)
-    theta[::7, 2] = np.nan
-    for tau in (0.0, 0.3, 0.5, 0.99, 1.0):
-        ln = oracle.select_threshold(theta, tau)
-        for b in range(50):
-            run = 0
-            while run < 6 and theta[b, run] >= tau:
-                run += 1
-            assert ln[b] == run
-    # non-increasing survivals: the run is the count of positions at or above tau
     th2 = oracle.survival((g.standard_normal((20, 5))).astype(np.float32), np.ones(5, dtype=np.float32))
     assert oracle.select_threshold(th2, 0.2).tolist() == (th2 >= np.float32(0.2)).sum(1).tolist()
 

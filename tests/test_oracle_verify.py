@@ -186,3 +186,118 @@ def test_target_p_reported_for_verified_positions_only():
                 assert tp[b, k] == pytest.approx(ref, rel=1e-6)
             else:
                 assert tp[b, k] == 0.0
+
+
+# ----------------------------------------------------------------------------- exact law by enumeration
+def _exact_softmax(x):
+    """Softmax of a float64 vector as exact rationals summing to 1: the float64 weights exp(x - max)
+    taken as exact fractions and normalised exactly (the law the enumeration below assumes)."""
+    from fractions import Fraction
+    x = np.asarray(x, dtype=np.float64)
+    w = [Fraction(float(v)) for v in np.exp(x - x.max())]
+    s = sum(w)
+    return [v / s for v in w]
+
+
+def _enumerate_law(q, pd_of, ell, gamma):
+    """Exact law of the emitted tuple for one request, by summing over every draft path and every
+    accept / reject event with exact rationals (menfem.com note, Methodology: the k-th drafted token is
+    kept with probability min(1, p_t/p_d) and the first rejection ends the step; the token after a
+    rejection comes from normalise(max(0, p_t - p_d)) at that position, and after ell acceptances from
+    p_t of position ell+1).
+    q[k] is the target law at position k+1 (k = 0..gamma); pd_of(k, x) the draft law at position k+1 given
+    the conditioning token x (x = -1 for the committed token x_0).  Returns {tuple: probability}."""
+    from fractions import Fraction
+    law = {}
+
+    def add(t, pr):
+        law[t] = law.get(t, Fraction(0)) + pr
+
+    def walk(k, prev, prefix, pr):
+        if pr == 0:
+            return
+        if k == ell:  # every verified token accepted: one token from the target at position ell+1
+            for w, qw in enumerate(q[k]):
+                add(prefix + (w,), pr * qw)
+            return
+        p = pd_of(k, prev)
+        resid = [max(Fraction(0), q[k][w] - p[w]) for w in range(len(p))]
+        rs = sum(resid)
+        for x, px in enumerate(p):
+            if px == 0:
+                continue
+            acc = min(Fraction(1), q[k][x] / px)
+            walk(k + 1, x, prefix + (x,), pr * px * acc)
+            if acc < 1:  # rejection at position k+1: the residual token ends the step
+                for w, rw in enumerate(resid):
+                    if rw:
+                        add(prefix + (w,), pr * px * (1 - acc) * rw / rs)
+
+    walk(0, -1, (), Fraction(1))
+    return law
+
+
+@pytest.mark.parametrize("V,gamma", [(3, 3), (4, 2), (4, 3)])
+def test_verify_law_exact_by_enumeration(V, gamma):
+    """For every verify length ell = 0..gamma: (i) the enumerated law satisfies the exactness identity of
+    the acceptance rule with no rounding at all -- given the emitted prefix y_1..y_{j-1} and that a j-th token
+    is emitted, y_j follows p_t at position j, so the law of the tuple is the product of the target
+    probabilities along it times a stopping law; (ii) the oracle's realised tuples (draft + verify over
+    many requests with identical rows, Markov-conditioned draft) follow the enumerated law (chi-square)."""
+    from fractions import Fraction
+    g = np.random.default_rng(100 + 10 * V + gamma)
+    r = 3
+    Tk = (g.standard_normal((gamma + 1, V)) * 1.2).astype(np.float32)
+    Lk = (g.standard_normal((gamma, V)) * 1.2).astype(np.float32)
+    A = (g.standard_normal((V, r)) * 0.8).astype(np.float32)
+    Bm = (g.standard_normal((r, V)) * 0.8).astype(np.float32)
+    x0v = int(g.integers(0, V))
+    q = [_exact_softmax(Tk[k].astype(np.float64)) for k in range(gamma + 1)]
+    pd_cache = {}
+
+    def pd_of(k, prev):
+        x = x0v if prev < 0 else prev
+        if (k, x) not in pd_cache:
+            f = Lk[k].astype(np.float64) + A[x].astype(np.float64) @ Bm.astype(np.float64)
+            pd_cache[(k, x)] = _exact_softmax(f)
+        return pd_cache[(k, x)]
+
+    n_per = 120000
+    ells = np.repeat(np.arange(gamma + 1, dtype=np.int32), n_per)
+    B = ells.size
+    T = np.broadcast_to(Tk, (B, gamma + 1, V)).copy()
+    L = np.broadcast_to(Lk, (B, gamma, V)).copy()
+    x0 = np.full(B, x0v, dtype=np.int32)
+    tok, pd, _ = oracle.markov_draft(L, A, Bm, x0, SEED)
+    acc, out, n_out, _ = oracle.verify(T, L, A, Bm, x0, tok, pd, ells, SEED)
+    for ell in range(gamma + 1):
+        law = _enumerate_law(q, pd_of, ell, gamma)
+        assert sum(law.values()) == 1
+        # (i) exactness: P(prefix, y_j = w, n >= j) = P(prefix, n >= j) * p_t,j(w) for every prefix and w
+        for j in range(1, ell + 2):
+            reach = {}
+            emit = {}
+            for t, pr in law.items():
+                if len(t) >= j:
+                    reach[t[:j - 1]] = reach.get(t[:j - 1], Fraction(0)) + pr
+                    emit[t[:j]] = emit.get(t[:j], Fraction(0)) + pr
+            for pre, pr in reach.items():
+                for w in range(V):
+                    assert emit.get(pre + (w,), Fraction(0)) == pr * q[j - 1][w]
+        # (ii) the oracle's tuples against the law
+        sel = ells == ell
+        keys = [tuple(int(v) for v in out[i, :n_out[i]]) for i in np.nonzero(sel)[0]]
+        cells = sorted(law, key=lambda t: (len(t), t))
+        idx = {t: i for i, t in enumerate(cells)}
+        counts = np.zeros(len(cells))
+        for t in keys:
+            assert t in idx, (ell, t)  # no tuple of probability zero
+            counts[idx[t]] += 1
+        expect = np.array([float(law[t]) for t in cells]) * len(keys)
+        big = expect >= 5
+        obs = np.append(counts[big], counts[~big].sum())
+        exp = np.append(expect[big], expect[~big].sum())
+        if exp[-1] == 0:
+            obs, exp = obs[:-1], exp[:-1]
+        pval = stats.chisquare(obs, exp * obs.sum() / exp.sum()).pvalue
+        assert pval > 1e-4, (V, gamma, ell, pval)

@@ -5,12 +5,15 @@ token ids, except counted near-boundary flips (|u - boundary| < 1e-5).
 Probabilities within 1e-5 relative, log-normalisers within 1e-5, survivals
 within 1e-5 relative.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
 
 from draft_verify_sampling_prev_amd import synth
 from gpu_util import check_step, run_step, structural_checks
+from oracle import check
 
 pytestmark = pytest.mark.gpu
 
@@ -18,16 +21,18 @@ pytestmark = pytest.mark.gpu
 MAX_FLIPS = 3
 
 
-def _run_and_check(wl, seed=None, draft_rows=None, requests=None, data_seed=None):
+def _run_and_check(wl, seed=None, draft_rows=None, requests=None, data_seed=None, inp=None):
     seed = wl.philox_seed if seed is None else seed
-    inp = synth.make_inputs(wl, seed=data_seed)
+    inp = synth.make_inputs(wl, seed=data_seed) if inp is None else inp
     print(f"case {wl.describe()} seed={seed:#x}", flush=True)
     out = run_step(inp, wl.budget, seed)
     structural_checks(out, wl.gamma)
-    rep = check_step(inp, out, wl.budget, seed, draft_rows=draft_rows, requests=requests)
-    print("  ", rep.summary(), flush=True)
+    t0 = time.perf_counter()
+    rep = check_step(inp, out, wl.budget, seed, draft_rows=draft_rows, requests=requests,
+                     threads=check.default_threads())
+    print("  ", rep.summary(), f"(oracle {time.perf_counter() - t0:.1f} s)", flush=True)
     assert rep.ok(), rep.summary()
-    assert rep.draft_flips + rep.accept_flips + rep.final_flips <= MAX_FLIPS
+    assert rep.flips <= MAX_FLIPS, rep.summary()
     return out, rep
 
 
@@ -93,14 +98,32 @@ def test_zero_markov_factors_reduce_to_plain_softmax():
     assert rep.ok(), rep.summary()
 
 
-def test_headline_shape_sampled():
-    """B=256, gamma=5, V=129280, r=256, bf16, budget 768: the benchmarked configuration."""
+_HEADLINE = {}
+
+
+def _headline_inputs():
+    if not _HEADLINE:
+        _HEADLINE["inp"] = synth.make_inputs(synth.dsv4())
+    return _HEADLINE["inp"]
+
+
+def test_headline_shape_full():
+    """B=256, gamma=5, V=129280, r=256, bf16, budget 768, in the launch configuration the benchmark times:
+    every one of the 1280 draft rows and every one of the 256 requests against the oracle."""
     wl = synth.dsv4()
-    g = np.random.default_rng(5)
-    rows = [(int(b), int(k)) for b, k in zip(g.integers(0, wl.B, 40), g.integers(1, wl.gamma + 1, 40))]
-    rows += [(0, 1), (wl.B - 1, wl.gamma)]
-    reqs = sorted(set(int(b) for b in g.integers(0, wl.B, 40)) | {0, wl.B - 1})
-    _run_and_check(wl, draft_rows=rows, requests=reqs)
+    out, rep = _run_and_check(wl, inp=_headline_inputs())
+    assert rep.decisions >= wl.B * wl.gamma + wl.B
+
+
+def test_headline_shape_run_to_run_bitwise():
+    """Two runs of the benchmarked step give identical bits in every output (the residual-row list is filled
+    by an atomic slot counter in no fixed order; no result may depend on that order)."""
+    wl = synth.dsv4()
+    inp = _headline_inputs()
+    a = run_step(inp, wl.budget, wl.philox_seed)
+    b = run_step(inp, wl.budget, wl.philox_seed)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
 
 
 def test_qwen_shape_sampled():
@@ -141,11 +164,16 @@ def test_load_sweep_sampled(mult):
     out = run_step(inp, wl.budget, wl.philox_seed)
     structural_checks(out, wl.gamma)
     assert int(out["ell"].sum()) == min(wl.budget, wl.B * wl.gamma)
-    rows, reqs = _sample(wl, 200 + mult)
-    rep = check_step(inp, out, wl.budget, wl.philox_seed, draft_rows=rows, requests=reqs)
+    rows, reqs = _sample(wl, 200 + mult, n=160)
+    rep = check_step(inp, out, wl.budget, wl.philox_seed, draft_rows=rows, requests=reqs,
+                     threads=check.default_threads())
     print("  ", rep.summary(), flush=True)
     assert rep.ok(), rep.summary()
-    assert rep.draft_flips + rep.accept_flips + rep.final_flips <= MAX_FLIPS
+    assert rep.flips <= MAX_FLIPS
+    if mult == 8:  # run to run, bitwise, at the B = 1024 shape (four row blocks, three rounds of tile slots)
+        again = run_step(inp, wl.budget, wl.philox_seed)
+        for k in out:
+            assert np.array_equal(out[k].view(np.uint8), again[k].view(np.uint8)), k
 
 
 def test_run_to_run_determinism():

@@ -1,8 +1,9 @@
 """GPU parity of the RNN sequential head (dspark_rnn_draft + dspark_rnn_verify)
 against the oracle, teacher-forced on the GPU's own states and tokens: each
 state within half an ulp of its element type of tanh(W h_prev + A[x]), each
-draft sample / residual from the GPU's state as the operand, with the flip
-allowance of the Markov path."""
+draft sample / residual from the GPU's state as the operand.  Near-boundary
+flips (sampling and accept decisions only) are capped at 3 per case, as on
+the Markov path."""
 import numpy as np
 import pytest
 import torch
@@ -13,6 +14,8 @@ from oracle import check
 
 pytestmark = pytest.mark.gpu
 
+MAX_FLIPS = 3
+
 
 def _f32(t):
     return np.ascontiguousarray(t.float().cpu().numpy())
@@ -20,6 +23,7 @@ def _f32(t):
 
 def _run(wl, seed=777, draft_rows=None, requests=None, state_rows=None):
     dev = torch.device("cuda:0")
+    print(f"case rnn {wl.describe()} seed={seed}", flush=True)
     inp = synth.make_inputs(wl)
     g = inp.to(dev)
     r = wl.r
@@ -33,13 +37,15 @@ def _run(wl, seed=777, draft_rows=None, requests=None, state_rows=None):
     A, Wh, Bm, L, T = _f32(g.A), _f32(Wt), _f32(g.Bm), _f32(g.L), _f32(g.T)
     rep = check.Report()
     check.check_rnn_states(A, Wh, inp.x0.numpy(), tk, Hh, rep, elem=wl.dtype, rows=state_rows)
+    nt = check.default_threads()
     check.check_draft(L, A, Bm, inp.x0.numpy(), seed, tk, p.cpu().numpy(), lse.cpu().numpy(), rep, rows=draft_rows,
-                      states=Hh)
+                      states=Hh, threads=nt)
     check.check_verify(T, L, A, Bm, inp.x0.numpy(), tk, p.cpu().numpy(), ell.cpu().numpy(), seed, acc.cpu().numpy(),
                        out_tok.cpu().numpy(), n_out.cpu().numpy(), tp.cpu().numpy(), rep, requests=requests,
-                       states=Hh)
+                       states=Hh, threads=nt)
+    print("  ", rep.summary(), flush=True)
     assert rep.ok(), rep.summary()
-    assert rep.draft_flips + rep.accept_flips + rep.final_flips <= max(2, rep.checked // 1000), rep.summary()
+    assert rep.flips <= MAX_FLIPS, rep.summary()
     # the states really carry the prefix: they differ from tanh(A[x]) once W acts (k >= 2)
     if wl.gamma >= 2:
         assert not np.allclose(Hh[:, 1], np.tanh(A[tk[:, 0]]), atol=1e-4)
@@ -60,9 +66,7 @@ def test_rnn_draft_verify_matches_oracle(case):
     _run(synth.tiny(**case))
 
 
-def test_rnn_headline_shape_sampled():
-    """B = 256, gamma = 5, V = 129280, r = 256, bf16: sampled rows and requests, every state."""
-    wl = synth.dsv4()
-    g = np.random.default_rng(31)
-    rows = [(int(b), int(k)) for b, k in zip(g.integers(0, wl.B, 24), g.integers(1, wl.gamma + 1, 24))]
-    _run(wl, draft_rows=rows, requests=sorted(set(int(b) for b in g.integers(0, wl.B, 16))))
+def test_rnn_headline_shape_full():
+    """B = 256, gamma = 5, V = 129280, r = 256, bf16: every state, every draft row and every request."""
+    rep = _run(synth.dsv4())
+    assert rep.decisions >= 256 * 5 + 256
