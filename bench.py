@@ -44,15 +44,16 @@ def _workload(name: str):
 
 
 def draft_tiles_bytes_flops(wl) -> tuple:
-    """Algorithmic bytes and flops of one launch of the draft Markov tile kernel:
-    the step's L rows (B*V), Bm (r*V) and the gathered A rows (B*r), plus the
-    per-(row, tile) partials written (float max + float sum = 8 bytes) and the
-    token reads."""
+    """Per launch of the draft Markov tile kernel (one draft step):
+    method bytes -- what the step itself must read: the step's L rows (B*V), Bm (r*V) and the gathered A rows
+    (B*r), s bytes each; implementation bytes -- what this kernel adds: its per-(row, 64-column tile) softmax
+    partials (8 bytes) and the token reads; flops -- the rank-r contraction, 2*B*r*V."""
     s = 2 if wl.dtype == "bf16" else 4
     nT = (wl.V + 63) // 64 if wl.dtype == "bf16" else (wl.V + 127) // 128
-    byts = s * (wl.B * wl.V + wl.r * wl.V + wl.B * wl.r) + wl.B * nT * 8 + wl.B * 4
+    method = s * (wl.B * wl.V + wl.r * wl.V + wl.B * wl.r)
+    impl = wl.B * nT * 8 + wl.B * 4
     flops = 2.0 * wl.B * wl.r * wl.V
-    return byts, flops
+    return method, impl, flops
 
 
 # The draft tile kernel's translation unit: the source and every header it includes.
@@ -64,13 +65,13 @@ def vocab_passes(wl, kern: dict, adm: float, rej: float) -> dict:
     """HBM fraction of the vocabulary passes and MFMA fraction of the rank-r contraction, per step.
 
     Algorithmic bytes (the method's minimum, s bytes per element): draft tiles, per launch the step's L rows,
-    Bm, the A rows, the partials and tokens; target rows, s*V per verified draft (adm per step); residual tiles,
+    Bm and the A rows; target rows, s*V per verified draft (adm per step); residual tiles,
     Bm plus the target row and the draft-L row of each request with a rejection (rej per step); bonus rows,
     s*V per request without one.  Flops: 2*r*V per draft row and per residual row.  Times are the per-kernel
-    averages of the event-bracketed pass (each includes its dispatch gap)."""
+    averages of the timed pass (events bound to each kernel's own dispatch)."""
     s = 2 if wl.dtype == "bf16" else 4
     B, V, r, gamma = wl.B, wl.V, wl.r, wl.gamma
-    tile_b, _ = draft_tiles_bytes_flops(wl)
+    tile_b, _, _ = draft_tiles_bytes_flops(wl)
     per_launch = {"draft_tiles": tile_b, "target_partials": s * V * adm,
                   "resid_tiles": s * (r * V + 2 * rej * V), "bonus_partials": s * V * (B - rej)}
     out = {}
@@ -126,31 +127,74 @@ def measured_traffic(workload: str):
     return t
 
 
-def cpu_baseline(inp, wl, seed: int, n_req: int) -> dict:
-    """The oracle, as it stands, on the first n_req requests of the same inputs (1 thread)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def host_threads() -> int:
+    """Threads for the multi-thread oracle run: the cores this process may use, at most 16 (the host share
+    of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(inp, wl, seed: int, n_req_1: int, n_req_n: int) -> dict:
+    """The oracle, as it stands, timed on the host: one thread on the first n_req_1 requests, and the requests
+    split over host_threads() POSIX threads (draft and verify; the selection is one thread) on the first
+    n_req_n requests, each a full draft + schedule + verify step with the budget scaled to the sample."""
     import numpy as np
     import oracle
 
-    b = slice(0, n_req)
-    T = np.ascontiguousarray(inp.T[b].float().numpy())
-    L = np.ascontiguousarray(inp.L[b].float().numpy())
     A = np.ascontiguousarray(inp.A.float().numpy())
     Bm = np.ascontiguousarray(inp.Bm.float().numpy())
-    x0 = inp.x0[b].numpy()
-    z = inp.z[b].numpy()
     temps = inp.temps.numpy()
-    budget = int(round(wl.budget * n_req / wl.B))
-    t0 = time.perf_counter()
-    tok, p, lse = oracle.markov_draft(L, A, Bm, x0, seed)
-    theta = oracle.survival(z, temps)
-    ell = oracle.select(theta, budget)
-    acc, out, n_out, tp = oracle.verify(T, L, A, Bm, x0, tok, p, ell, seed)
-    dt = time.perf_counter() - t0
-    emitted = int(n_out.sum())
-    return {"value": emitted / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n_req} of {wl.B} requests of the same workload, budget {budget} "
-                      f"(scaled), one full draft+schedule+verify step: {emitted} tokens in {dt:.2f} s",
-            "cpu": platform.processor() or platform.machine()}
+
+    def run(n_req, threads):
+        b = slice(0, n_req)
+        T = np.ascontiguousarray(inp.T[b].float().numpy())
+        L = np.ascontiguousarray(inp.L[b].float().numpy())
+        x0 = inp.x0[b].numpy()
+        z = inp.z[b].numpy()
+        budget = int(round(wl.budget * n_req / wl.B))
+        t0 = time.perf_counter()
+        tok, p, lse = oracle.markov_draft(L, A, Bm, x0, seed, threads=threads)
+        theta = oracle.survival(z, temps)
+        ell = oracle.select(theta, budget)
+        acc, out, n_out, tp = oracle.verify(T, L, A, Bm, x0, tok, p, ell, seed, threads=threads)
+        dt = time.perf_counter() - t0
+        emitted = int(n_out.sum())
+        return emitted / dt, (f"first {n_req} of {wl.B} requests, budget {budget} (scaled), one full "
+                              f"draft+schedule+verify step: {emitted} tokens in {dt:.2f} s")
+
+    nt = host_threads()
+    v1, s1 = run(n_req_1, 1)
+    vn, sn = run(n_req_n, nt)
+    return {"value": round(vn, 2), "unit": "tokens/s", "cores": nt, "kind": "oracle", "sample": sn,
+            "single_thread": {"value": round(v1, 2), "cores": 1, "sample": s1},
+            "cpu": cpu_model()}
+
+
+def acceptance_by_position(acc, ell, gamma: int) -> dict:
+    """Measured conditional acceptance per draft position k over the given steps: among requests that
+    verified position k and accepted 1..k-1, the share that accepted k."""
+    import numpy as np
+    acc, ell = np.asarray(acc), np.asarray(ell)
+    out = {}
+    for k in range(1, gamma + 1):
+        reach = (ell >= k) & (acc >= k - 1)
+        n = int(reach.sum())
+        out[str(k)] = {"reached": n, "accepted": round(float((acc[reach] >= k).mean()), 4) if n else None}
+    return out
 
 
 def main():
@@ -159,9 +203,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv4")
-    ap.add_argument("--cpu-requests", type=int, default=160, help="requests in the oracle CPU-baseline sample (~10 s)")
+    ap.add_argument("--cpu-requests", type=int, default=64,
+                    help="requests in the one-thread oracle CPU-baseline sample (~12 s)")
+    ap.add_argument("--cpu-requests-mt", type=int, default=256,
+                    help="requests in the multi-thread oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="also time HIP-graph replay of the whole step")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the whole step")
     ap.add_argument("--schedule", choices=("budget", "objective", "threshold"), default="budget",
                     help="admission rule of the step: the budget (default, the headline), objective-based "
                          "admission against a synthetic step-time profile capped at the budget, or a static threshold")
@@ -181,6 +228,7 @@ def main():
                                    "is a design, not an implementation", "n_gpus": args.gpus}))
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     if args.copy_calibration:
@@ -227,21 +275,22 @@ def main():
     zc = torch.empty((B, gamma), dtype=torch.float32, device=dev)
     zs = zc if args.confidence else g.z
 
-    def schedule():
+    def schedule(budget):
         if args.schedule == "budget":
-            dsp.dspark_schedule(zs, g.temps, wl.budget, survival=theta, out_len=ell)
+            dsp.dspark_schedule(zs, g.temps, budget, survival=theta, out_len=ell)
         elif args.schedule == "objective":
-            dsp.dspark_schedule_objective(zs, g.temps, prof, wl.budget, survival=theta, out_len=ell)
+            dsp.dspark_schedule_objective(zs, g.temps, prof, budget, survival=theta, out_len=ell)
         else:
             dsp.dspark_schedule_threshold(zs, g.temps, args.tau, survival=theta, out_len=ell)
 
     Wt = (torch.randn((r, r), generator=torch.Generator().manual_seed(wl.data_seed + 3)) / r ** 0.5).to(g.L.dtype).to(dev)
     Hst = torch.empty((B, gamma, r), dtype=g.L.dtype, device=dev)
 
-    def step(i: int, seed: int):
+    def step(i: int, seed, budget=None):
+        budget = wl.budget if budget is None else budget
         if args.head == "rnn":
             dsp.dspark_rnn_draft(g.L, g.A, g.Bm, Wt, g.x0, seed, ws=ws, out=(tok, p, lse, Hst))
-            schedule()
+            schedule(budget)
             dsp.dspark_rnn_verify(g.T, g.L, Hst, g.Bm, tok, p, lse, ell, seed, ws=ws,
                                   out=(acc, out_tok, n_out_all[i], tp))
             return
@@ -249,7 +298,7 @@ def main():
             dsp.dspark_markov_draft_conf(g.L, g.A, g.Bm, g.x0, seed, g.z, wc, ws=ws, out=(tok, p, lse, zc))
         else:
             dsp.dspark_markov_draft(g.L, g.A, g.Bm, g.x0, seed, ws=ws, out=(tok, p, lse))
-        schedule()
+        schedule(budget)
         dsp.dspark_verify(g.T, g.L, g.A, g.Bm, g.x0, tok, p, lse, ell, seed, ws=ws,
                           out=(acc, out_tok, n_out_all[i], tp))
 
@@ -275,9 +324,10 @@ def main():
     emitted = int(n_out_all[:K].sum().item())
     value = emitted / (ms_step * K / 1000.0)
 
-    # Roofline timing: the same K steps again, with HIP events bracketing
-    # every launch of the dominant kernel (draft Markov tiles) on the stream
-    # it is launched on.
+    # Roofline timing: the same K steps again, with a pair of HIP events bound
+    # to every dispatch of the dominant kernel (draft Markov tiles) through
+    # hipExtLaunchKernelGGL on the stream it runs on, so each interval is the
+    # kernel's own execution.
     binding.profile_start(max_launches=K * gamma + 16, kernels=("draft_tiles",))
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -290,34 +340,51 @@ def main():
     ms_step_instr = e0.elapsed_time(e1) / K
     tiles_ms, tiles_n = binding.profile_query("draft_tiles")
 
-    # Per-kernel averages (separate pass, all kernels bracketed) for context.
+    # Per-kernel averages (separate pass, every kernel timed) for context, and
+    # the verify lengths / accepted counts of those steps.
     kern = {}
-    n_adm = torch.zeros((), dtype=torch.int64, device=dev)  # verified drafts over the 10 steps
-    n_rej = torch.zeros((), dtype=torch.int64, device=dev)  # requests with a rejection over the 10 steps
-    binding.profile_start(max_launches=10 * (2 * gamma + 6) + 16)
-    for i in range(10):
+    NK = 10
+    acc_hist = torch.zeros((NK, B), dtype=torch.int32, device=dev)
+    ell_hist = torch.zeros((NK, B), dtype=torch.int32, device=dev)
+    binding.profile_start(max_launches=NK * (2 * gamma + 6) + 16)
+    for i in range(NK):
         step(K + args.warmup, base_seed + 5000 + i)
-        n_adm += ell.sum()
-        n_rej += (acc < ell).sum()
+        acc_hist[i].copy_(acc)
+        ell_hist[i].copy_(ell)
     torch.cuda.synchronize()
     binding.profile_stop()
     for name in binding.KERNELS:
         t, n = binding.profile_query(name)
         if n:
-            kern[name] = {"avg_us": round(1000.0 * t / n, 2), "launches_per_step": n // 10}
-    vocab = vocab_passes(wl, kern, n_adm.item() / 10.0, n_rej.item() / 10.0)
+            kern[name] = {"avg_us": round(1000.0 * t / n, 3), "launches_per_step": n // NK}
+    n_adm = int(ell_hist.sum().item()) / NK
+    n_rej = int((acc_hist < ell_hist).sum().item()) / NK
+    vocab = vocab_passes(wl, kern, n_adm, n_rej)
+
+    # Acceptance profile of the workload: NK untimed steps with every drafted
+    # token verified (budget B*gamma), conditional acceptance per position.
+    acc_full = torch.zeros((NK, B), dtype=torch.int32, device=dev)
+    for i in range(NK):
+        step(K + args.warmup, base_seed + 7000 + i, budget=B * gamma)
+        acc_full[i].copy_(acc)
+    torch.cuda.synchronize()
+    accept_profile = acceptance_by_position(acc_full.cpu().numpy().ravel(), np.full(NK * B, gamma), gamma)
 
     graph = None
-    if args.graph:
+    if not args.no_graph:
+        # The whole step captured once with its seed in device memory, advanced
+        # by one inside the graph, so every replay draws fresh uniforms.
+        seed_t = torch.full((1,), base_seed & 0x7FFFFFFFFFFFFFFF, dtype=torch.int64, device=dev)
         gr = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            step(K + args.warmup, base_seed)  # warm the capture stream
+            step(K + args.warmup, seed_t)  # warm the capture stream
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(gr):
-            step(K + args.warmup, base_seed)
+            seed_t.add_(1)
+            step(K + args.warmup, seed_t)
         torch.cuda.synchronize()
         gr.replay()
         torch.cuda.synchronize()
@@ -327,13 +394,16 @@ def main():
             gr.replay()
         e1.record()
         torch.cuda.synchronize()
-        graph = {"ms_per_step": round(e0.elapsed_time(e1) / K, 4)}
+        g_ms = e0.elapsed_time(e1) / K
+        graph = {"ms_per_step": round(g_ms, 4),
+                 "tokens_per_s": round(emitted / K / (g_ms / 1000.0), 1),
+                 "note": "HIP-graph replay of the whole step (seed in device memory, advanced in the graph); "
+                         "tokens/s = the eager timed steps' mean emitted tokens per step / replay time"}
 
-    byts, flops = draft_tiles_bytes_flops(wl)
+    method_b, impl_b, flops = draft_tiles_bytes_flops(wl)
     avg_s = tiles_ms / max(tiles_n, 1) / 1000.0
-    achieved = byts / avg_s / 1e9
+    achieved = method_b / avg_s / 1e9
     tr = measured_traffic(wl.name)
-    acc_rate = None
     result = {
         "metric": "draft+verify tokens/s at B=256,V=129280,gamma=5 (emitted tokens per step time)",
         "value": round(value, 1),
@@ -360,16 +430,22 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (tr["bytes_per_launch"] if tr else None),
                      "traffic_source": (tr["source"] if tr else "no counter summary for the current kernel sources"),
-                     "algorithmic_bytes_per_launch": byts, "avg_launch_us": round(avg_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": method_b,
+                     "algorithmic_bytes": "the step's L rows B*V + Bm r*V + gathered A rows B*r, 2 bytes each",
+                     "implementation_bytes_per_launch": impl_b,
+                     "implementation_bytes": "per-(row, 64-column tile) softmax partials written (8 bytes) + tokens; "
+                                             "not counted in achieved",
+                     "avg_launch_us": round(avg_s * 1e6, 3),
                      "launches": tiles_n,
-                     "timing": f"HIP events around each launch, over a second pass of the same {K} steps "
-                               f"({round(ms_step_instr, 4)} ms per step with the events)",
+                     "timing": f"HIP event pairs bound to each dispatch (hipExtLaunchKernelGGL), over a second "
+                               f"pass of the same {K} steps ({round(ms_step_instr, 4)} ms per step in that pass)",
                      "mfma_tflops": round(flops / avg_s / 1e12, 2),
                      "mfma_frac": round(flops / avg_s / 1e12 / (BF16_MFMA_PEAK_TFLOPS if wl.dtype == "bf16"
                                                                else FP32_MFMA_PEAK_TFLOPS), 4)},
         "kernels": kern,
         "vocab_passes": vocab,
         "verify_len_histogram": torch.bincount(ell.long().cpu(), minlength=gamma + 1).tolist(),
+        "acceptance_by_position": {"budget": B * gamma, "steps": NK, "conditional": accept_profile},
         "secondary": {"drafted_tokens_per_s": round(B * gamma / (ms_step / 1000.0), 1),
                       "verified_tokens_per_s": round(vocab["verified_per_step"] / (ms_step / 1000.0), 1),
                       "mean_emitted_per_request": round(emitted / K / B, 4)},
@@ -379,7 +455,8 @@ def main():
         result["graph_replay"] = graph
     if not args.no_cpu_baseline and args.schedule == "budget" and not args.confidence and args.head == "markov":
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(inp, wl, base_seed, min(args.cpu_requests, B))
+        result["cpu_baseline"] = cpu_baseline(inp, wl, base_seed, min(args.cpu_requests, B),
+                                              min(args.cpu_requests_mt, B))
     print(json.dumps(result), flush=True)
 
 

@@ -55,17 +55,17 @@ def load_library():
     L.dspark_workspace_size.restype = ctypes.c_size_t
     L.dspark_workspace_size.argtypes = [_I, _I, _I, _I]
     L.dspark_markov_draft.restype = _I
-    L.dspark_markov_draft.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P,
+    L.dspark_markov_draft.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]
     L.dspark_markov_draft_conf.restype = _I
     L.dspark_markov_draft_conf.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P,
-                                           _P, _P, ctypes.c_size_t, _P]
+                                           _P, _P, _P, ctypes.c_size_t, _P]
     L.dspark_rnn_draft.restype = _I
-    L.dspark_rnn_draft.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P,
+    L.dspark_rnn_draft.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P]
     L.dspark_rnn_verify.restype = _I
     L.dspark_rnn_verify.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P,
-                                    _P, _P, ctypes.c_size_t, _P]
+                                    _P, _P, _P, ctypes.c_size_t, _P]
     L.dspark_schedule.restype = _I
     L.dspark_schedule.argtypes = [_P, _P, _I, _I, ctypes.c_int64, _P, _P, _P]
     L.dspark_schedule_objective.restype = _I
@@ -74,7 +74,7 @@ def load_library():
     L.dspark_schedule_threshold.argtypes = [_P, _P, _I, _I, ctypes.c_float, _P, _P, _P]
     L.dspark_verify.restype = _I
     L.dspark_verify.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P,
-                                _P, _P, ctypes.c_size_t, _P]
+                                _P, _P, _P, ctypes.c_size_t, _P]
     L.dspark_profile_start.restype = _I
     L.dspark_profile_start.argtypes = [_I, ctypes.c_uint]
     L.dspark_profile_stop.restype = _I
@@ -132,15 +132,26 @@ def _stream(device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _seed(seed, device):
+    """(by-value seed, device seed pointer) for the C calls.  `seed` is an int (fixed when the call is
+    enqueued) or a one-element int64 tensor on the call's device, whose bits the kernels read as the
+    unsigned 64-bit seed when they run (so a captured graph draws new uniforms after the tensor changes)."""
+    if isinstance(seed, torch.Tensor):
+        _dev(seed, "seed", device, torch.int64, (1,))
+        return ctypes.c_uint64(0), ctypes.c_void_p(seed.data_ptr())
+    return ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), None
+
+
 def workspace(B: int, gamma: int, V: int, r: int, device) -> torch.Tensor:
     n = dspark_workspace_size(B, gamma, V, r)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def dspark_markov_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor, seed: int,
+def dspark_markov_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor, seed,
                         ws: Optional[torch.Tensor] = None, out: Optional[Tuple] = None,
                         stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Draft gamma tokens per request.  Returns (draft_tok int32 [B][g], draft_p f32 [B][g], draft_lse f64 [B][g])."""
+    """Draft gamma tokens per request.  seed: int, or a one-element int64 device tensor read when the kernels run.
+    Returns (draft_tok int32 [B][g], draft_p f32 [B][g], draft_lse f64 [B][g])."""
     dev = L.device
     _dev(L, "L", None)
     B, gamma, V = L.shape
@@ -157,13 +168,13 @@ def dspark_markov_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: 
     if ws is None:
         ws = workspace(B, gamma, V, r, dev)
     rc = load_library().dspark_markov_draft(_dtype_code(L), _ptr(L), _ptr(A), _ptr(Bm), _ptr(x0), B, gamma, V, r,
-                                            ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(tok), _ptr(p),
+                                            *_seed(seed, dev), _ptr(tok), _ptr(p),
                                             _ptr(lse), _ptr(ws), ws.numel(), _stream(dev, stream))
     _check(rc, "dspark_markov_draft")
     return tok, p, lse
 
 
-def dspark_markov_draft_conf(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor, seed: int,
+def dspark_markov_draft_conf(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor, seed,
                              z0: torch.Tensor, wc: torch.Tensor, ws: Optional[torch.Tensor] = None,
                              out: Optional[Tuple] = None, stream=None):
     """Draft gamma tokens per request and the Markov-conditioned confidence
@@ -188,14 +199,14 @@ def dspark_markov_draft_conf(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
     if ws is None:
         ws = workspace(B, gamma, V, r, dev)
     rc = load_library().dspark_markov_draft_conf(_dtype_code(L), _ptr(L), _ptr(A), _ptr(Bm), _ptr(x0), B, gamma, V,
-                                                 r, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(z0), _ptr(wc),
+                                                 r, *_seed(seed, dev), _ptr(z0), _ptr(wc),
                                                  _ptr(tok), _ptr(p), _ptr(lse), _ptr(z), _ptr(ws), ws.numel(),
                                                  _stream(dev, stream))
     _check(rc, "dspark_markov_draft_conf")
     return tok, p, lse, z
 
 
-def dspark_rnn_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, Wt: torch.Tensor, x0: torch.Tensor, seed: int,
+def dspark_rnn_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, Wt: torch.Tensor, x0: torch.Tensor, seed,
                      ws: Optional[torch.Tensor] = None, out: Optional[Tuple] = None, stream=None):
     """Draft gamma tokens per request with the RNN head.  Returns (draft_tok int32 [B][g], draft_p f32,
     draft_lse f64, H [B][g][r] in the logits' dtype)."""
@@ -218,7 +229,7 @@ def dspark_rnn_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, Wt: tor
     if ws is None:
         ws = workspace(B, gamma, V, r, dev)
     rc = load_library().dspark_rnn_draft(_dtype_code(L), _ptr(L), _ptr(A), _ptr(Bm), _ptr(Wt), _ptr(x0), B, gamma, V,
-                                         r, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(tok), _ptr(p), _ptr(lse),
+                                         r, *_seed(seed, dev), _ptr(tok), _ptr(p), _ptr(lse),
                                          _ptr(H), _ptr(ws), ws.numel(), _stream(dev, stream))
     _check(rc, "dspark_rnn_draft")
     return tok, p, lse, H
@@ -301,7 +312,7 @@ def dspark_schedule_threshold(z: Optional[torch.Tensor], temps: Optional[torch.T
 
 def dspark_verify(Tgt: torch.Tensor, L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor,
                   draft_tok: torch.Tensor, draft_p: torch.Tensor, draft_lse: torch.Tensor, verify_len: torch.Tensor,
-                  seed: int, ws: Optional[torch.Tensor] = None, out: Optional[Tuple] = None, want_target_p: bool = True,
+                  seed, ws: Optional[torch.Tensor] = None, out: Optional[Tuple] = None, want_target_p: bool = True,
                   stream=None):
     """Rejection-sampling verification.
     Returns (accepted int32 [B], out_tok int32 [B][g+1], n_out int32 [B], target_p f32 [B][g] or None)."""
@@ -328,14 +339,14 @@ def dspark_verify(Tgt: torch.Tensor, L: torch.Tensor, A: torch.Tensor, Bm: torch
         ws = workspace(B, gamma, V, r, dev)
     rc = load_library().dspark_verify(_dtype_code(L), _ptr(Tgt), _ptr(L), _ptr(A), _ptr(Bm), _ptr(x0), _ptr(draft_tok),
                                       _ptr(draft_p), _ptr(draft_lse), _ptr(verify_len), B, gamma, V, r,
-                                      ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(acc), _ptr(out_tok),
+                                      *_seed(seed, dev), _ptr(acc), _ptr(out_tok),
                                       _ptr(n_out), _ptr(tp), _ptr(ws), ws.numel(), _stream(dev, stream))
     _check(rc, "dspark_verify")
     return acc, out_tok, n_out, tp
 
 
 def dspark_rnn_verify(Tgt: torch.Tensor, L: torch.Tensor, H: torch.Tensor, Bm: torch.Tensor, draft_tok: torch.Tensor,
-                      draft_p: torch.Tensor, draft_lse: torch.Tensor, verify_len: torch.Tensor, seed: int,
+                      draft_p: torch.Tensor, draft_lse: torch.Tensor, verify_len: torch.Tensor, seed,
                       ws: Optional[torch.Tensor] = None, out: Optional[Tuple] = None, want_target_p: bool = True,
                       stream=None):
     """Verification of an RNN-head draft (the residual rebuilds draft rows from the states H [B][g][r]).
@@ -362,7 +373,7 @@ def dspark_rnn_verify(Tgt: torch.Tensor, L: torch.Tensor, H: torch.Tensor, Bm: t
         ws = workspace(B, gamma, V, r, dev)
     rc = load_library().dspark_rnn_verify(_dtype_code(L), _ptr(Tgt), _ptr(L), _ptr(H), _ptr(Bm), _ptr(draft_tok),
                                           _ptr(draft_p), _ptr(draft_lse), _ptr(verify_len), B, gamma, V, r,
-                                          ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), _ptr(acc), _ptr(out_tok),
+                                          *_seed(seed, dev), _ptr(acc), _ptr(out_tok),
                                           _ptr(n_out), _ptr(tp), _ptr(ws), ws.numel(), _stream(dev, stream))
     _check(rc, "dspark_rnn_verify")
     return acc, out_tok, n_out, tp

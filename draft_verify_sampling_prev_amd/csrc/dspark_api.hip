@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "dspark.h"
@@ -66,43 +67,37 @@ int cu_count()
 }
 
 // ---------------------------------------------------------------------------
-// Kernel timing.
+// Kernel timing (measurement only; off unless dspark_profile_start was
+// called).  The state is process-wide and guarded by a mutex; the events of
+// a pair are bound to one kernel dispatch (hipExtLaunchKernelGGL), so an
+// interval is that kernel's execution, not the gap before it.
 // ---------------------------------------------------------------------------
 struct ProfState {
     bool on = false;
     unsigned mask = 0u;                // bit i set: time kernel i
-    int capacity = 0;
+    int capacity = 0;                  // events available (two per launch)
     std::vector<hipEvent_t> pool;
     int used = 0;
-    int open_id = -1;
     std::vector<int> ids;              // kernel id of each recorded pair
-    std::vector<int> starts, stops;    // indices into pool
+    std::vector<int> starts;           // index into pool of each pair's start (stop = start + 1)
     bool overflow = false;
 };
 static ProfState g_prof;
+static std::mutex g_prof_mu;
 
-void prof_begin(int id, hipStream_t s)
+ProfPair prof_pair(int id)
 {
-    if (!g_prof.on || !(g_prof.mask & (1u << id))) return;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    if (!g_prof.on || !(g_prof.mask & (1u << id))) return ProfPair{ nullptr, nullptr };
     if (g_prof.used + 2 > g_prof.capacity) {
         g_prof.overflow = true;
-        g_prof.open_id = -1;
-        return;
+        return ProfPair{ nullptr, nullptr };
     }
-    const int e = g_prof.used++;
-    (void)hipEventRecord(g_prof.pool[e], s);
-    g_prof.open_id = id;
-    g_prof.starts.push_back(e);
-}
-
-void prof_end(int id, hipStream_t s)
-{
-    if (!g_prof.on || g_prof.open_id != id) return;
-    const int e = g_prof.used++;
-    (void)hipEventRecord(g_prof.pool[e], s);
+    const int e = g_prof.used;
+    g_prof.used += 2;
     g_prof.ids.push_back(id);
-    g_prof.stops.push_back(e);
-    g_prof.open_id = -1;
+    g_prof.starts.push_back(e);
+    return ProfPair{ g_prof.pool[e], g_prof.pool[e + 1] };
 }
 
 static int check_common(int B, int gamma, int V, int r)
@@ -144,7 +139,7 @@ size_t dspark_workspace_size(int B, int gamma, int V, int r)
 }
 
 static int markov_draft_impl(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
-                             int gamma, int V, int r, uint64_t seed, const float* z0, const void* wc,
+                             int gamma, int V, int r, SeedArg seed, const float* z0, const void* wc,
                              int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, const void* Wt,
                              void* H, void* ws, size_t ws_bytes, void* stream)
 {
@@ -169,34 +164,34 @@ static int markov_draft_impl(int dtype, const void* L, const void* A, const void
 }
 
 int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B, int gamma,
-                        int V, int r, uint64_t seed, int32_t* draft_tok, float* draft_p, double* draft_lse, void* ws,
-                        size_t ws_bytes, void* stream)
+                        int V, int r, uint64_t seed, const uint64_t* seed_dev, int32_t* draft_tok, float* draft_p,
+                        double* draft_lse, void* ws, size_t ws_bytes, void* stream)
 {
     g_err[0] = 0;
-    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, seed, nullptr, nullptr, draft_tok, draft_p,
+    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, SeedArg{ seed, seed_dev }, nullptr, nullptr, draft_tok, draft_p,
                              draft_lse, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
-                             int gamma, int V, int r, uint64_t seed, const float* z0, const void* wc,
-                             int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, void* ws,
-                             size_t ws_bytes, void* stream)
+                             int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, const float* z0,
+                             const void* wc, int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out,
+                             void* ws, size_t ws_bytes, void* stream)
 {
     g_err[0] = 0;
     if (B > 0 && (!z0 || !wc || !z_out)) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
-    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, seed, z0, wc, draft_tok, draft_p, draft_lse, z_out,
+    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, SeedArg{ seed, seed_dev }, z0, wc, draft_tok, draft_p, draft_lse, z_out,
                              nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 int dspark_rnn_draft(int dtype, const void* L, const void* A, const void* Bm, const void* Wt, const int32_t* x0, int B,
-                     int gamma, int V, int r, uint64_t seed, int32_t* draft_tok, float* draft_p, double* draft_lse,
-                     void* H, void* ws, size_t ws_bytes, void* stream)
+                     int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, int32_t* draft_tok,
+                     float* draft_p, double* draft_lse, void* H, void* ws, size_t ws_bytes, void* stream)
 {
     g_err[0] = 0;
     if (B > 0 && (!Wt || !H)) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
     if (B > 0 && (!aligned16(H) || !aligned16(Wt))) return fail(DSPARK_ERR_INVALID_ARG, "H and Wt must be 16-byte aligned");
-    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, seed, nullptr, nullptr, draft_tok, draft_p,
-                             draft_lse, nullptr, Wt, H, ws, ws_bytes, stream);
+    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, SeedArg{ seed, seed_dev }, nullptr, nullptr,
+                             draft_tok, draft_p, draft_lse, nullptr, Wt, H, ws, ws_bytes, stream);
 }
 
 int dspark_schedule(const float* z, const float* temps, int B, int gamma, int64_t budget, float* survival,
@@ -255,7 +250,7 @@ int dspark_schedule_threshold(const float* z, const float* temps, int B, int gam
 
 static int verify_impl(int dtype, const void* Tgt, const void* L, const void* A, const void* Bm, const int32_t* x0,
                        const int32_t* draft_tok, const float* draft_p, const double* draft_lse,
-                       const int32_t* verify_len, int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted,
+                       const int32_t* verify_len, int B, int gamma, int V, int r, SeedArg seed, int32_t* accepted,
                        int32_t* out_tok, int32_t* n_out, float* target_p, const void* H, void* ws, size_t ws_bytes,
                        void* stream)
 {
@@ -279,22 +274,25 @@ static int verify_impl(int dtype, const void* Tgt, const void* L, const void* A,
 
 int dspark_verify(int dtype, const void* Tgt, const void* L, const void* A, const void* Bm, const int32_t* x0,
                   const int32_t* draft_tok, const float* draft_p, const double* draft_lse, const int32_t* verify_len,
-                  int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok, int32_t* n_out,
-                  float* target_p, void* ws, size_t ws_bytes, void* stream)
+                  int B, int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, int32_t* accepted,
+                  int32_t* out_tok, int32_t* n_out, float* target_p, void* ws, size_t ws_bytes, void* stream)
 {
     g_err[0] = 0;
-    return verify_impl(dtype, Tgt, L, A, Bm, x0, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r, seed,
+    return verify_impl(dtype, Tgt, L, A, Bm, x0, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r,
+                       SeedArg{ seed, seed_dev },
                        accepted, out_tok, n_out, target_p, nullptr, ws, ws_bytes, stream);
 }
 
 int dspark_rnn_verify(int dtype, const void* Tgt, const void* L, const void* H, const void* Bm,
                       const int32_t* draft_tok, const float* draft_p, const double* draft_lse,
-                      const int32_t* verify_len, int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted,
-                      int32_t* out_tok, int32_t* n_out, float* target_p, void* ws, size_t ws_bytes, void* stream)
+                      const int32_t* verify_len, int B, int gamma, int V, int r, uint64_t seed,
+                      const uint64_t* seed_dev, int32_t* accepted, int32_t* out_tok, int32_t* n_out, float* target_p,
+                      void* ws, size_t ws_bytes, void* stream)
 {
     g_err[0] = 0;
     if (B > 0 && !H) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
-    return verify_impl(dtype, Tgt, L, H, Bm, nullptr, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r, seed,
+    return verify_impl(dtype, Tgt, L, H, Bm, nullptr, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r,
+                       SeedArg{ seed, seed_dev },
                        accepted, out_tok, n_out, target_p, H, ws, ws_bytes, stream);
 }
 
@@ -302,7 +300,7 @@ int dspark_profile_start(int max_launches, unsigned kernel_mask)
 {
     g_err[0] = 0;
     if (max_launches < 1) return fail(DSPARK_ERR_INVALID_ARG, "max_launches must be >= 1");
-    g_prof.mask = kernel_mask;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
     const int need = 2 * max_launches;
     while ((int)g_prof.pool.size() < need) {
         hipEvent_t e;
@@ -310,12 +308,11 @@ int dspark_profile_start(int max_launches, unsigned kernel_mask)
         if (err != hipSuccess) return hip_status(err, "hipEventCreate");
         g_prof.pool.push_back(e);
     }
+    g_prof.mask = kernel_mask;
     g_prof.capacity = need;
     g_prof.used = 0;
-    g_prof.open_id = -1;
     g_prof.ids.clear();
     g_prof.starts.clear();
-    g_prof.stops.clear();
     g_prof.overflow = false;
     g_prof.on = true;
     return DSPARK_OK;
@@ -323,6 +320,7 @@ int dspark_profile_start(int max_launches, unsigned kernel_mask)
 
 int dspark_profile_stop(void)
 {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
     g_prof.on = false;
     return DSPARK_OK;
 }
@@ -332,15 +330,17 @@ int dspark_profile_query(int kernel, double* total_ms, int* launches)
     g_err[0] = 0;
     if (kernel < 0 || kernel >= K_COUNT || !total_ms || !launches)
         return fail(DSPARK_ERR_INVALID_ARG, "bad profile query");
+    std::lock_guard<std::mutex> lock(g_prof_mu);
     if (g_prof.overflow) return fail(DSPARK_ERR_INVALID_ARG, "profile event capacity exceeded");
     double tot = 0.0;
     int n = 0;
     for (size_t i = 0; i < g_prof.ids.size(); ++i) {
         if (g_prof.ids[i] != kernel) continue;
-        hipError_t e = hipEventSynchronize(g_prof.pool[g_prof.stops[i]]);
+        hipEvent_t e0 = g_prof.pool[g_prof.starts[i]], e1 = g_prof.pool[g_prof.starts[i] + 1];
+        hipError_t e = hipEventSynchronize(e1);
         if (e != hipSuccess) return hip_status(e, "hipEventSynchronize");
         float ms = 0.0f;
-        e = hipEventElapsedTime(&ms, g_prof.pool[g_prof.starts[i]], g_prof.pool[g_prof.stops[i]]);
+        e = hipEventElapsedTime(&ms, e0, e1);
         if (e != hipSuccess) return hip_status(e, "hipEventElapsedTime");
         tot += ms;
         ++n;

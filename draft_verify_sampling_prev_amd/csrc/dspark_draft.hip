@@ -322,8 +322,9 @@ __global__ __launch_bounds__(kThreads) void k_draft_locate(const typename DT::T*
                                                            float* __restrict__ p_out, double* __restrict__ lse_out,
                                                            const float2* __restrict__ part,
                                                            const typename DT::T* __restrict__ H, int B, int gamma,
-                                                           int V, int r, int k, int nT, uint64_t seed, ConfOut co)
+                                                           int V, int r, int k, int nT, SeedArg seed_arg, ConfOut co)
 {
+    const uint64_t seed = seed_of(seed_arg);
     typedef TileTraits<DT> TT;
     __shared__ __attribute__((aligned(1024))) char lds[TT::kLdsBytes];
     __shared__ BlockScratch bs;
@@ -428,8 +429,9 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
                                                           const float2* __restrict__ part, uint16_t* __restrict__ ag,
                                                           const uint16_t* __restrict__ H, int B, int gamma, int V,
                                                           int r, int k, int nT, int nM_next, int S_next,
-                                                          uint64_t seed, ConfOut co)
+                                                          SeedArg seed_arg, ConfOut co)
 {
+    const uint64_t seed = seed_of(seed_arg);
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
     // AG (not the last step): a second wave reads the next tile launch's
     // first tile ahead; it shares nothing with the first wave.
@@ -610,7 +612,7 @@ __global__ __launch_bounds__(kMaxRank) void k_rnn_state(const typename DT::T* __
 }
 
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
-                             int gamma, int V, int r, int k, uint64_t seed, int32_t* tok, float* p, double* lse,
+                             int gamma, int V, int r, int k, SeedArg seed, int32_t* tok, float* p, double* lse,
                              const float* z0, const void* wc, float* z_out, const void* Wt, void* H, void* ws,
                              const WsLayout& lay, hipStream_t s)
 {
@@ -633,39 +635,35 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     // bf16 tile grid: nM row blocks x S persistent slots.
     const int nM = (B + kTileRows - 1) / kTileRows;
     const int S = tile_slots(nT, nM, cu_count(), kPartTiles);
-    prof_begin(K_DRAFT_TILES, s);
     if (dtype == 1) {
         auto kern = (r + 31) / 32 == 8 ? k_draft_tiles_bf16<8> : k_draft_tiles_bf16<0>;
-        hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s, static_cast<const uint16_t*>(L),
+        launch_timed(K_DRAFT_TILES, kern, dim3(S * nM), dim3(64 * kTileWaves), s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok,
                            static_cast<const uint16_t*>(ag_path && k >= 2 ? ag : nullptr),
                            static_cast<const uint16_t*>(H), B, gamma, V, r, k, nT, nM, S, part);
     } else {
         const int nM32 = (B + 255) / 256;
-        hipLaunchKernelGGL(k_draft_tiles_f32, dim3(nT * nM32), dim3(kThreads), 0, s, static_cast<const float*>(L),
+        launch_timed(K_DRAFT_TILES, k_draft_tiles_f32, dim3(nT * nM32), dim3(kThreads), s, static_cast<const float*>(L),
                            static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok,
                            static_cast<const float*>(H), B, gamma, V, r, k, nT, nM32, part);
     }
-    prof_end(K_DRAFT_TILES, s);
-    prof_begin(K_DRAFT_LOCATE, s);
     if (wave_locate) {
         const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32, wag = ag_path && k < gamma;
         auto kern = small ? (k8 ? (wag ? k_draft_locate_bf16<8, 32, true> : k_draft_locate_bf16<8, 32, false>)
                                 : k_draft_locate_bf16<0, 32, false>)
                           : (k8 ? (wag ? k_draft_locate_bf16<8, 64, true> : k_draft_locate_bf16<8, 64, false>)
                                 : k_draft_locate_bf16<0, 64, false>);
-        hipLaunchKernelGGL(kern, dim3(B), dim3(wag ? 128 : 64), 0, s, static_cast<const uint16_t*>(L),
+        launch_timed(K_DRAFT_LOCATE, kern, dim3(B), dim3(wag ? 128 : 64), s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
                            ag, static_cast<const uint16_t*>(H), B, gamma, V, r, k, nT, nM, S, seed, co);
     } else if (dtype == 1) {
-        hipLaunchKernelGGL(k_draft_locate<Bf16>, dim3(B), dim3(kThreads), 0, s, static_cast<const uint16_t*>(L),
+        launch_timed(K_DRAFT_LOCATE, k_draft_locate<Bf16>, dim3(B), dim3(kThreads), s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
                            static_cast<const uint16_t*>(H), B, gamma, V, r, k, nT, seed, co);
     } else
-        hipLaunchKernelGGL(k_draft_locate<F32>, dim3(B), dim3(kThreads), 0, s, static_cast<const float*>(L),
+        launch_timed(K_DRAFT_LOCATE, k_draft_locate<F32>, dim3(B), dim3(kThreads), s, static_cast<const float*>(L),
                            static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, p, lse, part,
                            static_cast<const float*>(H), B, gamma, V, r, k, nT, seed, co);
-    prof_end(K_DRAFT_LOCATE, s);
     return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // kernel launchers: workspace layout, launcher declarations, kernel timing.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -38,7 +39,19 @@ struct WsLayout {
 
 WsLayout ws_layout(int B, int gamma, int V);
 
-// Kernel timing (opt-in, host-side hipEvents around launches; not thread-safe).
+// The Philox seed of a call as the kernels receive it: the by-value seed, or,
+// when `dev` is set, the 64-bit value at that device address, read by each
+// kernel when it runs (so a captured graph replayed after the caller has
+// written a new value there draws new uniforms).
+struct SeedArg {
+    uint64_t value;
+    const uint64_t* dev;
+};
+
+__device__ __forceinline__ uint64_t seed_of(const SeedArg& s) { return s.dev ? *s.dev : s.value; }
+
+// Kernel timing (opt-in; event pairs attached to the timed kernels' own
+// dispatches, so an interval is one kernel's execution).
 enum KernelId {
     K_DRAFT_TILES = 0,
     K_DRAFT_LOCATE,
@@ -66,8 +79,24 @@ inline int tile_slots(int nT, int nM, int cus, int max_tiles)
 // Compute units of the current device (cached per device).
 int cu_count();
 
-void prof_begin(int id, hipStream_t s);
-void prof_end(int id, hipStream_t s);
+// A free pair of timing events for one launch of kernel `id`, or {null, null}
+// when timing is off for it (or the event pool is exhausted).
+struct ProfPair {
+    hipEvent_t start, stop;
+};
+ProfPair prof_pair(int id);
+
+// Launch `kernel` on `s`; when kernel `id` is being timed, through
+// hipExtLaunchKernelGGL with the pair's events bound to this dispatch.
+template <typename F, typename... Args>
+inline void launch_timed(int id, F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args)
+{
+    const ProfPair e = prof_pair(id);
+    if (e.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0u, s, e.start, e.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
 
 // Launchers (return hipGetLastError()).
 // z0/wc/z_out (all null, or all set): the Markov-conditioned confidence
@@ -76,7 +105,7 @@ void prof_end(int id, hipStream_t s);
 // state h_k = tanh(W h_{k-1} + A[x_{k-1}]) into row (b, k-1) of H, which
 // then replaces A[x_{k-1}] as the operand.
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0,
-                             int B, int gamma, int V, int r, int k, uint64_t seed, int32_t* tok, float* p,
+                             int B, int gamma, int V, int r, int k, SeedArg seed, int32_t* tok, float* p,
                              double* lse, const float* z0, const void* wc, float* z_out, const void* Wt, void* H,
                              void* ws, const WsLayout& lay, hipStream_t s);
 
@@ -89,7 +118,7 @@ hipError_t launch_schedule_threshold(const float* z, const float* temps, int B, 
 
 hipError_t launch_verify(int dtype, const void* Tg, const void* L, const void* A, const void* Bm, const int32_t* x0,
                          const int32_t* tok, const float* pd, const double* lse_d, const int32_t* len, int B,
-                         int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok,
+                         int gamma, int V, int r, SeedArg seed, int32_t* accepted, int32_t* out_tok,
                          int32_t* n_out, float* target_p, const void* H, void* ws, const WsLayout& lay, hipStream_t s);
 
 }  // namespace dspark

@@ -400,7 +400,6 @@ __global__ __launch_bounds__(256) void k_schedule_threshold(const float* __restr
 hipError_t launch_schedule_objective(const float* z, const float* temps, int B, int gamma, const float* step_time,
                                      int64_t cap, float* survival, int32_t* len, hipStream_t s)
 {
-    prof_begin(K_SCHEDULE, s);
     int P = 64;
     while (P < B * gamma) P <<= 1;
     const int E = std::max(1, P / kSchedThreads);
@@ -409,29 +408,24 @@ hipError_t launch_schedule_objective(const float* z, const float* temps, int B, 
               : E == 4 ? k_schedule_objective<4>
               : E == 8 ? k_schedule_objective<8>
                        : k_schedule_objective<16>;
-    hipLaunchKernelGGL(kern, dim3(1), dim3(kSchedThreads), 0, s, z, temps, B, gamma, step_time, (long long)cap,
+    launch_timed(K_SCHEDULE, kern, dim3(1), dim3(kSchedThreads), s, z, temps, B, gamma, step_time, (long long)cap,
                        survival, len);
-    prof_end(K_SCHEDULE, s);
     return hipGetLastError();
 }
 
 hipError_t launch_schedule_threshold(const float* z, const float* temps, int B, int gamma, float tau,
                                      float* survival, int32_t* len, hipStream_t s)
 {
-    prof_begin(K_SCHEDULE, s);
-    hipLaunchKernelGGL(k_schedule_threshold, dim3((B + 255) / 256), dim3(256), 0, s, z, temps, B, gamma, tau,
+    launch_timed(K_SCHEDULE, k_schedule_threshold, dim3((B + 255) / 256), dim3(256), s, z, temps, B, gamma, tau,
                        survival, len);
-    prof_end(K_SCHEDULE, s);
     return hipGetLastError();
 }
 
 hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,
                            int32_t* len, hipStream_t s)
 {
-    prof_begin(K_SCHEDULE, s);
-    hipLaunchKernelGGL(k_schedule, dim3(1), dim3(kSchedThreads), 0, s, z, temps, B, gamma, (long long)admit,
+    launch_timed(K_SCHEDULE, k_schedule, dim3(1), dim3(kSchedThreads), s, z, temps, B, gamma, (long long)admit,
                        survival, len);
-    prof_end(K_SCHEDULE, s);
     return hipGetLastError();
 }
 

@@ -151,11 +151,12 @@ template <class DT>
 __global__ __launch_bounds__(64 * kAcceptWaves) void k_lse_accept(
     const typename DT::T* __restrict__ Tg, const float* __restrict__ pd, const int32_t* __restrict__ len,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const float* __restrict__ tgm,
-    const double* __restrict__ tgs, int B, int gamma, int V, int nC, int rnn, uint64_t seed,
+    const double* __restrict__ tgs, int B, int gamma, int V, int nC, int rnn, SeedArg seed_arg,
     int32_t* __restrict__ accepted, int32_t* __restrict__ n_out, float* __restrict__ target_p,
     double* __restrict__ lse_t, int32_t* __restrict__ resid_idx, int4* __restrict__ resid_list,
     int32_t* __restrict__ resid_count)
 {
+    const uint64_t seed = seed_of(seed_arg);
     const int b = blockIdx.x * kAcceptWaves + (int)(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (b >= B) return;
@@ -537,8 +538,9 @@ __global__ __launch_bounds__(kThreads) void k_final(
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ len,
     const int32_t* __restrict__ accepted, const int32_t* __restrict__ resid_idx, const float2* __restrict__ rpart,
     const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rnn,
-    uint64_t seed, int32_t* __restrict__ out_tok)
+    SeedArg seed_arg, int32_t* __restrict__ out_tok)
 {
+    const uint64_t seed = seed_of(seed_arg);
     typedef typename DT::T T;
     typedef TileTraits<DT> TT;
     __shared__ __attribute__((aligned(1024))) char lds[TT::kLdsBytes];
@@ -677,8 +679,9 @@ __global__ __launch_bounds__(64) void k_final_bf16(
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ len,
     const int32_t* __restrict__ accepted, const int32_t* __restrict__ resid_idx, const float2* __restrict__ rpart,
     const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rnn,
-    uint64_t seed, int32_t* __restrict__ out_tok)
+    SeedArg seed_arg, int32_t* __restrict__ out_tok)
 {
+    const uint64_t seed = seed_of(seed_arg);
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
@@ -811,7 +814,7 @@ __global__ __launch_bounds__(64) void k_final_bf16(
 template <class DT>
 static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, const void* Bm_, const int32_t* x0,
                            const int32_t* tok, const float* pd, const double* lse_d, const int32_t* len, int B,
-                           int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok,
+                           int gamma, int V, int r, SeedArg seed, int32_t* accepted, int32_t* out_tok,
                            int32_t* n_out, float* target_p, const void* H, void* ws, const WsLayout& lay, hipStream_t s)
 {
     // RNN head: the operand rows are the draft's states H[b][k-1] (row b*gamma + k-1) instead of A[x].
@@ -834,56 +837,46 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     double* bsum = reinterpret_cast<double*>(w + lay.bon_s);
     const int nT = n_tiles(std::is_same<DT, Bf16>::value ? 1 : 0, V), nC = n_chunks(V);
 
-    prof_begin(K_TARGET_PARTIALS, s);
-    hipLaunchKernelGGL(k_row_partials<DT>, dim3(nC, B * gamma), dim3(kThreads), 0, s, Tg, len, accepted, B, gamma, V,
+    launch_timed(K_TARGET_PARTIALS, k_row_partials<DT>, dim3(nC, B * gamma), dim3(kThreads), s, Tg, len, accepted, B, gamma, V,
                        nC, 0, tgm, tgs, rcnt);
-    prof_end(K_TARGET_PARTIALS, s);
-    prof_begin(K_ACCEPT, s);
-    hipLaunchKernelGGL(k_lse_accept<DT>, dim3((B + kAcceptWaves - 1) / kAcceptWaves), dim3(64 * kAcceptWaves), 0, s,
+    launch_timed(K_ACCEPT, k_lse_accept<DT>, dim3((B + kAcceptWaves - 1) / kAcceptWaves), dim3(64 * kAcceptWaves), s,
                        Tg, pd, len, x0, tok, tgm, tgs, B, gamma, V, nC, rnn, seed, accepted, n_out, target_p, lse_t,
                        ridx, rlist, rcnt);
-    prof_end(K_ACCEPT, s);
-    prof_begin(K_RESID_TILES, s);
     if (std::is_same<DT, Bf16>::value) {
         const int nM = (B + kTileRows - 1) / kTileRows;
         const int S = tile_slots(nT, nM, cu_count(), kResPartTiles);
         auto kern = (r + 31) / 32 == 8 ? k_resid_tiles_bf16<8> : k_resid_tiles_bf16<0>;
-        hipLaunchKernelGGL(kern, dim3(S * nM), dim3(64 * kTileWaves), 0, s,
+        launch_timed(K_RESID_TILES, kern, dim3(S * nM), dim3(64 * kTileWaves), s,
                            reinterpret_cast<const uint16_t*>(Tg), reinterpret_cast<const uint16_t*>(L),
                            reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(Bm), x0, tok,
                            lse_d, lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, S, nA, rpart);
     } else {
         const int nM = (B + 255) / 256;
-        hipLaunchKernelGGL(k_resid_tiles_f32, dim3(nT * nM), dim3(kThreads), 0, s,
+        launch_timed(K_RESID_TILES, k_resid_tiles_f32, dim3(nT * nM), dim3(kThreads), s,
                            reinterpret_cast<const float*>(Tg), reinterpret_cast<const float*>(L),
                            reinterpret_cast<const float*>(A), reinterpret_cast<const float*>(Bm), x0, tok, lse_d,
                            lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, nA, rpart);
     }
-    prof_end(K_RESID_TILES, s);
-    prof_begin(K_BONUS_PARTIALS, s);
-    hipLaunchKernelGGL(k_row_partials<DT>, dim3(nC, B), dim3(kThreads), 0, s, Tg, len, accepted, B, gamma, V, nC, 1,
+    launch_timed(K_BONUS_PARTIALS, k_row_partials<DT>, dim3(nC, B), dim3(kThreads), s, Tg, len, accepted, B, gamma, V, nC, 1,
                        bm, bsum, (int32_t*)nullptr);
-    prof_end(K_BONUS_PARTIALS, s);
-    prof_begin(K_FINAL, s);
     if (std::is_same<DT, Bf16>::value && nT <= 64 * 64 && nC <= 64 * 4) {
         const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32;
         auto kern = small ? (k8 ? k_final_bf16<8, 32> : k_final_bf16<0, 32>)
                           : (k8 ? k_final_bf16<8, 64> : k_final_bf16<0, 64>);
-        hipLaunchKernelGGL(kern, dim3(B), dim3(64), 0, s, reinterpret_cast<const uint16_t*>(Tg),
+        launch_timed(K_FINAL, kern, dim3(B), dim3(64), s, reinterpret_cast<const uint16_t*>(Tg),
                            reinterpret_cast<const uint16_t*>(L), reinterpret_cast<const uint16_t*>(A),
                            reinterpret_cast<const uint16_t*>(Bm), x0, tok, lse_d, lse_t, len, accepted, ridx, rpart, bm,
                            bsum, gamma, V, r, nT, nC, rnn, seed, out_tok);
     } else {
-        hipLaunchKernelGGL(k_final<DT>, dim3(B), dim3(kThreads), 0, s, Tg, L, A, Bm, x0, tok, lse_d, lse_t, len,
+        launch_timed(K_FINAL, k_final<DT>, dim3(B), dim3(kThreads), s, Tg, L, A, Bm, x0, tok, lse_d, lse_t, len,
                            accepted, ridx, rpart, bm, bsum, gamma, V, r, nT, nC, rnn, seed, out_tok);
     }
-    prof_end(K_FINAL, s);
     return hipGetLastError();
 }
 
 hipError_t launch_verify(int dtype, const void* Tg, const void* L, const void* A, const void* Bm, const int32_t* x0,
                          const int32_t* tok, const float* pd, const double* lse_d, const int32_t* len, int B,
-                         int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok,
+                         int gamma, int V, int r, SeedArg seed, int32_t* accepted, int32_t* out_tok,
                          int32_t* n_out, float* target_p, const void* H, void* ws, const WsLayout& lay,
                          hipStream_t s)
 {

@@ -15,10 +15,11 @@
  * Conventions shared by every call
  *   - Every pointer except `stream` is DEVICE memory owned by the caller,
  *     row-major and contiguous.  The library allocates nothing, keeps no state
- *     between calls and never synchronises the host; a call only validates
- *     its arguments and enqueues fixed-shape kernels on `stream` (a
- *     hipStream_t; NULL = the null stream), so a sequence of calls can be
- *     captured in a HIP graph.  Inputs must stay alive until the stream has
+ *     between calls (the measurement-only timing hook at the end aside) and
+ *     never synchronises the host; a call only validates its arguments and
+ *     enqueues fixed-shape kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream), so a sequence of calls can be captured in a HIP graph (see
+ *     seed_dev below for fresh random draws on each replay).  Inputs must stay alive until the stream has
  *     passed the work.
  *   - Positions are 1-based, k = 1..gamma; array index k-1.
  *   - dtype: DSPARK_BF16 (bfloat16 logits and Markov factors) or DSPARK_F32;
@@ -35,6 +36,14 @@
  *     and counter (k, b, d, 0), times 2^-24.  Draw d = 0 draft sample,
  *     1 accept test, 2 residual sample, 3 bonus sample.  A step is therefore a
  *     pure function of its inputs and the seed.
+ *   - Seed: the calls that draw uniforms take `uint64_t seed` and
+ *     `const uint64_t* seed_dev`.  With seed_dev == NULL the seed is `seed`,
+ *     fixed at enqueue time (and therefore fixed inside a captured graph:
+ *     every replay would draw the same uniforms).  With seed_dev set (device
+ *     memory, 8-byte aligned) `seed` is ignored and each kernel reads the seed
+ *     from *seed_dev when it runs, so a graph replayed after the caller has
+ *     written a new value there (e.g. one per decoding step) draws new
+ *     uniforms.  The value must not change while the call's kernels run.
  *   - Sampling is at temperature 1 by inverse CDF over vocabulary index
  *     order: token = min{ j : w_0 + ... + w_j > u * S }.
  *   - Errors: a negative return means nothing was enqueued;
@@ -68,17 +77,6 @@ enum {
 const char* dspark_version(void);
 
 /* Message for the last non-OK return on this thread ("" if none). */
-/*
- * dspark_rnn_verify -- dspark_verify for a draft made by dspark_rnn_draft:
- * the residual at a rejected position k rebuilds the draft logits from the
- * state H[b][k-1] (f = L[b][k-1] + h_k . Bm) instead of A[x_{k-1}]; there is
- * no x0.  Everything else as dspark_verify.
- */
-int dspark_rnn_verify(int dtype, const void* Tgt, const void* L, const void* H, const void* Bm,
-                      const int32_t* draft_tok, const float* draft_p, const double* draft_lse,
-                      const int32_t* verify_len, int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted,
-                      int32_t* out_tok, int32_t* n_out, float* target_p, void* ws, size_t ws_bytes, void* stream);
-
 const char* dspark_last_error(void);
 
 /*
@@ -112,11 +110,12 @@ size_t dspark_workspace_size(int B, int gamma, int V, int r);
  *                                 verifier: paperlayer.ai summary, section 6)
  *   draft_lse  [B][gamma] f64     out: log sum_j exp(f_j); kept in double so the
  *                                 verifier can rebuild p_d over the vocabulary
+ *   seed, seed_dev  the Philox seed (see the conventions above)
  *   ws         workspace of at least dspark_workspace_size(B, gamma, V, r) bytes
  */
 int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B, int gamma,
-                        int V, int r, uint64_t seed, int32_t* draft_tok, float* draft_p, double* draft_lse, void* ws,
-                        size_t ws_bytes, void* stream);
+                        int V, int r, uint64_t seed, const uint64_t* seed_dev, int32_t* draft_tok, float* draft_p,
+                        double* draft_lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dspark_markov_draft_conf -- dspark_markov_draft plus the Markov-conditioned
@@ -137,9 +136,9 @@ int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm,
  * must be non-null when B > 0).
  */
 int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
-                             int gamma, int V, int r, uint64_t seed, const float* z0, const void* wc,
-                             int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, void* ws,
-                             size_t ws_bytes, void* stream);
+                             int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, const float* z0,
+                             const void* wc, int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dspark_rnn_draft -- the draft steps with the RNN sequential head instead of
@@ -158,8 +157,8 @@ int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void
  *                             needs them (dspark_rnn_verify)
  */
 int dspark_rnn_draft(int dtype, const void* L, const void* A, const void* Bm, const void* Wt, const int32_t* x0, int B,
-                     int gamma, int V, int r, uint64_t seed, int32_t* draft_tok, float* draft_p, double* draft_lse,
-                     void* H, void* ws, size_t ws_bytes, void* stream);
+                     int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, int32_t* draft_tok,
+                     float* draft_p, double* draft_lse, void* H, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dspark_schedule -- confidence-scheduled verify lengths (paperlayer.ai
@@ -255,18 +254,34 @@ int dspark_schedule_threshold(const float* z, const float* temps, int B, int gam
  *   out_tok    [B][gamma+1] int32 out
  *   n_out      [B] int32 out
  *   target_p   [B][gamma] f32 out p_t(x_k) for k <= ell, 0 beyond; may be NULL
+ *   seed, seed_dev  the Philox seed; the same value as the draft's
  */
 int dspark_verify(int dtype, const void* Tgt, const void* L, const void* A, const void* Bm, const int32_t* x0,
                   const int32_t* draft_tok, const float* draft_p, const double* draft_lse, const int32_t* verify_len,
-                  int B, int gamma, int V, int r, uint64_t seed, int32_t* accepted, int32_t* out_tok, int32_t* n_out,
-                  float* target_p, void* ws, size_t ws_bytes, void* stream);
+                  int B, int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, int32_t* accepted,
+                  int32_t* out_tok, int32_t* n_out, float* target_p, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Opt-in kernel timing for measurement tools (not for production paths; not
- * thread-safe, not for use under graph capture).  dspark_profile_start
- * creates up to 2*max_launches hipEvents and from then on records an event
- * pair, on the launch stream, around every launch of the kernels whose bit is
- * set in kernel_mask (bit i = kernel id i below).
+ * dspark_rnn_verify -- dspark_verify for a draft made by dspark_rnn_draft:
+ * the residual at a rejected position k rebuilds the draft logits from the
+ * state H[b][k-1] (f = L[b][k-1] + h_k . Bm) instead of A[x_{k-1}]; there is
+ * no x0.  Everything else as dspark_verify.
+ */
+int dspark_rnn_verify(int dtype, const void* Tgt, const void* L, const void* H, const void* Bm,
+                      const int32_t* draft_tok, const float* draft_p, const double* draft_lse,
+                      const int32_t* verify_len, int B, int gamma, int V, int r, uint64_t seed,
+                      const uint64_t* seed_dev, int32_t* accepted, int32_t* out_tok, int32_t* n_out, float* target_p,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Opt-in kernel timing, for measurement tools only (benchmarks, profiling
+ * scripts; not for production paths and not for use under graph capture).
+ * Its state is process-wide (shared by all threads and devices, guarded by a
+ * lock); while it is off (the default) no call above touches it.
+ * dspark_profile_start creates up to 2*max_launches hipEvents and from then
+ * on binds an event pair to every launch of the kernels whose bit is set in
+ * kernel_mask (bit i = kernel id i below), through hipExtLaunchKernelGGL, so
+ * a pair's interval is that kernel's own execution.
  * dspark_profile_query waits for the recorded events and returns the summed
  * duration in ms and the launch count of one kernel:
  *   0 draft tiles, 1 draft locate, 2 schedule, 3 target partials, 4 accept,

@@ -62,7 +62,7 @@ MISALIGNED = ctypes.c_void_p(0x10008)
 
 
 def _draft(lib, dtype=1, B=4, gamma=5, V=1024, r=16, L=FAKE, ws_bytes=1 << 30, ptr=FAKE):
-    return lib.dspark_markov_draft(dtype, L, ptr, ptr, ptr, B, gamma, V, r, ctypes.c_uint64(1), ptr, ptr, ptr, ptr,
+    return lib.dspark_markov_draft(dtype, L, ptr, ptr, ptr, B, gamma, V, r, ctypes.c_uint64(1), None, ptr, ptr, ptr, ptr,
                                    ws_bytes, None)
 
 
@@ -87,7 +87,7 @@ def test_draft_conf_argument_errors(lib):
     f = lib.dspark_markov_draft_conf
 
     def call(z0=FAKE, wc=FAKE, z=FAKE, B=4, dtype=1):
-        return f(dtype, FAKE, FAKE, FAKE, FAKE, B, 5, 1024, 16, ctypes.c_uint64(1), z0, wc, FAKE, FAKE, FAKE, z, FAKE,
+        return f(dtype, FAKE, FAKE, FAKE, FAKE, B, 5, 1024, 16, ctypes.c_uint64(1), None, z0, wc, FAKE, FAKE, FAKE, z, FAKE,
                  1 << 30, None)
 
     assert call(z0=None) == INVALID
@@ -101,7 +101,7 @@ def test_rnn_argument_errors(lib):
     fd = lib.dspark_rnn_draft
 
     def draft(Wt=FAKE, H=FAKE, B=4, dtype=1):
-        return fd(dtype, FAKE, FAKE, FAKE, Wt, FAKE, B, 5, 1024, 16, ctypes.c_uint64(1), FAKE, FAKE, FAKE, H, FAKE,
+        return fd(dtype, FAKE, FAKE, FAKE, Wt, FAKE, B, 5, 1024, 16, ctypes.c_uint64(1), None, FAKE, FAKE, FAKE, H, FAKE,
                   1 << 30, None)
 
     assert draft(Wt=None) == INVALID
@@ -113,7 +113,7 @@ def test_rnn_argument_errors(lib):
     fv = lib.dspark_rnn_verify
 
     def verify(H=FAKE, B=4, ws_bytes=1 << 30):
-        return fv(1, FAKE, FAKE, H, FAKE, FAKE, FAKE, FAKE, FAKE, B, 5, 1024, 16, ctypes.c_uint64(1), FAKE, FAKE, FAKE,
+        return fv(1, FAKE, FAKE, H, FAKE, FAKE, FAKE, FAKE, FAKE, B, 5, 1024, 16, ctypes.c_uint64(1), None, FAKE, FAKE, FAKE,
                   None, FAKE, ws_bytes, None)
 
     assert verify(H=None) == INVALID
@@ -164,7 +164,7 @@ def test_verify_argument_errors(lib):
     def call(**kw):
         a = dict(args, **kw)
         return f(a["dtype"], a["Tgt"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["gamma"], a["V"],
-                 a["r"], ctypes.c_uint64(1), a["acc"], FAKE, FAKE, None, FAKE, a["ws_bytes"], None)
+                 a["r"], ctypes.c_uint64(1), None, a["acc"], FAKE, FAKE, None, FAKE, a["ws_bytes"], None)
 
     assert call(dtype=3) == UNSUPPORTED
     assert call(Tgt=None) == INVALID

@@ -11,11 +11,28 @@ from draft_verify_sampling_prev_amd import synth  # noqa: E402
 
 
 def test_draft_tile_bytes_and_flops_at_headline_shape():
+    """Method bytes (L rows, Bm, A rows) apart from the kernel's own partials; 2*B*r*V flops."""
     wl = synth.dsv4()
-    byts, flops = bench.draft_tiles_bytes_flops(wl)
+    method, impl, flops = bench.draft_tiles_bytes_flops(wl)
     nT = (129280 + 63) // 64
-    assert byts == 2 * (256 * 129280 + 256 * 129280 + 256 * 256) + 256 * nT * 8 + 256 * 4
+    assert method == 2 * (256 * 129280 + 256 * 129280 + 256 * 256) == 132_513_792
+    assert impl == 256 * nT * 8 + 256 * 4
     assert flops == 2.0 * 256 * 256 * 129280
+    # the fused kernel's intensity: ~128 flop per method byte, so at 8 TB/s it would run the MFMA at
+    # ~1.02 PFLOP/s, 0.41 of the 2.5 PFLOP/s bf16 peak
+    assert flops / method == pytest.approx(127.9, abs=0.1)
+    assert flops / (method / 8.0e12) / 2.5e15 == pytest.approx(0.409, abs=0.001)
+
+
+def test_acceptance_by_position():
+    acc = [0, 1, 2, 2, 5, 3]
+    ell = [5, 5, 5, 2, 5, 3]
+    a = bench.acceptance_by_position(acc, ell, 5)
+    # position 1: all six reach it, five accept; position 3: requests 2 and 4 (acc >= 2, ell >= 3)
+    # and 5 (acc 3, ell 3) reach it, requests 4 and 5 accept it
+    assert a["1"] == {"reached": 6, "accepted": round(5 / 6, 4)}
+    assert a["3"] == {"reached": 3, "accepted": round(2 / 3, 4)}
+    assert a["5"] == {"reached": 1, "accepted": 1.0}
 
 
 def test_vocab_passes_sums_and_rates():
@@ -27,7 +44,7 @@ def test_vocab_passes_sums_and_rates():
     adm, rej = 768.0, 100.0
     v = bench.vocab_passes(wl, kern, adm, rej)
     s, V, r, B = 2, wl.V, wl.r, wl.B
-    tile_b, _ = bench.draft_tiles_bytes_flops(wl)
+    tile_b, _, _ = bench.draft_tiles_bytes_flops(wl)
     expect = {"draft_tiles": tile_b, "target_partials": s * V * adm,
               "resid_tiles": s * (r * V + 2 * rej * V), "bonus_partials": s * V * (B - rej)}
     for name, b in expect.items():
