@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     DsparkError,
     dspark_markov_draft,
     dspark_markov_draft_conf,
+    dspark_markov_draft_noalloc,
     dspark_rnn_draft,
     dspark_rnn_verify,
     dspark_schedule,
@@ -26,6 +27,7 @@ __all__ = [
     "DsparkError",
     "dspark_markov_draft",
     "dspark_markov_draft_conf",
+    "dspark_markov_draft_noalloc",
     "dspark_rnn_draft",
     "dspark_rnn_verify",
     "dspark_schedule",

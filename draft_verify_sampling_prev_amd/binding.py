@@ -57,6 +57,8 @@ def load_library():
     L.dspark_markov_draft.restype = _I
     L.dspark_markov_draft.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]
+    L.dspark_markov_draft_noalloc.restype = _I
+    L.dspark_markov_draft_noalloc.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P]
     L.dspark_markov_draft_conf.restype = _I
     L.dspark_markov_draft_conf.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P,
                                            _P, _P, _P, ctypes.c_size_t, _P]
@@ -171,6 +173,33 @@ def dspark_markov_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: 
                                             *_seed(seed, dev), _ptr(tok), _ptr(p),
                                             _ptr(lse), _ptr(ws), ws.numel(), _stream(dev, stream))
     _check(rc, "dspark_markov_draft")
+    return tok, p, lse
+
+
+def dspark_markov_draft_noalloc(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor, seed,
+                                out: Optional[Tuple] = None, stream=None):
+    """dspark_markov_draft without a workspace (the library's static device scratch); allocates nothing when
+    `out` is given.  Returns (draft_tok int32 [B][g], draft_p f32 [B][g], draft_lse f64 [B][g])."""
+    dev = L.device
+    _dev(L, "L", None)
+    B, gamma, V = L.shape
+    r = A.shape[1]
+    _dev(A, "A", dev, L.dtype, (V, r))
+    _dev(Bm, "Bm", dev, L.dtype, (r, V))
+    _dev(x0, "x0", dev, torch.int32, (B,))
+    if out is None:
+        tok = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+        p = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, gamma), dtype=torch.float64, device=dev)
+    else:
+        tok, p, lse = out
+        _dev(tok, "draft_tok", dev, torch.int32, (B, gamma))
+        _dev(p, "draft_p", dev, torch.float32, (B, gamma))
+        _dev(lse, "draft_lse", dev, torch.float64, (B, gamma))
+    rc = load_library().dspark_markov_draft_noalloc(_dtype_code(L), _ptr(L), _ptr(A), _ptr(Bm), _ptr(x0), B, gamma, V,
+                                                    r, *_seed(seed, dev), _ptr(tok), _ptr(p), _ptr(lse),
+                                                    _stream(dev, stream))
+    _check(rc, "dspark_markov_draft_noalloc")
     return tok, p, lse
 
 

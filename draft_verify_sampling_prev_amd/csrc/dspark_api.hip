@@ -67,6 +67,52 @@ int cu_count()
 }
 
 // ---------------------------------------------------------------------------
+// Static scratch for the allocation-free draft entry point: the draft's tile
+// partials and A-row hand-over, in a file-scope device array.  Each device
+// that runs the library holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address is taken once per device with hipGetSymbolAddress (the
+// device current) and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(32) << 20;  // 32 MiB
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static void* g_scratch_ptr[64];
+static std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array (nullptr and *err set on failure).
+static void* scratch_address(hipError_t* err)
+{
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= 64) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// The draft's share of a workspace (the tile partials, then the A rows in
+// MFMA order); the other offsets are unused by the draft kernels.
+static WsLayout draft_layout(int B, int V)
+{
+    WsLayout l = {};
+    const size_t Bz = (size_t)(B > 0 ? B : 0);
+    l.draft_part = 0;
+    l.ag = align256(Bz * (size_t)n_tiles(1, V) * 8);
+    l.total = align256(l.ag + ((Bz + 15) / 16) * 16 * (size_t)kAgRank * 2);
+    return l;
+}
+
+// ---------------------------------------------------------------------------
 // Kernel timing (measurement only; off unless dspark_profile_start was
 // called).  The state is process-wide and guarded by a mutex; the events of
 // a pair are bound to one kernel dispatch (hipExtLaunchKernelGGL), so an
@@ -141,7 +187,7 @@ size_t dspark_workspace_size(int B, int gamma, int V, int r)
 static int markov_draft_impl(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
                              int gamma, int V, int r, SeedArg seed, const float* z0, const void* wc,
                              int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, const void* Wt,
-                             void* H, void* ws, size_t ws_bytes, void* stream)
+                             void* H, void* ws, size_t ws_bytes, void* stream, const WsLayout* layout = nullptr)
 {
     if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
     int rc = check_common(B, gamma, V, r);
@@ -151,7 +197,7 @@ static int markov_draft_impl(int dtype, const void* L, const void* A, const void
         return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
     if (!aligned16(L) || !aligned16(A) || !aligned16(Bm))
         return fail(DSPARK_ERR_INVALID_ARG, "L, A and Bm must be 16-byte aligned");
-    const WsLayout lay = ws_layout(B, gamma, V);
+    const WsLayout lay = layout ? *layout : ws_layout(B, gamma, V);
     if (ws_bytes < lay.total)
         return fail(DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, lay.total);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -170,6 +216,28 @@ int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm,
     g_err[0] = 0;
     return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, SeedArg{ seed, seed_dev }, nullptr, nullptr, draft_tok, draft_p,
                              draft_lse, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int dspark_markov_draft_noalloc(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
+                                int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, int32_t* draft_tok,
+                                float* draft_p, double* draft_lse, void* stream)
+{
+    g_err[0] = 0;
+    if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    int rc = check_common(B, gamma, V, r);
+    if (rc) return rc;
+    if (B == 0) return DSPARK_OK;
+    const WsLayout lay = draft_layout(B, V);
+    if (lay.total > kScratchBytes)
+        return fail(DSPARK_ERR_WORKSPACE, "the draft needs %zu bytes of scratch; the static scratch holds %zu", lay.total,
+                    kScratchBytes);
+    if (!L || !A || !Bm || !x0 || !draft_tok || !draft_p || !draft_lse)
+        return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    hipError_t e = hipSuccess;
+    void* ws = scratch_address(&e);
+    if (!ws) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, SeedArg{ seed, seed_dev }, nullptr, nullptr, draft_tok,
+                             draft_p, draft_lse, nullptr, nullptr, nullptr, ws, lay.total, stream, &lay);
 }
 
 int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,

@@ -118,6 +118,26 @@ int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm,
                         double* draft_lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dspark_markov_draft_noalloc -- dspark_markov_draft for callers that cannot
+ * allocate or pass device memory for a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, outputs, limits and errors as dspark_markov_draft, without
+ * ws/ws_bytes: the draft's per-tile softmax partials and its A-row hand-over
+ * live in a static device array of the library (32 MiB per device, held until
+ * the process ends), enough for B * ceil(V/64) * 8 + ceil(B/16) * 8192 bytes
+ * (e.g. B = 256 at V up to ~2M, B = 1024 at V = 129280).  Larger sizes return
+ * DSPARK_ERR_WORKSPACE with nothing enqueued.  The call allocates nothing
+ * (no hipMalloc/hipFree, no allocating library call); its first call on a
+ * device looks up that device's copy of the array.  All calls on one device
+ * share the array, whose contents need no initialisation: calls that overlap
+ * in time on one device (different streams, or different threads without
+ * ordering) race and give undefined results.
+ */
+int dspark_markov_draft_noalloc(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
+                                int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, int32_t* draft_tok,
+                                float* draft_p, double* draft_lse, void* stream);
+
+/*
  * dspark_markov_draft_conf -- dspark_markov_draft plus the Markov-conditioned
  * confidence logits, fused into the draft steps (paperlayer.ai summary,
  * Appendix A: the Markov confidence head sees the previously sampled token,

@@ -39,7 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_python_binding_has_the_same_names():
-    for n in ("dspark_markov_draft", "dspark_markov_draft_conf", "dspark_rnn_draft", "dspark_rnn_verify",
+    for n in ("dspark_markov_draft", "dspark_markov_draft_conf", "dspark_markov_draft_noalloc", "dspark_rnn_draft",
+              "dspark_rnn_verify",
               "dspark_schedule", "dspark_schedule_objective",
               "dspark_schedule_threshold",
               "dspark_verify", "dspark_workspace_size", "dspark_version"):
@@ -193,3 +194,23 @@ def test_no_cpu_fallback_in_product_path():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "dspark_oracle" not in text, fn
+
+
+def test_noalloc_draft_argument_errors(lib):
+    """The allocation-free draft validates everything, including the size of its static scratch (32 MiB),
+    before touching the device."""
+    f = lib.dspark_markov_draft_noalloc
+
+    def call(B=4, gamma=5, V=1024, r=16, dtype=1, ptr=FAKE, L=FAKE):
+        return f(dtype, L, ptr, ptr, ptr, B, gamma, V, r, ctypes.c_uint64(1), None, ptr, ptr, ptr, None)
+
+    assert call(dtype=3) == UNSUPPORTED
+    assert call(gamma=17) == UNSUPPORTED
+    assert call(V=1001) == UNSUPPORTED
+    assert call(B=-1) == INVALID
+    # B * ceil(V/64) * 8 bytes of partials beyond 32 MiB: B = 1024 at V = 600000 needs ~73 MiB
+    assert call(B=1024, gamma=8, V=600000, r=256) == WORKSPACE
+    assert b"scratch" in lib.dspark_last_error()
+    assert call(B=2048, gamma=8, V=129280, r=256) == WORKSPACE  # 2048 * 2020 * 8 bytes > 32 MiB
+    assert call(ptr=None) == INVALID
+    assert call(B=0, ptr=None, L=None) == OK
