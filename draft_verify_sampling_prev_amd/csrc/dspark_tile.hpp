@@ -76,7 +76,7 @@ __device__ __forceinline__ void dma16(const uint16_t* base, uint32_t voff, char*
 
 // DMA the Bm tile starting at column n0 into buf: 32 blocks of 8 LDS rows,
 // block w + NW*t issued by wave w (t < 32/NW, so every wave issues the same
-// number of DMA instructions).  Rows >= r and chunks past V come from clamped
+// number of DMA instructions; NW == 1: the calling wave issues them all).  Rows >= r and chunks past V come from clamped
 // (valid, finite) addresses: the A operand is zero for k >= r and columns >= V
 // are masked.  `dummy` (wave-uniform) issues the same instructions with every
 // lane reading Bm[0][0..7], for pipelines that keep a fixed number of
@@ -89,7 +89,9 @@ __device__ __forceinline__ void dma_bm_tile(const uint16_t* __restrict__ Bm, int
 {
     n0 = __builtin_amdgcn_readfirstlane(n0);
     dummy = __builtin_amdgcn_readfirstlane((int)dummy) != 0;
-    const int w = wave_id(), lane = threadIdx.x & 63;
+    // With NW == 1 the calling wave issues all 32 blocks, whichever wave of
+    // its workgroup it is.
+    const int w = NW == 1 ? 0 : wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
     for (int t = 0; t < 32 / NW; ++t) {
         const int blk = w + NW * t;
