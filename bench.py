@@ -56,19 +56,6 @@ def draft_tiles_bytes_flops(wl) -> tuple:
     return method, impl, flops
 
 
-def draft_persistent_bytes_flops(wl) -> tuple:
-    """Per launch of the persistent draft kernel (all gamma draft steps):
-    method bytes -- the gamma steps' L rows (gamma*B*V), Bm once (r*V: it stays on chip across the steps) and
-    the gathered A rows (gamma*B*r), s bytes each; implementation bytes -- the per-(row, tile) partials written
-    and read back (2 * 8 bytes per row and tile per step) and the tokens; flops -- 2*gamma*B*r*V."""
-    s = 2
-    nT = (wl.V + 63) // 64
-    method = s * (wl.gamma * wl.B * wl.V + wl.r * wl.V + wl.gamma * wl.B * wl.r)
-    impl = wl.gamma * (2 * wl.B * nT * 8 + wl.B * 4)
-    flops = 2.0 * wl.gamma * wl.B * wl.r * wl.V
-    return method, impl, flops
-
-
 # The draft tile kernel's translation unit: the source and every header it includes.
 DRAFT_TILE_SOURCES = ("dspark_device.hpp", "dspark_draft.hip", "dspark_internal.hpp", "dspark_locate.hpp",
                       "dspark_markov.hpp", "dspark_tile.hpp")
@@ -78,15 +65,14 @@ def vocab_passes(wl, kern: dict, adm: float, rej: float) -> dict:
     """HBM fraction of the vocabulary passes and MFMA fraction of the rank-r contraction, per step.
 
     Algorithmic bytes (the method's minimum, s bytes per element): draft tiles, per launch the step's L rows,
-    Bm and the A rows; the persistent draft, per launch the gamma steps' L rows, Bm once and the A rows; target rows, s*V per verified draft (adm per step); residual tiles,
+    Bm and the A rows; target rows, s*V per verified draft (adm per step); residual tiles,
     Bm plus the target row and the draft-L row of each request with a rejection (rej per step); bonus rows,
     s*V per request without one.  Flops: 2*r*V per draft row and per residual row.  Times are the per-kernel
     averages of the timed pass (events bound to each kernel's own dispatch)."""
     s = 2 if wl.dtype == "bf16" else 4
     B, V, r, gamma = wl.B, wl.V, wl.r, wl.gamma
     tile_b, _, _ = draft_tiles_bytes_flops(wl)
-    pers_b, _, _ = draft_persistent_bytes_flops(wl)
-    per_launch = {"draft_tiles": tile_b, "draft_persistent": pers_b, "target_partials": s * V * adm,
+    per_launch = {"draft_tiles": tile_b, "target_partials": s * V * adm,
                   "resid_tiles": s * (r * V + 2 * rej * V), "bonus_partials": s * V * (B - rej)}
     out = {}
     tot_b = tot_us = 0.0
@@ -103,10 +89,9 @@ def vocab_passes(wl, kern: dict, adm: float, rej: float) -> dict:
         gbs = tot_b / (tot_us * 1e-6) / 1e9
         out["all"] = {"bytes_per_step": int(tot_b), "us_per_step": round(tot_us, 2), "GB/s": round(gbs, 1),
                       "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    draft_k = "draft_persistent" if "draft_persistent" in kern else "draft_tiles"
-    if draft_k in kern and "resid_tiles" in kern:
+    if "draft_tiles" in kern and "resid_tiles" in kern:
         flops = 2.0 * r * V * (gamma * B + rej)
-        us = kern[draft_k]["avg_us"] * kern[draft_k]["launches_per_step"] + kern["resid_tiles"]["avg_us"]
+        us = kern["draft_tiles"]["avg_us"] * kern["draft_tiles"]["launches_per_step"] + kern["resid_tiles"]["avg_us"]
         tf = flops / (us * 1e-6) / 1e12
         peak = BF16_MFMA_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
         out["markov_mfma"] = {"flops_per_step": flops, "us_per_step": round(us, 2), "TFLOP/s": round(tf, 1),
@@ -128,11 +113,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str = "draft_tiles"):
-    """HBM bytes per launch of the roofline kernel (draft_tiles or draft_persistent) from the committed
-    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), if it was taken
-    on the current kernel sources; None otherwise."""
-    path = os.path.join(ROOT, "profiles", f"k_{kernel}_{workload}_traffic.json")
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the draft tile kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), if it was taken on the current
+    kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"k_draft_tiles_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -343,7 +328,7 @@ def main():
     # to every dispatch of the dominant kernel (draft Markov tiles) through
     # hipExtLaunchKernelGGL on the stream it runs on, so each interval is the
     # kernel's own execution.
-    binding.profile_start(max_launches=K * gamma + 16, kernels=("draft_tiles", "draft_persistent"))
+    binding.profile_start(max_launches=K * gamma + 16, kernels=("draft_tiles",))
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -353,11 +338,7 @@ def main():
     torch.cuda.synchronize()
     binding.profile_stop()
     ms_step_instr = e0.elapsed_time(e1) / K
-    roof_kernel = "draft_tiles"
     tiles_ms, tiles_n = binding.profile_query("draft_tiles")
-    pers_ms, pers_n = binding.profile_query("draft_persistent")
-    if pers_n:
-        roof_kernel, tiles_ms, tiles_n = "draft_persistent", pers_ms, pers_n
 
     # Per-kernel averages (separate pass, every kernel timed) for context, and
     # the verify lengths / accepted counts of those steps.
@@ -419,26 +400,10 @@ def main():
                  "note": "HIP-graph replay of the whole step (seed in device memory, advanced in the graph); "
                          "tokens/s = the eager timed steps' mean emitted tokens per step / replay time"}
 
-    if roof_kernel == "draft_persistent":
-        method_b, impl_b, flops = draft_persistent_bytes_flops(wl)
-        roof = {"kernel": "persistent draft, all gamma steps in one cooperative launch (k_draft_persistent_bf16)",
-                "algorithmic_bytes": "the gamma steps' L rows gamma*B*V + Bm r*V (read once; held on chip) + "
-                                     "gathered A rows gamma*B*r, 2 bytes each",
-                "implementation_bytes": "per-(row, 64-column tile) softmax partials written and read back "
-                                        "(2 x 8 bytes per step) + tokens; not counted in achieved",
-                "timing": f"HIP event pair recorded on the stream around each cooperative launch, over a second "
-                          f"pass of the same {K} steps ({round(ms_step_instr, 4)} ms per step in that pass)"}
-    else:
-        method_b, impl_b, flops = draft_tiles_bytes_flops(wl)
-        roof = {"kernel": "draft Markov tiles (k_draft_tiles)",
-                "algorithmic_bytes": "the step's L rows B*V + Bm r*V + gathered A rows B*r, 2 bytes each",
-                "implementation_bytes": "per-(row, 64-column tile) softmax partials written (8 bytes) + tokens; "
-                                        "not counted in achieved",
-                "timing": f"HIP event pairs bound to each dispatch (hipExtLaunchKernelGGL), over a second "
-                          f"pass of the same {K} steps ({round(ms_step_instr, 4)} ms per step in that pass)"}
+    method_b, impl_b, flops = draft_tiles_bytes_flops(wl)
     avg_s = tiles_ms / max(tiles_n, 1) / 1000.0
     achieved = method_b / avg_s / 1e9
-    tr = measured_traffic(wl.name, roof_kernel)
+    tr = measured_traffic(wl.name)
     result = {
         "metric": "draft+verify tokens/s at B=256,V=129280,gamma=5 (emitted tokens per step time)",
         "value": round(value, 1),
@@ -460,18 +425,20 @@ def main():
                    + (", RNN sequential head" if args.head == "rnn" else ""),
                    "emitted_per_step": round(emitted / K, 2), "verified_per_step": int(ell.sum().item()),
                    "accumulation": "fp32 MFMA, fp64 softmax masses"},
-        "roofline": {"kernel": roof["kernel"], "bound": "hbm",
+        "roofline": {"kernel": "draft Markov tiles (k_draft_tiles)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (tr["bytes_per_launch"] if tr else None),
                      "traffic_source": (tr["source"] if tr else "no counter summary for the current kernel sources"),
                      "algorithmic_bytes_per_launch": method_b,
-                     "algorithmic_bytes": roof["algorithmic_bytes"],
+                     "algorithmic_bytes": "the step's L rows B*V + Bm r*V + gathered A rows B*r, 2 bytes each",
                      "implementation_bytes_per_launch": impl_b,
-                     "implementation_bytes": roof["implementation_bytes"],
+                     "implementation_bytes": "per-(row, 64-column tile) softmax partials written (8 bytes) + tokens; "
+                                             "not counted in achieved",
                      "avg_launch_us": round(avg_s * 1e6, 3),
                      "launches": tiles_n,
-                     "timing": roof["timing"],
+                     "timing": f"HIP event pairs bound to each dispatch (hipExtLaunchKernelGGL), over a second "
+                               f"pass of the same {K} steps ({round(ms_step_instr, 4)} ms per step in that pass)",
                      "mfma_tflops": round(flops / avg_s / 1e12, 2),
                      "mfma_frac": round(flops / avg_s / 1e12 / (BF16_MFMA_PEAK_TFLOPS if wl.dtype == "bf16"
                                                                else FP32_MFMA_PEAK_TFLOPS), 4)},

@@ -23,7 +23,7 @@ _LIB_PATH = os.environ.get("DSPARK_LIB") or os.path.join(_PKG, "libdspark.so")
 
 # Kernel ids for dspark_profile_query.
 KERNELS = ("draft_tiles", "draft_locate", "schedule", "target_partials", "accept", "resid_tiles",
-           "bonus_partials", "final", "draft_persistent")
+           "bonus_partials", "final")
 
 
 class DsparkError(RuntimeError):
@@ -77,10 +77,6 @@ def load_library():
     L.dspark_verify.restype = _I
     L.dspark_verify.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P,
                                 _P, _P, _P, ctypes.c_size_t, _P]
-    L.dspark_draft_status.restype = _I
-    L.dspark_draft_status.argtypes = [_P, _I, _I, _I, _I, _P]
-    L.dspark_debug_draft.restype = _I
-    L.dspark_debug_draft.argtypes = [_I, ctypes.c_uint, ctypes.c_uint]
     L.dspark_profile_start.restype = _I
     L.dspark_profile_start.argtypes = [_I, ctypes.c_uint]
     L.dspark_profile_stop.restype = _I
@@ -410,21 +406,6 @@ def dspark_rnn_verify(Tgt: torch.Tensor, L: torch.Tensor, H: torch.Tensor, Bm: t
                                           _ptr(n_out), _ptr(tp), _ptr(ws), ws.numel(), _stream(dev, stream))
     _check(rc, "dspark_rnn_verify")
     return acc, out_tok, n_out, tp
-
-
-def dspark_draft_status(B: int, gamma: int, V: int, r: int, ws: Optional[torch.Tensor] = None, device=None,
-                        stream=None) -> None:
-    """Raise DsparkError if the last draft on `ws` (None: the static scratch of the allocation-free draft)
-    gave up at a device-wide barrier; synchronises the stream."""
-    dev = ws.device if ws is not None else (device or torch.device("cuda", torch.cuda.current_device()))
-    rc = load_library().dspark_draft_status(_ptr(ws), B, gamma, V, r, _stream(dev, stream))
-    _check(rc, "dspark_draft_status")
-
-
-def debug_draft(per_step_only: bool = False, phantom_arrivals: int = 0, poll_limit: int = 0) -> None:
-    """Test hook (process-wide): force per-step drafts, or make the persistent draft's barriers give up."""
-    _check(load_library().dspark_debug_draft(int(per_step_only), int(phantom_arrivals), int(poll_limit)),
-           "dspark_debug_draft")
 
 
 # ----------------------------------------------------------------------------- timing (measurement tools)

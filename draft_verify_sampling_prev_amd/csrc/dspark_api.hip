@@ -48,7 +48,6 @@ WsLayout ws_layout(int B, int gamma, int V)
     l.bon_m = take(Bz * nC * 4);
     l.bon_s = take(Bz * nC * 8);
     l.ag = take(((Bz + 15) / 16) * 16 * (size_t)kAgRank * 2);
-    l.sync = take(8);
     l.total = o;
     return l;
 }
@@ -109,8 +108,7 @@ static WsLayout draft_layout(int B, int V)
     const size_t Bz = (size_t)(B > 0 ? B : 0);
     l.draft_part = 0;
     l.ag = align256(Bz * (size_t)n_tiles(1, V) * 8);
-    l.sync = align256(l.ag + ((Bz + 15) / 16) * 16 * (size_t)kAgRank * 2);
-    l.total = align256(l.sync + 8);
+    l.total = align256(l.ag + ((Bz + 15) / 16) * 16 * (size_t)kAgRank * 2);
     return l;
 }
 
@@ -203,15 +201,9 @@ static int markov_draft_impl(int dtype, const void* L, const void* A, const void
     if (ws_bytes < lay.total)
         return fail(DSPARK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, lay.total);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (persistent_draft_applies(dtype, B, V, r, H, s))
-        return hip_status(launch_draft_persistent(L, A, Bm, x0, B, gamma, V, r, seed, draft_tok, draft_p, draft_lse, z0,
-                                                  wc, z_out, ws, lay, s),
-                          "persistent draft launch");
-    hipError_t e = launch_clear_sync(ws, lay, s);
-    if (e != hipSuccess) return hip_status(e, "draft launch");
     for (int k = 1; k <= gamma; ++k) {
-        e = launch_draft_step(dtype, L, A, Bm, x0, B, gamma, V, r, k, seed, draft_tok, draft_p, draft_lse, z0, wc,
-                              z_out, Wt, H, ws, lay, s);
+        hipError_t e = launch_draft_step(dtype, L, A, Bm, x0, B, gamma, V, r, k, seed, draft_tok, draft_p, draft_lse,
+                                         z0, wc, z_out, Wt, H, ws, lay, s);
         if (e != hipSuccess) return hip_status(e, "draft launch");
     }
     return DSPARK_OK;
@@ -370,40 +362,6 @@ int dspark_rnn_verify(int dtype, const void* Tgt, const void* L, const void* H, 
     return verify_impl(dtype, Tgt, L, H, Bm, nullptr, draft_tok, draft_p, draft_lse, verify_len, B, gamma, V, r,
                        SeedArg{ seed, seed_dev },
                        accepted, out_tok, n_out, target_p, H, ws, ws_bytes, stream);
-}
-
-int dspark_draft_status(const void* ws, int B, int gamma, int V, int r, void* stream)
-{
-    g_err[0] = 0;
-    int rc = check_common(B, gamma, V, r);
-    if (rc) return rc;
-    if (B == 0) return DSPARK_OK;
-    const char* base = static_cast<const char*>(ws);
-    WsLayout lay;
-    if (ws) {
-        lay = ws_layout(B, gamma, V);
-    } else {
-        lay = draft_layout(B, V);
-        if (lay.total > kScratchBytes) return fail(DSPARK_ERR_WORKSPACE, "sizes beyond the static scratch");
-        hipError_t e = hipSuccess;
-        base = static_cast<const char*>(scratch_address(&e));
-        if (!base) return hip_status(e, "hipGetSymbolAddress(scratch)");
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    unsigned words[2] = { 0u, 0u };
-    hipError_t e = hipStreamSynchronize(s);
-    if (e == hipSuccess) e = hipMemcpy(words, base + lay.sync, sizeof(words), hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return hip_status(e, "reading the draft status");
-    if (words[1] != 0u)
-        return fail(DSPARK_ERR_SYNC, "the persistent draft's device-wide barrier gave up; its outputs are invalid");
-    return DSPARK_OK;
-}
-
-int dspark_debug_draft(int per_step_only, unsigned phantom_arrivals, unsigned poll_limit)
-{
-    g_err[0] = 0;
-    set_draft_test_mode(per_step_only != 0, phantom_arrivals, poll_limit);
-    return DSPARK_OK;
 }
 
 int dspark_profile_start(int max_launches, unsigned kernel_mask)

@@ -26,7 +26,6 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "dspark_gridsync.hpp"
 #include "dspark_internal.hpp"
 #include "dspark_locate.hpp"
 #include "dspark_markov.hpp"
@@ -610,417 +609,6 @@ __global__ __launch_bounds__(kMaxRank) void k_rnn_state(const typename DT::T* __
         }
         hout[t] = store_elem(DT{}, tanhf(pre));
     }
-}
-
-// ---------------------------------------------------------------------------
-// bf16, rank 256, B <= one request per compute unit: all gamma draft steps in
-// one persistent launch with the Markov factor Bm resident on chip.
-//
-// One workgroup of 8 waves per compute unit (a cooperative launch, so all
-// are resident at once).  Wave w of workgroup g owns the 64-column tile
-// t = 8g + w and keeps its Bm^T fragments -- the MFMA A operand for all 256 k,
-// 128 VGPRs -- in registers for the whole launch: Bm is read from HBM once per
-// call instead of once per draft step.  Per step k:
-//   tiles   each wave streams its tile's L values row block by row block (16
-//           rows, several blocks in flight), takes the rows' A vectors (the
-//           MFMA B operand) from the workgroup's LDS copy "Ag" (k step ks of
-//           block bb is 1 KB contiguous, one 16-byte read per lane), and
-//           leaves each row's tile max and sum of exp in LDS; the workgroup
-//           writes its tiles' partials, one 64-byte run per row.  The MFMA
-//           sequence, accumulator start values and epilogue are those of
-//           k_draft_tiles_bf16, so the partials are the same bits.
-//   barrier (device-wide, bounded wait) every partial is visible.
-//   locate  wave 0 of workgroup b samples request b exactly as the one-wave
-//           locate kernel does (same partial combination, same recompute of
-//           the chosen tile), so the tokens, p_d and lse_d equal the per-step
-//           path's.  Its Bm fragments are not live meanwhile: the wave DMAs
-//           its Bm tile into LDS alongside the locate and reads the fragments
-//           back afterwards, so the locate has the register file to itself.
-//   barrier every token is visible.
-//   Ag      every workgroup gathers A[x_k] of every row into LDS in MFMA
-//           operand order for step k+1.
-// A barrier that gives up (it cannot while all workgroups are resident) sets
-// the error word and every workgroup returns; the outputs are then invalid
-// and dspark_draft_status reports it.
-// ---------------------------------------------------------------------------
-constexpr int kPW = 4;                            // waves per workgroup (one per SIMD), two tiles each
-constexpr int kPTiles = 2 * kPW;                  // 64-column tiles per workgroup
-constexpr int kPRows = 256;                       // batch rows the LDS copy of the A rows holds
-constexpr int kPAgBytes = kPRows * kAgRank * 2;   // 128 KB
-
-// Data that crosses workgroups inside the launch (the partials, the tokens)
-// is written and read with agent-scope atomic accesses, which go to the
-// device-coherent level directly (past the per-XCD L2), so the barrier needs
-// no cache write-back or invalidation -- both would walk the whole L2 of
-// every XCD at every barrier, and every access after them would miss.
-__device__ __forceinline__ void store_coherent(float2* p, float2 v)
-{
-    const unsigned long long u = pack_f2(v.x, v.y);
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 load_coherent(const float2* p)
-{
-    return unpack_f2(__hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ void store_coherent(int32_t* p, int32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t load_coherent(const int32_t* p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The barrier's atomic operations: all relaxed at agent scope.  Ordering
-// comes from the waits around them: every wave waits for its own coherent
-// stores to complete before its workgroup arrives, and the accesses after
-// the barrier are issued only after the waiter has seen the count.
-struct AgentSyncOps {
-    unsigned* ctr;
-    unsigned* err;
-    __device__ void arrive() { __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-    __device__ unsigned count() { return __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-    __device__ void acquire() {}
-    __device__ bool failed() { return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u; }
-    __device__ void fail() { __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-    __device__ void pause() { __builtin_amdgcn_s_sleep(1); }
-};
-
-// Every wave of the workgroup calls.  A workgroup barrier does not wait for
-// the waves' outstanding stores, so each wave first waits for its own
-// (coherent stores: complete = visible at agent scope); then thread 0 arrives
-// and waits.  Returns false when the wait gave up.
-__device__ __forceinline__ bool grid_barrier(AgentSyncOps& ops, unsigned target, unsigned limit, int* sh_ok)
-{
-    wait_all_mem();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        *sh_ok = gridsync_arrive_and_wait(ops, target, limit) ? 1 : 0;
-        wait_all_mem();  // the poll has returned before anything after the barrier is issued
-    }
-    __syncthreads();
-    return *sh_ok != 0;
-}
-
-__global__ __launch_bounds__(64) void k_zero_words(unsigned* p, int n)
-{
-    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
-}
-
-template <int PER>
-__global__ __launch_bounds__(64 * kPW, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_draft_persistent_bf16(
-    const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
-    const int32_t* __restrict__ x0, int32_t* tok, float* p_out, double* lse_out, float2* part, unsigned* sync,
-    int B, int gamma, int V, int nT, SeedArg seed_arg, ConfOut co, unsigned limit, unsigned arrivals)
-{
-    __shared__ __attribute__((aligned(1024))) char agl[kPAgBytes];
-    __shared__ unsigned long long stage[kPTiles][kPRows];  // (tile max, sum of exp) per tile and row
-    __shared__ double scr[64];
-    __shared__ int sh_tok[kPRows];
-    __shared__ int sh_ok;
-
-    const uint64_t seed = seed_of(seed_arg);
-    const int g = blockIdx.x;
-    const int w = wave_id(), lane = threadIdx.x & 63, c = lane & 15;
-    // This wave's tiles: 8g + 2w and 8g + 2w + 1 (clamped for waves past the
-    // vocabulary: their loads stay in bounds, their results are not kept).
-    int n0[2];
-    bool has[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int t = g * kPTiles + 2 * w + j;
-        has[j] = t < nT;
-        n0[j] = min(t, nT - 1) * kTcols;
-    }
-    const int nBB = (B + 15) >> 4;  // 16-row blocks
-    AgentSyncOps ops{ sync, sync + 1 };
-    unsigned passed = 0;            // device-wide barriers passed
-
-    // Prologue: the Bm fragments of both tiles, one tile per wave at a time
-    // through its own 32 KB LDS buffer (each wave waits for its own DMA).
-    int off[4];
-    bm_lane_offsets(off);
-    bf16x8 bmf[2][4][8];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        char* buf = agl + w * kBmTileBytes;
-        dma_bm_tile<1>(Bm, V, kAgRank, n0[j], false, buf);
-        wait_all_mem();
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-            for (int vb = 0; vb < 4; ++vb) bmf[j][vb][ks] = bm_frag(buf, off, ks, vb);
-        __syncthreads();
-    }
-
-    // The rows' A vectors for step k in MFMA B-operand order (Ag layout):
-    // each row's token is read once into LDS, then thread piece q = (row,
-    // 16-byte piece), 32 consecutive threads per row; rows past the batch
-    // repeat the last row (never reported).
-    auto build_ag = [&](int k) {
-        {
-            const int Rc = min((int)threadIdx.x, B - 1);
-            sh_tok[threadIdx.x] = clamp_token(k == 1 ? x0[Rc] : load_coherent(tok + Rc * gamma + (k - 2)), V);
-        }
-        __syncthreads();
-        int tq = (int)threadIdx.x;
-        asm volatile("" : "+v"(tq));  // (keeps the piece addresses inside the step loop)
-        // Thread tq takes pieces q = tq + 256 i: row (tq >> 5) + 8 i, piece tq & 31.
-        // Tokens first, then the loads of a group of rows, then their stores
-        // (an LDS token read cannot move above an earlier LDS store).
-        constexpr int kRowsPerThread = kPRows * 32 / (64 * kPW);  // 32
-        const int pc = tq & 31, R0 = tq >> 5;
-        int xr[kRowsPerThread];
-#pragma unroll
-        for (int i = 0; i < kRowsPerThread; ++i) xr[i] = sh_tok[R0 + 8 * i];
-#pragma unroll
-        for (int i0 = 0; i0 < kRowsPerThread; i0 += 8) {
-            uint4 v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = ld16(A + (size_t)xr[i0 + i] * kAgRank + 8 * pc);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<uint4*>(agl + 2 * ag_offset(R0 + 8 * (i0 + i), pc >> 2, pc & 3)) = v[i];
-        }
-    };
-    build_ag(1);
-    __syncthreads();
-
-    for (int k = 1; k <= gamma; ++k) {
-        // --- tiles ---
-        if (has[0]) {
-            // L through a buffer resource at the step's first tile of this
-            // wave: per lane and tile, two 16-byte pieces of row R at byte
-            // offset R * gamma * V * 2 + colb[j][h] (32-bit offsets; B * gamma
-            // * V * 2 < 2^31 here).  The second tile's pieces are clamped into
-            // the vocabulary like the first's.
-            const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(L + (size_t)(k - 1) * V + n0[0]), (short)0, 0x7FFFFFFF, 0x00020000);
-            const uint32_t rowb = (uint32_t)gamma * (uint32_t)V * 2u;
-            uint32_t colb[2][2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    colb[j][h] = 2u * (uint32_t)(min(n0[j] + 16 * (lane >> 4) + 8 * h, V - 8) - n0[0]);
-            auto issue = [&](int bb, uint4 (&dst)[2][2]) {
-                const uint32_t ro = (uint32_t)min(16 * bb + c, B - 1) * rowb;
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        dst[j][h] = __builtin_bit_cast(
-                            uint4, __builtin_amdgcn_raw_buffer_load_b128(lrs, ro + colb[j][h], 0, 0));
-            };
-            auto compute = [&](int bb, const uint4 (&lv)[2][2]) {
-                floatx4 acc[2][4];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int vb = 0; vb < 4; ++vb) acc[j][vb] = bf16x4_to_f32(row16_block(lv[j], vb));
-                const char* ab = agl + (size_t)bb * 8 * 1024 + lane * 16;
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8 bop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ab + ks * 1024));
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int vb = 0; vb < 4; ++vb)
-                            acc[j][vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bmf[j][vb][ks], bop, acc[j][vb],
-                                                                                0, 0, 0);
-                }
-                // The masked form for every tile: columns at or past V count as
-                // absent, and a full tile (V - n0 >= 64) masks nothing, so the
-                // bits are those of the unmasked form, without a branch.
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    float m, sum;
-                    row64_max_sum<true>(acc[j], V - n0[j], &m, &sum);
-                    stage[2 * w + j][16 * bb + c] = pack_f2(m, sum);
-                }
-            };
-            // L values kPAhead row blocks ahead, in a rotation of register sets
-            // (kPAhead + 1 bodies per loop iteration, each with fixed
-            // registers).  Every block issues its loads -- blocks past the
-            // batch re-read the last one -- so a fixed number of loads is in
-            // flight behind a block's own.
-            constexpr int kPAhead = 3;
-            uint4 lv[kPAhead + 1][2][2];
-#pragma unroll
-            for (int i = 0; i < kPAhead; ++i) issue(min(i, nBB - 1), lv[i]);
-            for (int bb0 = 0; bb0 < nBB; bb0 += kPAhead + 1) {
-#pragma unroll
-                for (int u = 0; u <= kPAhead; ++u) {
-                    const int bb = bb0 + u;
-                    issue(min(bb + kPAhead, nBB - 1), lv[(u + kPAhead) % (kPAhead + 1)]);
-                    if (bb < nBB) compute(bb, lv[u]);
-                }
-            }
-        }
-        __syncthreads();
-        // This workgroup's partials: row R's tiles 8g .. 8g+7 are one 64-byte run.
-        for (int e = threadIdx.x; e < kPRows * kPTiles; e += 64 * kPW) {
-            const int row = e >> 3, j = e & 7, tt = g * kPTiles + j;
-            if (row < B && tt < nT) store_coherent(part + (size_t)row * nT + tt, unpack_f2(stage[j][row]));
-        }
-        if (!grid_barrier(ops, ++passed * arrivals, limit, &sh_ok)) return;
-
-        // --- locate: wave 0 of workgroup b samples request b ---
-        if (w == 0 && g < B) {
-            const int b = g;
-            char* lds_tile = agl;  // the chosen tile's Bm for the recompute
-            const float2* pr = part + (size_t)b * nT;
-            float2 q[PER];
-            int i0;
-            {   // load_slices with coherent loads
-                const int per = (nT + 63) / 64;
-                i0 = lane * per;
-                // (opaque per step: addresses that do not depend on k would be
-                // hoisted out of the step loop and kept -- spilled -- across it)
-                asm volatile("" : "+v"(i0));
-#pragma unroll
-                for (int j = 0; j < PER; ++j) {
-                    const float2 v = load_coherent(pr + min(i0 + j, nT - 1));
-                    q[j] = (j < per && i0 + j < nT) ? v : make_float2(-INFINITY, 0.0f);
-                }
-            }
-            const int prev = clamp_token(k == 1 ? x0[b] : load_coherent(tok + b * gamma + (k - 2)), V);
-            uint4 a[1][8];
-            {
-                const uint16_t* arow[1] = { A + (size_t)prev * kAgRank };
-                load_a_frags<1>(arow, kAgRank, a);
-            }
-            uint4 wcf[8];
-            if (co.z) {
-                const uint16_t* wc = static_cast<const uint16_t*>(co.wc);
-                const int kq8 = 8 * (lane >> 4);
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks) wcf[ks] = ld16(wc + 32 * ks + kq8);
-            }
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < PER; ++j) mloc = fmaxf(mloc, q[j].x);
-            const float M = wave_max(mloc);
-            const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)k, 0u);
-            const Located loc = wave_locate_slices<PER>(
-                i0, [&](int j) { return tile_mass(q[j].x, (double)q[j].y, M); }, u, scr);
-            const int n0l = loc.idx * kTcols;
-            const float mt = load_coherent(pr + loc.idx).x;
-            floatx4 f[4];
-            row_tile_vm_wave<8>(L + ((size_t)b * gamma + (k - 1)) * V, a, Bm, V, kAgRank, n0l, lds_tile, f);
-            if (co.z) {
-                float sdot = 0.0f;
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        sdot = __builtin_fmaf(Bf16::get(a[0][ks], e), Bf16::get(wcf[ks], e), sdot);
-                sdot = sum_xor16_32(sdot);
-                if (lane == 0) co.z[b * gamma + (k - 1)] = co.z0[b * gamma + (k - 1)] + sdot;
-            }
-            const double scale = tile_mass(mt, 1.0, M);
-            const float ml = row_mlog2(mt);
-            double wsel;
-            const int j = scan_row_tile_lanes(
-                n0l, scale, loc.cprev, loc.tau,
-                [&](int col, auto pick) {
-                    return col < V && mt != -INFINITY ? (double)softmax_w(pick(f), ml) : 0.0;
-                },
-                &wsel);
-            const int xk = min(n0l + j, V - 1);
-            if (lane == 0) {
-                store_coherent(tok + b * gamma + (k - 1), xk);
-                p_out[b * gamma + (k - 1)] = (float)(scale * wsel / loc.S);
-                lse_out[b * gamma + (k - 1)] = (double)M + log(loc.S);
-            }
-        }
-        if (k == gamma) break;
-        if (!grid_barrier(ops, ++passed * arrivals, limit, &sh_ok)) return;
-        build_ag(k + 1);
-        __syncthreads();
-    }
-}
-
-// Persistent draft: whether it applies, and the launch (cooperative, after a
-// one-wave kernel has cleared the barrier counter and error word).
-struct PersistentDevice {
-    int checked = 0;
-    int ok = 0;
-};
-static PersistentDevice g_persistent[64];
-
-static bool persistent_supported()
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-    PersistentDevice& d = g_persistent[dev];
-    if (!d.checked) {
-        int coop = 0, nb = 0;
-        const bool attr = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess;
-        const bool occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                             &nb, reinterpret_cast<const void*>(&k_draft_persistent_bf16<32>), 64 * kPW, 0) ==
-                         hipSuccess;
-        d.ok = attr && occ && coop && nb >= 1;
-        d.checked = 1;
-    }
-    return d.ok != 0;
-}
-
-static unsigned g_barrier_limit = 1u << 22;    // polls of a waiter before it gives up (about a second)
-static unsigned g_barrier_phantom = 0u;        // extra arrivals a barrier waits for (tests of the give-up path)
-static bool g_per_step_only = true;            // the persistent draft measured slower: off unless a test enables it
-
-void set_draft_test_mode(bool per_step_only, unsigned phantom, unsigned limit)
-{
-    g_per_step_only = per_step_only;
-    g_barrier_phantom = phantom;
-    g_barrier_limit = limit ? limit : (1u << 22);
-}
-
-hipError_t launch_clear_sync(void* ws, const WsLayout& lay, hipStream_t s)
-{
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s,
-                       reinterpret_cast<unsigned*>(static_cast<char*>(ws) + lay.sync), 2);
-    return hipGetLastError();
-}
-
-bool persistent_draft_applies(int dtype, int B, int V, int r, const void* H, hipStream_t s)
-{
-    if (g_per_step_only || dtype != 1 || r != kAgRank || H || B < 1) return false;
-    const int cus = cu_count();
-    if (B > cus || B > kPRows || n_tiles(1, V) > kPTiles * cus) return false;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
-    return persistent_supported();
-}
-
-hipError_t launch_draft_persistent(const void* L_, const void* A_, const void* Bm_, const int32_t* x0, int B, int gamma,
-                                   int V, int r, SeedArg seed, int32_t* tok, float* p, double* lse, const float* z0,
-                                   const void* wc, float* z_out, void* ws, const WsLayout& lay, hipStream_t s)
-{
-    (void)r;
-    const uint16_t* L = static_cast<const uint16_t*>(L_);
-    const uint16_t* A = static_cast<const uint16_t*>(A_);
-    const uint16_t* Bm = static_cast<const uint16_t*>(Bm_);
-    float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.draft_part);
-    unsigned* sync = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + lay.sync);
-    int nT = n_tiles(1, V);
-    ConfOut co{ z0, wc, z_out };
-    unsigned limit = g_barrier_limit;
-    const int nG = cu_count();
-    unsigned arrivals = (unsigned)nG + g_barrier_phantom;
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, s, sync, 2);
-    void* args[] = { (void*)&L, (void*)&A, (void*)&Bm, (void*)&x0, (void*)&tok, (void*)&p, (void*)&lse,
-                     (void*)&part, (void*)&sync, (void*)&B, (void*)&gamma, (void*)&V, (void*)&nT, (void*)&seed,
-                     (void*)&co, (void*)&limit, (void*)&arrivals };
-    const ProfPair e = prof_pair(K_DRAFT_PERSISTENT);
-    if (e.start) (void)hipEventRecord(e.start, s);
-    hipError_t err = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_draft_persistent_bf16<32>), dim3(nG),
-                                                dim3(64 * kPW), args, 0, s);
-    if (e.stop) (void)hipEventRecord(e.stop, s);
-    if (err != hipSuccess) return err;
-    return hipGetLastError();
 }
 
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,

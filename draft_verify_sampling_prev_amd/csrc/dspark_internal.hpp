@@ -34,7 +34,6 @@ struct WsLayout {
     size_t res_part;              // [B][nT] float2 : per tile sum of max(0, p_t - p_d) and of p_t
     size_t bon_m, bon_s;          // [B][nC] f32 / f64 : bonus-row chunk max and sum of exp
     size_t ag;                    // [ceil(B/16)*16][256] bf16 : the next draft step's A rows, MFMA order (rank 256)
-    size_t sync;                  // [2] u32 : device-wide barrier counter and error word of the draft
     size_t total;
 };
 
@@ -62,7 +61,6 @@ enum KernelId {
     K_RESID_TILES,
     K_BONUS_PARTIALS,
     K_FINAL,
-    K_DRAFT_PERSISTENT,
     K_COUNT
 };
 // Persistent slots per row block of a tile pass over nT tiles with nM row
@@ -110,22 +108,6 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
                              int B, int gamma, int V, int r, int k, SeedArg seed, int32_t* tok, float* p,
                              double* lse, const float* z0, const void* wc, float* z_out, const void* Wt, void* H,
                              void* ws, const WsLayout& lay, hipStream_t s);
-
-// Persistent draft (bf16, rank 256, B <= compute units, V <= 512 * compute
-// units, Markov head, eager launches): all gamma steps in one cooperative
-// launch with Bm resident on chip.  persistent_draft_applies says whether
-// the call qualifies; launch_draft_persistent clears the barrier words and
-// launches.  set_draft_test_mode (tests only) forces the per-step path, or
-// makes the device-wide barrier wait for `phantom` arrivals that never come,
-// giving up after `limit` polls (0: the default), so tests can compare the
-// two paths and drive the give-up path from the host.
-bool persistent_draft_applies(int dtype, int B, int V, int r, const void* H, hipStream_t s);
-hipError_t launch_draft_persistent(const void* L, const void* A, const void* Bm, const int32_t* x0, int B, int gamma,
-                                   int V, int r, SeedArg seed, int32_t* tok, float* p, double* lse, const float* z0,
-                                   const void* wc, float* z_out, void* ws, const WsLayout& lay, hipStream_t s);
-void set_draft_test_mode(bool per_step_only, unsigned phantom, unsigned limit);
-// Clears the draft's barrier words (the per-step path's first launch).
-hipError_t launch_clear_sync(void* ws, const WsLayout& lay, hipStream_t s);
 
 hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,
                            int32_t* len, hipStream_t s);

@@ -70,8 +70,7 @@ enum {
     DSPARK_ERR_INVALID_ARG = -1, /* null pointer, negative size or budget, misalignment */
     DSPARK_ERR_UNSUPPORTED = -2, /* dtype or a size outside the limits above */
     DSPARK_ERR_WORKSPACE = -3,   /* ws_bytes < dspark_workspace_size(...) */
-    DSPARK_ERR_HIP = -4,         /* a HIP launch or event call failed */
-    DSPARK_ERR_SYNC = -5         /* dspark_draft_status: the draft's device-wide barrier gave up */
+    DSPARK_ERR_HIP = -4          /* a HIP launch or event call failed */
 };
 
 /* Library version string (static storage). */
@@ -117,33 +116,6 @@ size_t dspark_workspace_size(int B, int gamma, int V, int r);
 int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B, int gamma,
                         int V, int r, uint64_t seed, const uint64_t* seed_dev, int32_t* draft_tok, float* draft_p,
                         double* draft_lse, void* ws, size_t ws_bytes, void* stream);
-
-/*
- * dspark_draft_status -- whether the last draft call on workspace `ws` (NULL:
- * the static scratch of dspark_markov_draft_noalloc on the current device)
- * completed.  Waits for `stream`, then reads the draft's error word:
- * DSPARK_OK, or DSPARK_ERR_SYNC when the draft ran as one persistent launch
- * and its device-wide barrier gave up waiting (its outputs are then
- * invalid).  How a draft runs: at bf16, rank 256, B <= the number of compute
- * units and V <= 512 * compute units, an eager call (not under stream
- * capture) runs all gamma steps as one cooperative launch that keeps Bm on
- * chip and synchronises its workgroups with a bounded device-wide barrier;
- * every other call (and every call under capture) runs gamma tile + locate
- * launches.  Both give the same outputs bit for bit.  B, gamma, V, r as
- * given to the draft.  Not for use under graph capture (it synchronises).
- */
-int dspark_draft_status(const void* ws, int B, int gamma, int V, int r, void* stream);
-
-/*
- * dspark_debug_draft -- test hook, process-wide, not for production use.
- * per_step_only != 0 runs every draft as per-step launches (to compare the
- * two ways a draft runs).  phantom_arrivals > 0 makes every device-wide
- * barrier of the persistent draft also wait for that many arrivals that
- * never come, a waiter giving up after poll_limit polls (0 = the default,
- * about a second): every workgroup then exits and dspark_draft_status
- * reports DSPARK_ERR_SYNC.  (0, 0, 0) restores normal operation.
- */
-int dspark_debug_draft(int per_step_only, unsigned phantom_arrivals, unsigned poll_limit);
 
 /*
  * dspark_markov_draft_noalloc -- dspark_markov_draft for callers that cannot
@@ -333,9 +305,7 @@ int dspark_rnn_verify(int dtype, const void* Tgt, const void* L, const void* H, 
  * dspark_profile_query waits for the recorded events and returns the summed
  * duration in ms and the launch count of one kernel:
  *   0 draft tiles, 1 draft locate, 2 schedule, 3 target partials, 4 accept,
- *   5 residual tiles, 6 bonus partials, 7 final, 8 persistent draft (the
- *   whole gamma-step draft as one cooperative launch; its pair brackets the
- *   launch on the stream instead of being bound to the dispatch).
+ *   5 residual tiles, 6 bonus partials, 7 final.
  */
 int dspark_profile_start(int max_launches, unsigned kernel_mask);
 int dspark_profile_stop(void);
