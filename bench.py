@@ -197,6 +197,28 @@ def acceptance_by_position(acc, ell, gamma: int) -> dict:
     return out
 
 
+def calibration_report(wl, z, acc_steps) -> dict:
+    """ECE (15 equal-width bins) of the prefix survival at each position against survival labels
+    1[accepted >= k] from steps that verified every drafted token (acc_steps [steps][B]; the confidence
+    logits z are the workload's, the same in every step): with the workload's temperatures and with the
+    default 1 + 0.1k."""
+    import numpy as np
+    from draft_verify_sampling_prev_amd import calibration as cal
+    gamma = wl.gamma
+    n = acc_steps.shape[0]
+    labels = cal.survival_labels(acc_steps.ravel(), gamma)
+    zz = np.tile(np.asarray(z, dtype=np.float32), (n, 1))
+    default = np.array([1.0 + 0.1 * k for k in range(1, gamma + 1)], dtype=np.float32)
+    th = cal.survival(zz, np.asarray(wl.temps, dtype=np.float32))
+    th0 = cal.survival(zz, default)
+    return {"temps": [round(float(t), 4) for t in wl.temps],
+            "ece": [round(cal.ece(th[:, k], labels[:, k]), 4) for k in range(gamma)],
+            "default_temps": [round(float(t), 4) for t in default],
+            "ece_default_temps": [round(cal.ece(th0[:, k], labels[:, k]), 4) for k in range(gamma)],
+            "survival_rate": [round(float(v), 4) for v in labels.mean(0)],
+            "mean_survival": [round(float(v), 4) for v in th.mean(0)]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +391,7 @@ def main():
         acc_full[i].copy_(acc)
     torch.cuda.synchronize()
     accept_profile = acceptance_by_position(acc_full.cpu().numpy().ravel(), np.full(NK * B, gamma), gamma)
+    calib = calibration_report(wl, inp.z.numpy(), acc_full.cpu().numpy())
 
     graph = None
     if not args.no_graph:
@@ -446,6 +469,7 @@ def main():
         "vocab_passes": vocab,
         "verify_len_histogram": torch.bincount(ell.long().cpu(), minlength=gamma + 1).tolist(),
         "acceptance_by_position": {"budget": B * gamma, "steps": NK, "conditional": accept_profile},
+        "calibration": calib,
         "secondary": {"drafted_tokens_per_s": round(B * gamma / (ms_step / 1000.0), 1),
                       "verified_tokens_per_s": round(vocab["verified_per_step"] / (ms_step / 1000.0), 1),
                       "mean_emitted_per_request": round(emitted / K / B, 4)},
