@@ -25,6 +25,11 @@ import numpy as np
 from . import accept_scan, draft_row, final_token, rnn_state, select, survival, uniform
 
 FLIP_TOL = 1e-5
+# Flips observed between the GPU path and the oracle lie within 1e-7 of their boundary (the GPU sums fp32
+# exponentials per tile and combines tiles in fp64; the oracle sums in fp64), at about one per 500 decisions at
+# V = 129280, where a token's CDF interval is itself ~1e-5 wide.  The tests require every flip within
+# MAX_FLIP_GAP, and at most max(3, decisions / 250) flips per case.
+MAX_FLIP_GAP = 1e-6
 P_RTOL = 1e-5       # probabilities, relative
 LSE_ATOL = 1e-5     # log-normalisers, absolute
 THETA_RTOL = 1e-5   # survivals, relative
@@ -38,6 +43,7 @@ class Report:
     accept_flips: int = 0
     final_flips: int = 0
     failures: List[str] = dataclasses.field(default_factory=list)
+    flip_gaps: List[float] = dataclasses.field(default_factory=list)  # |u - boundary| of every allowed flip
 
     def fail(self, msg: str):
         if len(self.failures) < 50:
@@ -56,13 +62,24 @@ class Report:
         self.draft_flips += other.draft_flips
         self.accept_flips += other.accept_flips
         self.final_flips += other.final_flips
+        self.flip_gaps.extend(other.flip_gaps)
         for f in other.failures:
             self.fail(f)
 
     def summary(self) -> str:
+        gaps = f" max_flip_gap={max(self.flip_gaps):.2e}" if self.flip_gaps else ""
         return (f"checked={self.checked} decisions={self.decisions} draft_flips={self.draft_flips} "
-                f"accept_flips={self.accept_flips} final_flips={self.final_flips} failures={len(self.failures)}"
+                f"accept_flips={self.accept_flips} final_flips={self.final_flips}{gaps} failures={len(self.failures)}"
                 + ("" if self.ok() else "\n  " + "\n  ".join(self.failures[:10])))
+
+
+def flip_cap(rep: "Report") -> int:
+    """Largest number of near-boundary flips a case may have: 3, or one per 250 decisions if more."""
+    return max(3, -(-rep.decisions // 250))
+
+
+def flips_ok(rep: "Report") -> bool:
+    return rep.flips <= flip_cap(rep) and all(g < MAX_FLIP_GAP for g in rep.flip_gaps)
 
 
 def default_threads() -> int:
@@ -84,12 +101,15 @@ def _parallel(fn, items: list, rep: Report, threads: int):
         rep.merge(r)
 
 
-def _sample_flip_allowed(o_tok: int, y: int, o: dict) -> bool:
-    """o: oracle row result queried at token y (cdf_before = C_{y-1}/S, cdf_through = C_y/S)."""
+def _sample_flip_gap(o_tok: int, y: int, o: dict) -> float:
+    """Distance of u from the oracle's CDF boundary between the oracle token and the GPU token y
+    (o: oracle row result queried at y: cdf_before = C_{y-1}/S, cdf_through = C_y/S)."""
     u = o["u"]
-    if y > o_tok:
-        return o["cdf_before"] - u < FLIP_TOL
-    return u - o["cdf_through"] < FLIP_TOL
+    return o["cdf_before"] - u if y > o_tok else u - o["cdf_through"]
+
+
+def _sample_flip_allowed(o_tok: int, y: int, o: dict) -> bool:
+    return _sample_flip_gap(o_tok, y, o) < FLIP_TOL
 
 
 def check_draft(L, A, Bm, x0, seed, tok, p, lse, rep: Report, rows: Optional[Iterable[Tuple[int, int]]] = None,
@@ -122,6 +142,7 @@ def _check_draft_rows(L, A, Bm, x0, seed, tok, p, lse, rep: Report, rows, states
         if o["tok"] != y:
             if _sample_flip_allowed(o["tok"], y, o):
                 rep.draft_flips += 1
+                rep.flip_gaps.append(_sample_flip_gap(o["tok"], y, o))
                 continue
             rep.fail(f"draft b={b} k={k}: gpu token {y} oracle {o['tok']} (u={u:.8f}, "
                      f"C_before={o['cdf_before']:.8f}, C_through={o['cdf_through']:.8f})")
@@ -215,6 +236,7 @@ def _check_verify_requests(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_
             if gpu_acc != orc_acc:
                 if abs(float(us[k]) - ratio[k]) < FLIP_TOL:
                     rep.accept_flips += 1
+                    rep.flip_gaps.append(abs(float(us[k]) - ratio[k]))
                 else:
                     rep.fail(f"verify b={b} k={k + 1}: gpu {'accept' if gpu_acc else 'reject'} but "
                              f"u={us[k]:.8f} ratio={ratio[k]:.8f}")
@@ -239,6 +261,7 @@ def _check_verify_requests(T, L, A, Bm, x0, tok, pd, ell, seed, acc, out_tok, n_
         if o["tok"] != y:
             if _sample_flip_allowed(o["tok"], y, o):
                 rep.final_flips += 1
+                rep.flip_gaps.append(_sample_flip_gap(o["tok"], y, o))
             else:
                 kind = "residual" if a_g < l else "bonus"
                 rep.fail(f"verify b={b} ({kind}, a={a_g}, l={l}): gpu token {y} oracle {o['tok']} "

@@ -67,6 +67,7 @@ def test_graph_replays_with_device_seed_draw_fresh_uniforms():
     seed's uniforms: every replay equals the eager step run with the same seed, replays with different
     seeds differ, and one replay is checked against the oracle."""
     from gpu_util import check_step, host
+    from oracle import check
 
     wl = synth.tiny(B=48, gamma=5, V=4096, r=64, budget=100, dtype="bf16")
     inp = synth.make_inputs(wl)
@@ -128,4 +129,4 @@ def test_graph_replays_with_device_seed_draw_fresh_uniforms():
     assert not np.array_equal(replays[seeds[0]]["tok"], replays[seeds[1]]["tok"])
     rep = check_step(inp, replays[seeds[2]], wl.budget, seeds[2])
     assert rep.ok(), rep.summary()
-    assert rep.flips <= 3
+    assert check.flips_ok(rep), rep.summary()

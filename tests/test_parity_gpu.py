@@ -1,7 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the oracle, teacher-forced.
 
 Bit-exact: verify lengths (given the GPU's own survivals), accepted counts and
-token ids, except counted near-boundary flips (|u - boundary| < 1e-5).
+token ids, except counted near-boundary flips: |u - boundary| < 1e-5 by the
+parity protocol, and in addition every flip within 1e-6 of its boundary and
+at most max(3, decisions / 250) flips per case (oracle/check.py flips_ok).
 Probabilities within 1e-5 relative, log-normalisers within 1e-5, survivals
 within 1e-5 relative.
 """
@@ -17,8 +19,6 @@ from oracle import check
 
 pytestmark = pytest.mark.gpu
 
-# Flips are rounding-level events; at these sizes more than a handful means a bug.
-MAX_FLIPS = 3
 
 
 def _run_and_check(wl, seed=None, draft_rows=None, requests=None, data_seed=None, inp=None):
@@ -32,7 +32,7 @@ def _run_and_check(wl, seed=None, draft_rows=None, requests=None, data_seed=None
                      threads=check.default_threads())
     print("  ", rep.summary(), f"(oracle {time.perf_counter() - t0:.1f} s)", flush=True)
     assert rep.ok(), rep.summary()
-    assert rep.flips <= MAX_FLIPS, rep.summary()
+    assert check.flips_ok(rep), rep.summary()
     return out, rep
 
 
@@ -169,7 +169,7 @@ def test_load_sweep_sampled(mult):
                      threads=check.default_threads())
     print("  ", rep.summary(), flush=True)
     assert rep.ok(), rep.summary()
-    assert rep.flips <= MAX_FLIPS
+    assert check.flips_ok(rep), rep.summary()
     if mult == 8:  # run to run, bitwise, at the B = 1024 shape (four row blocks, three rounds of tile slots)
         again = run_step(inp, wl.budget, wl.philox_seed)
         for k in out:

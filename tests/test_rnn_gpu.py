@@ -2,8 +2,8 @@
 against the oracle, teacher-forced on the GPU's own states and tokens: each
 state within half an ulp of its element type of tanh(W h_prev + A[x]), each
 draft sample / residual from the GPU's state as the operand.  Near-boundary
-flips (sampling and accept decisions only) are capped at 3 per case, as on
-the Markov path."""
+flips are counted over sampling and accept decisions only (not state
+elements) and held to the Markov path's rule (oracle/check.py flips_ok)."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +14,6 @@ from oracle import check
 
 pytestmark = pytest.mark.gpu
 
-MAX_FLIPS = 3
 
 
 def _f32(t):
@@ -45,7 +44,7 @@ def _run(wl, seed=777, draft_rows=None, requests=None, state_rows=None):
                        states=Hh, threads=nt)
     print("  ", rep.summary(), flush=True)
     assert rep.ok(), rep.summary()
-    assert rep.flips <= MAX_FLIPS, rep.summary()
+    assert check.flips_ok(rep), rep.summary()
     # the states really carry the prefix: they differ from tanh(A[x]) once W acts (k >= 2)
     if wl.gamma >= 2:
         assert not np.allclose(Hh[:, 1], np.tanh(A[tk[:, 0]]), atol=1e-4)
