@@ -225,7 +225,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv4")
-    ap.add_argument("--cpu-requests", type=int, default=64,
+    ap.add_argument("--cpu-requests", type=int, default=128,
                     help="requests in the one-thread oracle CPU-baseline sample (~12 s)")
     ap.add_argument("--cpu-requests-mt", type=int, default=256,
                     help="requests in the multi-thread oracle CPU-baseline sample")
@@ -446,7 +446,7 @@ def main():
                                                 f" (tau {args.tau})" if args.schedule == "threshold" else "")
                    + (", z from the fused Markov-conditioned confidence head" if args.confidence else "")
                    + (", RNN sequential head" if args.head == "rnn" else ""),
-                   "emitted_per_step": round(emitted / K, 2), "verified_per_step": int(ell.sum().item()),
+                   "emitted_per_step": round(emitted / K, 2), "verified_per_step": round(n_adm, 2),
                    "accumulation": "fp32 MFMA, fp64 softmax masses"},
         "roofline": {"kernel": "draft Markov tiles (k_draft_tiles)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -467,7 +467,8 @@ def main():
                                                                else FP32_MFMA_PEAK_TFLOPS), 4)},
         "kernels": kern,
         "vocab_passes": vocab,
-        "verify_len_histogram": torch.bincount(ell.long().cpu(), minlength=gamma + 1).tolist(),
+        # verify lengths of the last of the NK per-kernel steps (the workload's own budget)
+        "verify_len_histogram": torch.bincount(ell_hist[NK - 1].long().cpu(), minlength=gamma + 1).tolist(),
         "acceptance_by_position": {"budget": B * gamma, "steps": NK, "conditional": accept_profile},
         "calibration": calib,
         "secondary": {"drafted_tokens_per_s": round(B * gamma / (ms_step / 1000.0), 1),
