@@ -291,15 +291,29 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     // would otherwise all be waited for before the loop is entered).
     const std::true_type more{};
     body(std::false_type{}, 0, s0, s3, l0, l1);
-    for (int i = 1; i < cnt;) {
+    // Whole rounds of four tiles, then at most three more.  (A loop with an
+    // exit between its bodies joins that exit with its back edge, and the
+    // compiler then waits for nearly every load in flight at the top of the
+    // loop.)
+    int i = 1;
+    for (; i + 4 <= cnt; i += 4) {
         body(more, i, s1, s0, l1, l0);
-        if (++i >= cnt) break;
-        body(more, i, s2, s1, l0, l1);
-        if (++i >= cnt) break;
-        body(more, i, s3, s2, l1, l0);
-        if (++i >= cnt) break;
-        body(more, i, s0, s3, l0, l1);
-        ++i;
+        body(more, i + 1, s2, s1, l0, l1);
+        body(more, i + 2, s3, s2, l1, l0);
+        body(more, i + 3, s0, s3, l0, l1);
+    }
+    // The rest as straight-line code per count (a body that may or may not
+    // have run before another also makes the compiler wait early).
+    const int rest = cnt - i;
+    if (rest == 1) {
+        body(more, i, s1, s0, l1, l0);
+    } else if (rest == 2) {
+        body(more, i, s1, s0, l1, l0);
+        body(more, i + 1, s2, s1, l0, l1);
+    } else if (rest == 3) {
+        body(more, i, s1, s0, l1, l0);
+        body(more, i + 1, s2, s1, l0, l1);
+        body(more, i + 2, s3, s2, l1, l0);
     }
     if (active) epilogue(std::true_type{});  // the slot's last tile (the vocabulary's tail for the last slot)
     wait_all_mem();  // the dummy loads past the last tile

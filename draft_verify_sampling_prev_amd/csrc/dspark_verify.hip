@@ -510,15 +510,25 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     }
     // Tile 0 is peeled off the loop (see the draft tile kernel).
     body(0, s0, s3, l0, t0r, l1, t1r);
-    for (int i = 1; i < cnt;) {
+    // Whole rounds of four tiles, then at most three more (see the draft tile
+    // kernel: no exit between the bodies of the loop).
+    int i = 1;
+    for (; i + 4 <= cnt; i += 4) {
         body(i, s1, s0, l1, t1r, l0, t0r);
-        if (++i >= cnt) break;
-        body(i, s2, s1, l0, t0r, l1, t1r);
-        if (++i >= cnt) break;
-        body(i, s3, s2, l1, t1r, l0, t0r);
-        if (++i >= cnt) break;
-        body(i, s0, s3, l0, t0r, l1, t1r);
-        ++i;
+        body(i + 1, s2, s1, l0, t0r, l1, t1r);
+        body(i + 2, s3, s2, l1, t1r, l0, t0r);
+        body(i + 3, s0, s3, l0, t0r, l1, t1r);
+    }
+    const int rest = cnt - i;
+    if (rest == 1) {
+        body(i, s1, s0, l1, t1r, l0, t0r);
+    } else if (rest == 2) {
+        body(i, s1, s0, l1, t1r, l0, t0r);
+        body(i + 1, s2, s1, l0, t0r, l1, t1r);
+    } else if (rest == 3) {
+        body(i, s1, s0, l1, t1r, l0, t0r);
+        body(i + 1, s2, s1, l0, t0r, l1, t1r);
+        body(i + 2, s3, s2, l1, t1r, l0, t0r);
     }
     wait_all_mem();
     __syncthreads();
