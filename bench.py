@@ -113,6 +113,43 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
+def tile_slots(nT: int, nM: int, cus: int, max_tiles: int = 12) -> int:
+    """Persistent slots of the bf16 draft tile kernel (the library's rule): enough slots that each holds at most
+    max_tiles tiles, rounded up to whole rounds of one workgroup per compute unit per row block."""
+    per_round = max(cus // nM, 1)
+    need = -(-nT // max_tiles)
+    rounds = -(-need // per_round)
+    return min(nT, per_round * rounds)
+
+
+def pattern_ceiling(g, wl, dev, method_b: int, tile_us: float, reps: int = 8):
+    """Duration of a load-only kernel (libdspark_probe.so) that reads exactly the draft tile kernel's bytes in its
+    per-workgroup order; the tile kernel cannot run faster than it.  bf16 with one row block (B <= 256) only."""
+    import ctypes
+    import torch
+    if wl.dtype != "bf16" or wl.B > 256:
+        return None
+    path = os.path.join(ROOT, "draft_verify_sampling_prev_amd", "libdspark_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.dspark_probe_time_tile_reads.restype = ctypes.c_int
+    lib.dspark_probe_time_tile_reads.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 6 + [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    nT = (wl.V + 63) // 64
+    S = tile_slots(nT, 1, torch.cuda.get_device_properties(dev).multi_processor_count)
+    sink = torch.empty(S * 512, dtype=torch.int32, device=dev)
+    us = ctypes.c_double(0.0)
+    rc = lib.dspark_probe_time_tile_reads(g.L.data_ptr(), g.Bm.data_ptr(), wl.B, wl.gamma, wl.V, wl.r, S, reps,
+                                          sink.data_ptr(), torch.cuda.current_stream(dev).cuda_stream,
+                                          ctypes.byref(us))
+    if rc != 0:
+        raise RuntimeError(f"dspark_probe_time_tile_reads failed ({rc})")
+    return {"kernel": "load-only kernel reading the draft tile kernel's L rows and Bm rows in its per-workgroup "
+                      "order (libdspark_probe.so), timed like the tile kernel",
+            "avg_launch_us": round(us.value, 3), "GB/s": round(method_b / (us.value * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(method_b / (us.value * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "tile_kernel_frac_of_ceiling": round(us.value / tile_us, 4), "launches": reps * wl.gamma}
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the draft tile kernel from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), if it was taken on the current
@@ -427,6 +464,7 @@ def main():
     avg_s = tiles_ms / max(tiles_n, 1) / 1000.0
     achieved = method_b / avg_s / 1e9
     tr = measured_traffic(wl.name)
+    ceiling = pattern_ceiling(g, wl, dev, method_b, avg_s * 1e6)
     result = {
         "metric": "draft+verify tokens/s at B=256,V=129280,gamma=5 (emitted tokens per step time)",
         "value": round(value, 1),
@@ -464,7 +502,8 @@ def main():
                                f"pass of the same {K} steps ({round(ms_step_instr, 4)} ms per step in that pass)",
                      "mfma_tflops": round(flops / avg_s / 1e12, 2),
                      "mfma_frac": round(flops / avg_s / 1e12 / (BF16_MFMA_PEAK_TFLOPS if wl.dtype == "bf16"
-                                                               else FP32_MFMA_PEAK_TFLOPS), 4)},
+                                                               else FP32_MFMA_PEAK_TFLOPS), 4),
+                     "pattern_ceiling": ceiling},
         "kernels": kern,
         "vocab_passes": vocab,
         # verify lengths of the last of the NK per-kernel steps (the workload's own budget)

@@ -1,7 +1,9 @@
 """Build libdspark.so (gfx950) in-tree with hipcc.
 
 Every translation unit is compiled to an object in parallel, then linked into
-``draft_verify_sampling_prev_amd/libdspark.so``.  Flags:
+``draft_verify_sampling_prev_amd/libdspark.so``; the load-only measurement
+kernel (``csrc/dspark_probe.hip``) goes into its own
+``libdspark_probe.so``, outside the library's ABI.  Flags:
   --offload-arch=gfx950                 MI355X only
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                         no packed fp32 VALU instructions
@@ -19,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdspark.so")
+PROBE_LIB = os.path.join(PKG, "libdspark_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["dspark_api.hip", "dspark_draft.hip", "dspark_schedule.hip", "dspark_verify.hip"]
@@ -49,8 +52,11 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    probe_tmp = PROBE_LIB + ".tmp"
+    cmds.append([HIPCC, *FLAGS, "-shared", os.path.join(CSRC, "dspark_probe.hip"), "-o", probe_tmp])
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
         outs = list(ex.map(_run, cmds))
+    os.replace(probe_tmp, PROBE_LIB)
     tmp = LIB + ".tmp"
     outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
     os.replace(tmp, LIB)

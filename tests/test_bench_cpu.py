@@ -75,3 +75,21 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert p.returncode != 0
     assert "one GPU" in (p.stdout + p.stderr)
+
+
+def test_tile_slots_match_the_library_rule():
+    """The bench's copy of the slot rule (used to split the load-only ceiling kernel as the tile kernel splits its
+    tiles): at most 12 tiles per slot, whole rounds of one workgroup per compute unit and row block."""
+    assert bench.tile_slots(2020, 1, 256) == 256       # V = 129280, B <= 256: one round
+    assert bench.tile_slots(2020, 4, 256) == 192       # B = 1024: 169 needed, three rounds of 64
+    assert bench.tile_slots(16, 1, 256) == 16          # fewer tiles than compute units
+    assert bench.tile_slots(3200, 1, 256) == 512       # 267 needed: two rounds
+
+
+def test_probe_library_exports_its_timer():
+    import ctypes
+    path = os.path.join(os.path.dirname(bench.__file__), "draft_verify_sampling_prev_amd", "libdspark_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libdspark_probe.so not built")
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "dspark_probe_time_tile_reads")
