@@ -187,6 +187,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     };
     const BmDmaLanes<NW> dml = bm_dma_lanes<NW>(V, r);
     auto dma = [&](int i, char* buf) { dma_bm_tile_pre<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf, dml); };
+    auto dma_block = [&](int i, char* buf, int t) {
+        dma_bm_block_pre<NW>(Bm, V, (t0 + i * ts) * kTcols, i >= cnt, buf, dml, t);
+    };
 
     floatx4 fprev[4][2];
     int prev = -1;  // local index of the tile held in fprev
@@ -224,9 +227,20 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
             dma(2, s2);
             issue_fence();
         }
-        dma(i + 3, nxt);
-        issue_fence();
-        if (active) {
+        // Bm tile i+3: with a compile-time rank its four DMA instructions go
+        // between the MFMAs below (after k steps 0, 2, 4, 6), still after this
+        // iteration's L loads and before the next iteration's, so the waits
+        // keep their counts.
+        if constexpr (KS == 0) {
+            dma(i + 3, nxt);
+            issue_fence();
+        }
+        if (active || KS > 0) {
+            // (With a compile-time rank every wave computes, also one whose
+            // rows all lie past the batch: it works on the clamped last row
+            // and its partials are never written.  A branch would leave the
+            // two paths with different loads pending, and the compiler would
+            // then wait for far more loads than needed.)
             // The previous tile's epilogue first: it needs no memory, so it
             // runs while this tile's L values are still arriving.  (Measured
             // on MI355X: giving the two waves of a SIMD opposite phase orders
@@ -240,7 +254,13 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(row16_block(lc[bb], vb));
-            tile_mma_vm<2, KS>(a, cur, nks, acc);
+            if constexpr (KS > 0) {
+                tile_mma_vm<2, KS>(a, cur, nks, acc, [&](int ks) {
+                    if ((ks & 1) == 0) dma_block(i + 3, nxt, ks >> 1);
+                });
+            } else {
+                tile_mma_vm<2, KS>(a, cur, nks, acc);
+            }
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
@@ -315,7 +335,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
         body(more, i + 1, s2, s1, l0, l1);
         body(more, i + 2, s3, s2, l1, l0);
     }
-    if (active) epilogue(std::true_type{});  // the slot's last tile (the vocabulary's tail for the last slot)
+    if (active || KS > 0) epilogue(std::true_type{});  // the slot's last tile (the vocabulary's tail for the last slot)
     wait_all_mem();  // the dummy loads past the last tile
     __syncthreads();
     // Write the staged partials (consecutive threads take consecutive tiles of a row).

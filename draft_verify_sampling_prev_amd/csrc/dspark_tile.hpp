@@ -31,6 +31,8 @@
 // and in the one-row recompute, so both produce the same bits.
 #pragma once
 
+#include <type_traits>
+
 #include "dspark_device.hpp"
 
 namespace dspark {
@@ -152,6 +154,24 @@ __device__ __forceinline__ void dma_bm_tile_pre(const uint16_t* __restrict__ Bm,
         dma16(base, voff, buf + blk * 1024);
     }
 }
+
+// Block t (< 32 / NW) of this wave's share of dma_bm_tile_pre, alone: the
+// pipelines spread a tile's DMA instructions over the MFMA chain.
+template <int NW>
+__device__ __forceinline__ void dma_bm_block_pre(const uint16_t* __restrict__ Bm, int V, int n0, bool dummy, char* buf,
+                                                 const BmDmaLanes<NW>& d, int t)
+{
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    dummy = __builtin_amdgcn_readfirstlane((int)dummy) != 0;
+    const int blk = wave_id() + NW * t;
+    const uint16_t* base = Bm + (dummy ? 0ll : d.kbv[t] + n0);
+    const uint32_t voff = dummy ? 0u : d.kv[t] + 2u * (uint32_t)min(d.c8[t], V - 8 - n0);
+    dma16(base, voff, buf + blk * 1024);
+}
+
+struct NoHook {
+    __device__ void operator()(int) const {}
+};
 
 __device__ __forceinline__ v4s tr_read(const char* buf, int off)
 {
@@ -279,9 +299,13 @@ __device__ __forceinline__ uint2 row16_block(const uint4 (&raw)[2], int vb)
     return make_uint2(lane_select(x.x, x.z, high), lane_select(x.y, x.w, high));
 }
 
-template <int NBB, int KS>
+// hook(ks) runs after the MFMAs of k step ks (KS > 0 only), in program order
+// between scheduling fences: the pipelines issue their next tile's DMA there,
+// so the address unit's queue, which all waves of a workgroup fill at once
+// after each barrier, drains while the matrix unit is busy.
+template <int NBB, int KS, class Hook = NoHook>
 __device__ __forceinline__ void tile_mma_vm(const uint4 (&a)[NBB][8], const char* bufB, int nks,
-                                            floatx4 (&acc)[4][NBB])
+                                            floatx4 (&acc)[4][NBB], Hook hook = Hook{})
 {
     int off[4];
     bm_lane_offsets(off);
@@ -313,6 +337,11 @@ __device__ __forceinline__ void tile_mma_vm(const uint4 (&a)[NBB][8], const char
                     acc[vb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         b[vb], __builtin_bit_cast(bf16x8, a[bb][ks]), acc[vb][bb], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0x0406);
+            if constexpr (!std::is_same<Hook, NoHook>::value) {
+                __builtin_amdgcn_sched_barrier(0);
+                hook(ks);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb) {
                 b[vb] = b1[vb];
