@@ -399,6 +399,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     };
     const BmDmaLanes<NW> dml = bm_dma_lanes<NW>(V, r);
     auto dma = [&](int i, char* buf) { dma_bm_tile_pre<NW>(Bm, V, r, (t0 + i * ts) * kTcols, i >= cnt, buf, dml); };
+    auto dma_block = [&](int i, char* buf, int t) {
+        dma_bm_block_pre<NW>(Bm, V, (t0 + i * ts) * kTcols, i >= cnt, buf, dml, t);
+    };
 
     // Row sums of tile i from its logits f (accumulators) and target values,
     // for the first NBB batch blocks.  Every lane of a row ends with the same
@@ -457,8 +460,15 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
             dma(2, s2);
             issue_fence();
         }
-        dma(i + 3, nxt);
-        issue_fence();
+        // Bm tile i+3: with a compile-time rank its DMA instructions go between
+        // the MFMAs (see the draft tile kernel), in the same order on every path.
+        if constexpr (KS == 0) {
+            dma(i + 3, nxt);
+            issue_fence();
+        }
+        auto hook = [&](int ks) {
+            if ((ks & 1) == 0) dma_block(i + 3, nxt, ks >> 1);
+        };
         if (act1) {
             mask_tail(i, tc);
             floatx4 acc[4][2];
@@ -466,15 +476,21 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(row16_block(lc[bb], vb));
-            tile_mma_vm<2, KS>(a, cur, nks, acc);
+            if constexpr (KS > 0) tile_mma_vm<2, KS>(a, cur, nks, acc, hook);
+            else tile_mma_vm<2, KS>(a, cur, nks, acc);
             epilogue(std::integral_constant<int, 2>{}, i, acc, tc);
         } else if (act0) {  // only the first batch block holds rejected rows
             mask_tail(i, tc);
             floatx4 acc[4][1];
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(row16_block(lc[0], vb));
-            tile_mma_vm<1, KS>(*reinterpret_cast<const uint4(*)[1][8]>(&a[0]), cur, nks, acc);
+            const uint4(&a0)[1][8] = *reinterpret_cast<const uint4(*)[1][8]>(&a[0]);
+            if constexpr (KS > 0) tile_mma_vm<1, KS>(a0, cur, nks, acc, hook);
+            else tile_mma_vm<1, KS>(a0, cur, nks, acc);
             epilogue(std::integral_constant<int, 1>{}, i, acc, tc);
+        } else if constexpr (KS > 0) {
+            for (int t = 0; t < 32 / NW; ++t) dma_block(i + 3, nxt, t);
+            issue_fence();
         }
     };
 
