@@ -336,13 +336,18 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
         body(more, i + 2, s3, s2, l1, l0);
     }
     if (active || KS > 0) epilogue(std::true_type{});  // the slot's last tile (the vocabulary's tail for the last slot)
-    wait_all_mem();  // the dummy loads past the last tile
-    __syncthreads();
+    // The staged partials are visible to the workgroup after an LDS wait and
+    // a barrier.  The dummy loads past the last tile (DMAs into LDS among
+    // them) drain while the partials are written, and are waited for before
+    // the waves end.
+    wait_lds();
+    barrier_lds();
     // Write the staged partials (consecutive threads take consecutive tiles of a row).
     for (int e = threadIdx.x; e < R * cnt; e += 64 * NW) {
         const int row = e / cnt, i = e - row * cnt;
         if (m0 + row < B) part[(size_t)(m0 + row) * nT + t0 + i * ts] = unpack_f2(stage[i][row]);
     }
+    wait_all_mem();
 }
 
 // ---------------------------------------------------------------------------

@@ -406,6 +406,9 @@ __device__ __forceinline__ void barrier_lds() { __builtin_amdgcn_s_barrier(); }
 // Wait for every outstanding memory operation of this wave.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait for this wave's LDS operations only (vector-memory count untouched).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
 // A float pair as one 64-bit word: LDS staging stores it with a single
 // ds_write_b64 whose alias information the compiler keeps (two float stores
 // merged late lose it, and an LDS store without it waits for every

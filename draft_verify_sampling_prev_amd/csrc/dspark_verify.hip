@@ -546,12 +546,15 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
         body(i + 1, s2, s1, l0, t0r, l1, t1r);
         body(i + 2, s3, s2, l1, t1r, l0, t0r);
     }
-    wait_all_mem();
-    __syncthreads();
+    // As in the draft tile kernel: LDS wait and barrier for the staging, the
+    // dummy loads drain while the sums are written.
+    wait_lds();
+    barrier_lds();
     for (int e = threadIdx.x; e < R * cnt; e += 64 * NW) {
         const int row = e / cnt, i = e - row * cnt;
         if (m0 + row < cntr) rpart[(size_t)(m0 + row) * nT + t0 + i * ts] = unpack_f2(stage[i][row]);
     }
+    wait_all_mem();
 }
 
 // ---------------------------------------------------------------------------
