@@ -150,7 +150,11 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
 // ---------------------------------------------------------------------------
 constexpr int kPartTiles = 12;  // tiles per slot whose partials fit the LDS staging
 
-template <int KS>
+// FULL: every row block holds 256 rows of the batch (B a multiple of 256),
+// so every wave has rows and the body has no branch.  Otherwise a wave whose
+// rows all lie past the batch skips the MFMAs and only issues its share of
+// the Bm DMA (the two paths then leave the compiler less exact waits).
+template <int KS, bool FULL>
 __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const uint16_t* __restrict__ ag,
@@ -235,12 +239,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
             dma(i + 3, nxt);
             issue_fence();
         }
-        if (active || KS > 0) {
-            // (With a compile-time rank every wave computes, also one whose
-            // rows all lie past the batch: it works on the clamped last row
-            // and its partials are never written.  A branch would leave the
-            // two paths with different loads pending, and the compiler would
-            // then wait for far more loads than needed.)
+        if (FULL || active) {
             // The previous tile's epilogue first: it needs no memory, so it
             // runs while this tile's L values are still arriving.  (Measured
             // on MI355X: giving the two waves of a SIMD opposite phase orders
@@ -266,6 +265,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
 #pragma unroll
                 for (int bb = 0; bb < 2; ++bb) fprev[vb][bb] = acc[vb][bb];
             prev = i;
+        } else if constexpr (KS > 0) {
+            for (int t = 0; t < 32 / NW; ++t) dma_block(i + 3, nxt, t);
+            issue_fence();
         }
     };
 
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
         body(more, i + 1, s2, s1, l0, l1);
         body(more, i + 2, s3, s2, l1, l0);
     }
-    if (active || KS > 0) epilogue(std::true_type{});  // the slot's last tile (the vocabulary's tail for the last slot)
+    if (FULL || active) epilogue(std::true_type{});  // the slot's last tile (the vocabulary's tail for the last slot)
     // The staged partials are visible to the workgroup after an LDS wait and
     // a barrier.  The dummy loads past the last tile (DMAs into LDS among
     // them) drain while the partials are written, and are waited for before
@@ -675,7 +677,8 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     const int nM = (B + kTileRows - 1) / kTileRows;
     const int S = tile_slots(nT, nM, cu_count(), kPartTiles);
     if (dtype == 1) {
-        auto kern = (r + 31) / 32 == 8 ? k_draft_tiles_bf16<8> : k_draft_tiles_bf16<0>;
+        auto kern = (r + 31) / 32 == 8 ? (B % kTileRows == 0 ? k_draft_tiles_bf16<8, true> : k_draft_tiles_bf16<8, false>)
+                                       : k_draft_tiles_bf16<0, false>;
         launch_timed(K_DRAFT_TILES, kern, dim3(S * nM), dim3(64 * kTileWaves), s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok,
                            static_cast<const uint16_t*>(ag_path && k >= 2 ? ag : nullptr),
