@@ -381,7 +381,6 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     uint4 a[2][8];  // B operand: the rows' A vectors (loaded in the prologue)
     const uint16_t* lrow[2];
     const uint16_t* trow[2];
-    const uint16_t* arow[2];
     int lrow_idx[2];
     float ld[2], lt[2];
     int4 rec[2];  // the rows' records (decoded after the first Bm tile is issued)
@@ -389,10 +388,10 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     for (int bb = 0; bb < 2; ++bb) rec[bb] = resid_list[min(m0 + row_of(bb) + c, cntr - 1)];
     const int nks = KS > 0 ? KS : (r + 31) / 32;
 
-    auto load_lt = [&](int i, uint4 (&lv)[2][2], uint4 (&tv)[2][2]) {
+    auto load_lt = [&](auto nbb, int i, uint4 (&lv)[2][2], uint4 (&tv)[2][2]) {
         const bool dummy = i >= cnt;
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
+        for (int bb = 0; bb < decltype(nbb)::value; ++bb) {
             load_row16(lrow[bb], (t0 + i * ts) * kTcols, V, dummy, lv[bb]);
             load_row16(trow[bb], (t0 + i * ts) * kTcols, V, dummy, tv[bb]);
         }
@@ -431,12 +430,12 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     // The vocabulary's tail tile: target values of columns at or past V
     // become -inf, so their residual weight and target probability are 0
     // (V is a multiple of 8: a 16-byte group is entirely in or out).
-    auto mask_tail = [&](int i, uint4 (&tv)[2][2]) {
+    auto mask_tail = [&](auto nbb, int i, uint4 (&tv)[2][2]) {
         const int n0 = (t0 + i * ts) * kTcols;
         if (n0 + kTcols > V) {  // uniform
             const uint4 ninf = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
+            for (int bb = 0; bb < decltype(nbb)::value; ++bb)
 #pragma unroll
                 for (int h = 0; h < kRow16Loads; ++h)
                     if (n0 + 16 * G + 8 * h >= V) tv[bb][h] = ninf;
@@ -445,107 +444,114 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     // L and T values of two tiles in flight: the four unrolled bodies
     // alternate between two register sets, so no copy waits on a load just issued.
     uint4 l0[2][2], t0r[2][2], l1[2][2], t1r[2][2];
-    auto body = [&](int i, const char* cur, char* nxt, uint4 (&lc)[2][2], uint4 (&tc)[2][2], uint4 (&ln)[2][2],
-                    uint4 (&tn)[2][2]) {
-        if (KS > 0) wait_stage<4 * kRow16Loads, 32 / NW, 20>(i);
-        else if (i == 0) wait_all_mem();  // run-time rank
-        else wait_stage<4 * kRow16Loads, 32 / NW, 20>(i);
-        barrier_lds();  // Bm tile i has landed in cur; every wave is done with nxt
-        issue_fence();
-        load_lt(i + 1, ln, tn);
-        issue_fence();
-        if (i == 0) {  // ramp-up: tiles 1 and 2 (buffers s1, s2) behind tile 3
-            dma(1, s1);
+    // The whole pipeline for a wave whose first NB batch blocks hold rejected
+    // rows (NB = 2, 1 or 0, uniform per wave): only those blocks' L and T rows
+    // are loaded, and every wait counts exactly this path's loads.  All waves
+    // take part in every tile's DMA and barrier.
+    auto run = [&](auto nbb) {
+        constexpr int NB = decltype(nbb)::value;
+        constexpr int NL = 2 * kRow16Loads * NB;  // L and T row loads per tile
+        constexpr int NA = 10 * NB;               // after the first tile: A operand (8 per block), normalisers (2)
+        auto body = [&](int i, const char* cur, char* nxt, uint4 (&lc)[2][2], uint4 (&tc)[2][2], uint4 (&ln)[2][2],
+                        uint4 (&tn)[2][2]) {
+            if (KS > 0) wait_stage<NL, 32 / NW, NA>(i);
+            else if (i == 0) wait_all_mem();  // run-time rank
+            else wait_stage<NL, 32 / NW, NA>(i);
+            barrier_lds();  // Bm tile i has landed in cur; every wave is done with nxt
             issue_fence();
-            dma(2, s2);
+            load_lt(nbb, i + 1, ln, tn);
             issue_fence();
-        }
-        // Bm tile i+3: with a compile-time rank its DMA instructions go between
-        // the MFMAs (see the draft tile kernel), in the same order on every path.
-        if constexpr (KS == 0) {
-            dma(i + 3, nxt);
-            issue_fence();
-        }
-        auto hook = [&](int ks) {
-            if ((ks & 1) == 0) dma_block(i + 3, nxt, ks >> 1);
+            if (i == 0) {  // ramp-up: tiles 1 and 2 (buffers s1, s2) behind tile 3
+                dma(1, s1);
+                issue_fence();
+                dma(2, s2);
+                issue_fence();
+            }
+            // Bm tile i+3: with a compile-time rank its DMA instructions go
+            // between the MFMAs (see the draft tile kernel).
+            if constexpr (KS == 0) {
+                dma(i + 3, nxt);
+                issue_fence();
+            }
+            auto hook = [&](int ks) {
+                if ((ks & 1) == 0) dma_block(i + 3, nxt, ks >> 1);
+            };
+            if constexpr (NB > 0) {
+                mask_tail(nbb, i, tc);
+                floatx4 acc[4][NB];
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                    for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(row16_block(lc[bb], vb));
+                const uint4(&an)[NB][8] = *reinterpret_cast<const uint4(*)[NB][8]>(&a[0]);
+                if constexpr (KS > 0) tile_mma_vm<NB, KS>(an, cur, nks, acc, hook);
+                else tile_mma_vm<NB, KS>(an, cur, nks, acc);
+                epilogue(nbb, i, acc, tc);
+            } else if constexpr (KS > 0) {
+                for (int t = 0; t < 32 / NW; ++t) dma_block(i + 3, nxt, t);
+                issue_fence();
+            }
         };
-        if (act1) {
-            mask_tail(i, tc);
-            floatx4 acc[4][2];
+
+        // Prologue: the rows' records were loaded first; the first Bm tile
+        // does not depend on them and is issued before they are used; then
+        // the first L and T tiles, the A-operand gather and the rows'
+        // normalisers (NA loads after the first tile).
+        issue_fence();
+        dma(0, s0);
+        issue_fence();
+        if constexpr (NB > 0) {
+            const uint16_t* arn[NB];
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int vb = 0; vb < 4; ++vb) acc[vb][bb] = bf16x4_to_f32(row16_block(lc[bb], vb));
-            if constexpr (KS > 0) tile_mma_vm<2, KS>(a, cur, nks, acc, hook);
-            else tile_mma_vm<2, KS>(a, cur, nks, acc);
-            epilogue(std::integral_constant<int, 2>{}, i, acc, tc);
-        } else if (act0) {  // only the first batch block holds rejected rows
-            mask_tail(i, tc);
-            floatx4 acc[4][1];
-#pragma unroll
-            for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(row16_block(lc[0], vb));
-            const uint4(&a0)[1][8] = *reinterpret_cast<const uint4(*)[1][8]>(&a[0]);
-            if constexpr (KS > 0) tile_mma_vm<1, KS>(a0, cur, nks, acc, hook);
-            else tile_mma_vm<1, KS>(a0, cur, nks, acc);
-            epilogue(std::integral_constant<int, 1>{}, i, acc, tc);
-        } else if constexpr (KS > 0) {
-            for (int t = 0; t < 32 / NW; ++t) dma_block(i + 3, nxt, t);
+            for (int bb = 0; bb < NB; ++bb) {
+                const ResidRow rr = resid_decode(rec[bb], B, gamma, nA);
+                arn[bb] = A + (size_t)rr.x * r;
+                lrow[bb] = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
+                trow[bb] = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
+                lrow_idx[bb] = rr.b * gamma + rr.ks - 1;
+            }
+            load_lt(nbb, 0, l0, t0r);
             issue_fence();
+            load_a_frags<NB>(arn, r, *reinterpret_cast<uint4(*)[NB][8]>(&a[0]));
+            double lsd[NB], lst[NB];
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                lsd[bb] = lse_d[lrow_idx[bb]];
+                lst[bb] = lse_t[lrow_idx[bb]];
+            }
+            issue_fence();
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                ld[bb] = lse_log2(lsd[bb]);
+                lt[bb] = lse_log2(lst[bb]);
+            }
+        }
+        // Tile 0 is peeled off the loop (see the draft tile kernel).
+        body(0, s0, s3, l0, t0r, l1, t1r);
+        // Whole rounds of four tiles, then at most three more (see the draft
+        // tile kernel: no exit between the bodies of the loop).
+        int i = 1;
+        for (; i + 4 <= cnt; i += 4) {
+            body(i, s1, s0, l1, t1r, l0, t0r);
+            body(i + 1, s2, s1, l0, t0r, l1, t1r);
+            body(i + 2, s3, s2, l1, t1r, l0, t0r);
+            body(i + 3, s0, s3, l0, t0r, l1, t1r);
+        }
+        const int rest = cnt - i;
+        if (rest == 1) {
+            body(i, s1, s0, l1, t1r, l0, t0r);
+        } else if (rest == 2) {
+            body(i, s1, s0, l1, t1r, l0, t0r);
+            body(i + 1, s2, s1, l0, t0r, l1, t1r);
+        } else if (rest == 3) {
+            body(i, s1, s0, l1, t1r, l0, t0r);
+            body(i + 1, s2, s1, l0, t0r, l1, t1r);
+            body(i + 2, s3, s2, l1, t1r, l0, t0r);
         }
     };
-
-    // Prologue: the rows' records were loaded first; the first Bm tile does
-    // not depend on them and is issued before they are used; then the first
-    // L and T tiles, the A-operand gather and the rows' normalisers (NA =
-    // 16 + 4 loads after the first tile).
-    issue_fence();
-    dma(0, s0);
-    issue_fence();
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        const ResidRow rr = resid_decode(rec[bb], B, gamma, nA);
-        arow[bb] = A + (size_t)rr.x * r;
-        lrow[bb] = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
-        trow[bb] = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
-        lrow_idx[bb] = rr.b * gamma + rr.ks - 1;
-    }
-    load_lt(0, l0, t0r);
-    issue_fence();
-    load_a_frags<2>(arow, r, a);
-    double lsd[2], lst[2];
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        lsd[bb] = lse_d[lrow_idx[bb]];
-        lst[bb] = lse_t[lrow_idx[bb]];
-    }
-    issue_fence();
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        ld[bb] = lse_log2(lsd[bb]);
-        lt[bb] = lse_log2(lst[bb]);
-    }
-    // Tile 0 is peeled off the loop (see the draft tile kernel).
-    body(0, s0, s3, l0, t0r, l1, t1r);
-    // Whole rounds of four tiles, then at most three more (see the draft tile
-    // kernel: no exit between the bodies of the loop).
-    int i = 1;
-    for (; i + 4 <= cnt; i += 4) {
-        body(i, s1, s0, l1, t1r, l0, t0r);
-        body(i + 1, s2, s1, l0, t0r, l1, t1r);
-        body(i + 2, s3, s2, l1, t1r, l0, t0r);
-        body(i + 3, s0, s3, l0, t0r, l1, t1r);
-    }
-    const int rest = cnt - i;
-    if (rest == 1) {
-        body(i, s1, s0, l1, t1r, l0, t0r);
-    } else if (rest == 2) {
-        body(i, s1, s0, l1, t1r, l0, t0r);
-        body(i + 1, s2, s1, l0, t0r, l1, t1r);
-    } else if (rest == 3) {
-        body(i, s1, s0, l1, t1r, l0, t0r);
-        body(i + 1, s2, s1, l0, t0r, l1, t1r);
-        body(i + 2, s3, s2, l1, t1r, l0, t0r);
-    }
+    if (act1) run(std::integral_constant<int, 2>{});
+    else if (act0) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 0>{});
     // As in the draft tile kernel: LDS wait and barrier for the staging, the
     // dummy loads drain while the sums are written.
     wait_lds();
