@@ -483,11 +483,11 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
         }
         return;
     }
-    // With AG (rank 256): the A rows of the chosen tile's 64 columns, the
-    // candidates for the sampled token, DMA'd alongside the Bm tile; the
-    // sampled one is copied into `ag` in MFMA order for the next step's tile
-    // kernel, with no memory round trip after the sample.
-    __shared__ __attribute__((aligned(1024))) char lds_a[AG ? kBmTileBytes : 1024];
+    // With AG (rank 256) the sampled token's A row is copied into `ag` in MFMA
+    // order for the next step's tile kernel.  (Measured on MI355X: reading
+    // that one row after the sample is faster than reading the chosen tile's
+    // 64 candidate rows, 32 KB, alongside its Bm tile: 7.78 against 8.02 us
+    // per launch, 8.4 MB less traffic.)
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     // The partial loads go first: the A-operand loads wait for the token.
@@ -537,18 +537,7 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
     // hides behind the tile's own loads).
     const float mt = pr[idx].x;
     floatx4 f[4];
-    auto dma_candidates = [&]() {
-        if constexpr (AG) {
-            // Rows n0 .. n0+63 of A are 32 KB contiguous; rows past V read the last 16 bytes of A.
-            const int n0u = __builtin_amdgcn_readfirstlane(n0);
-            const uint32_t lim = V - n0u >= 64 ? 32768u - 16u : (uint32_t)(V - n0u) * (kAgRank * 2) - 16u;
-            const uint16_t* base = A + (size_t)n0u * kAgRank;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) dma16(base, min((uint32_t)(i * 1024 + lane * 16), lim), lds_a + i * 1024);
-        }
-    };
-    row_tile_vm_wave<KS, AG ? 32 : 0>(L + ((size_t)b * gamma + (k - 1)) * V, a, Bm, V, r, n0, lds, f,
-                                      dma_candidates);
+    row_tile_vm_wave<KS>(L + ((size_t)b * gamma + (k - 1)) * V, a, Bm, V, r, n0, lds, f);
     if (co.z) {
         // z = z0 + <A[prev], wc> from the A operand already in registers
         // (pieces past r are zero): 64 products per lane in (k step, element)
@@ -570,9 +559,8 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
         &wsel);
     const int xk = min(n0 + j, V - 1);
     if constexpr (AG) {
-        wait_all_mem();   // the candidate rows
         if (lane < 32) {  // piece (ks, G) = (lane >> 2, lane & 3) of A[xk]: elements 8 * lane .. +7
-            const uint4 v = *reinterpret_cast<const uint4*>(lds_a + (xk - n0) * (kAgRank * 2) + lane * 16);
+            const uint4 v = *reinterpret_cast<const uint4*>(A + (size_t)xk * kAgRank + lane * 8);
             *reinterpret_cast<uint4*>(ag + ag_offset(b, lane >> 2, lane & 3)) = v;
         }
     }

@@ -173,24 +173,14 @@ __device__ __forceinline__ void row_tile_vm(const uint16_t* L_row, const uint16_
 // wave stages the Bm tile in its own LDS buffer and waits only for its own
 // loads (no barrier).  The A operand (a, k steps < nks) is loaded by the
 // caller ahead of time.
-struct NoExtraLoads {
-    __device__ __forceinline__ void operator()() const {}
-};
-// `extra` issues NEXTRA more vector-memory loads of the caller's behind the
-// tile's; they stay in flight (the caller waits for them).
-template <int KS, int NEXTRA = 0, class Extra = NoExtraLoads>
+template <int KS>
 __device__ __forceinline__ void row_tile_vm_wave(const uint16_t* L_row, const uint4 (&a)[1][8], const uint16_t* Bm,
-                                                 int V, int r, int n0, char* lds, floatx4 (&f)[4],
-                                                 Extra extra = Extra{})
+                                                 int V, int r, int n0, char* lds, floatx4 (&f)[4])
 {
     dma_bm_tile<1>(Bm, V, r, n0, false, lds);
     uint4 lv[2];
     load_row16(L_row, n0, V, false, lv);
-    issue_fence();
-    extra();
-    issue_fence();
-    if constexpr (NEXTRA == 0) wait_all_mem();
-    else wait_vmem<NEXTRA>();  // loads complete in order: the tile's (and everything older) have landed
+    wait_all_mem();
     floatx4 acc[4][1];
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb) acc[vb][0] = bf16x4_to_f32(row16_block(lv, vb));
