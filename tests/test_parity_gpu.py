@@ -63,6 +63,21 @@ def test_rank256_two_row_blocks():
     _run_and_check(wl, requests=range(0, 300, 5))
 
 
+@pytest.mark.parametrize("B,budget,rej_lo,rej_hi", [(512, 900, 129, 512), (256, 1280, 129, 256), (256, 100, 0, 111)])
+def test_full_row_blocks_all_residual_paths(B, budget, rej_lo, rej_hi):
+    """B a multiple of 256 at r = 256: the draft tile kernel's branch-free variant (every wave has rows), with
+    one and two 256-row blocks, checked in full against the oracle.  The budgets put the residual tile pass in
+    its different per-wave pipelines: with many verified drafts most requests reject and waves hold two blocks
+    of rejected rows; with budget 100 only a few requests can reject, so most waves hold none."""
+    wl = synth.tiny(B=B, gamma=5, V=3000, r=256, budget=budget, dtype="bf16")
+    out, rep = _run_and_check(wl)
+    n_rej = int((out["acc"] < out["ell"]).sum())
+    print(f"  rejected requests: {n_rej}", flush=True)
+    # more than 128 rejected rows: some waves of the residual pass hold two blocks of them; fewer than 112: some
+    # waves hold none
+    assert rej_lo <= n_rej <= rej_hi
+
+
 @pytest.mark.parametrize("B,gamma,budget", [(1, 1, 1), (1, 16, 7), (3, 16, 48), (17, 2, 0), (9, 4, 10**9)])
 def test_edge_shapes_and_budgets(B, gamma, budget):
     wl = synth.tiny(B=B, gamma=gamma, V=256, r=8, budget=budget, dtype="bf16")
