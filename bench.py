@@ -259,8 +259,12 @@ def calibration_report(wl, z, acc_steps) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="after the warmup steps, keep running untimed steps until the GPU has been busy with "
+                         "them for this long (the part's clocks take tens of milliseconds of sustained load to "
+                         "settle; the timed region then measures the steady state)")
     ap.add_argument("--workload", default="dsv4")
     ap.add_argument("--cpu-requests", type=int, default=128,
                     help="requests in the one-thread oracle CPU-baseline sample (~12 s)")
@@ -362,10 +366,23 @@ def main():
                           out=(acc, out_tok, n_out_all[i], tp))
 
     base_seed = wl.philox_seed
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
     for i in range(args.warmup):
         step(K + i, base_seed + 1000 + i)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    # Settling: more untimed steps, in blocks of 20, until the warm-up has
+    # kept the GPU busy for settle_ms (from a cold start the step takes about
+    # 5 % longer for the first ~30 ms of sustained load).
+    settle = 0
+    while (time.perf_counter() - t_warm) * 1000.0 < args.settle_ms:
+        for _ in range(20):
+            step(K + args.warmup, base_seed + 3000 + settle)
+            settle += 1
+        torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t_warm) * 1000.0
+    print(f"[bench] warmup done ({args.warmup} steps + {settle} settling steps, {warm_ms:.1f} ms)",
+          file=sys.stderr, flush=True)
 
     # Timed region: K steps, nothing else on the stream (an event recorded
     # between two kernels costs a few microseconds of GPU time, so the step
@@ -472,6 +489,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle": {"steps": settle, "ms": round(warm_ms, 1)},
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
