@@ -276,6 +276,9 @@ def main():
                     help="admission rule of the step: the budget (default, the headline), objective-based "
                          "admission against a synthetic step-time profile capped at the budget, or a static threshold")
     ap.add_argument("--tau", type=float, default=0.3, help="survival threshold for --schedule threshold")
+    ap.add_argument("--separate-schedule", action="store_true",
+                    help="budget schedule as its own dspark_schedule call after the draft, instead of inside the "
+                         "draft call (dspark_markov_draft_sched)")
     ap.add_argument("--head", choices=("markov", "rnn"), default="markov",
                     help="sequential head of the draft: the Markov head (default, the headline) or the RNN head "
                          "(h_k = tanh(W h_{k-1} + A[x_{k-1}]), synthetic W ~ N(0, 1/r))")
@@ -349,6 +352,8 @@ def main():
     Wt = (torch.randn((r, r), generator=torch.Generator().manual_seed(wl.data_seed + 3)) / r ** 0.5).to(g.L.dtype).to(dev)
     Hst = torch.empty((B, gamma, r), dtype=g.L.dtype, device=dev)
 
+    fused_schedule = args.schedule == "budget" and not args.separate_schedule
+
     def step(i: int, seed, budget=None):
         budget = wl.budget if budget is None else budget
         if args.head == "rnn":
@@ -359,9 +364,14 @@ def main():
             return
         if args.confidence:
             dsp.dspark_markov_draft_conf(g.L, g.A, g.Bm, g.x0, seed, g.z, wc, ws=ws, out=(tok, p, lse, zc))
+            schedule(budget)
+        elif fused_schedule:
+            # The budget schedule needs only z: it runs inside the draft call, beside the last draft step.
+            dsp.dspark_markov_draft_sched(g.L, g.A, g.Bm, g.x0, seed, g.z, g.temps, budget, ws=ws,
+                                          out=(tok, p, lse), survival=theta, out_len=ell)
         else:
             dsp.dspark_markov_draft(g.L, g.A, g.Bm, g.x0, seed, ws=ws, out=(tok, p, lse))
-        schedule(budget)
+            schedule(budget)
         dsp.dspark_verify(g.T, g.L, g.A, g.Bm, g.x0, tok, p, lse, ell, seed, ws=ws,
                           out=(acc, out_tok, n_out_all[i], tp))
 
@@ -499,7 +509,10 @@ def main():
         "config": {"workload": wl.name, "B": B, "gamma": gamma, "V": V, "r": r, "budget": wl.budget,
                    "schedule": args.schedule + (" (step time 1 ms + 1 us/token, capped at the budget)"
                                                 if args.schedule == "objective" else
-                                                f" (tau {args.tau})" if args.schedule == "threshold" else "")
+                                                f" (tau {args.tau})" if args.schedule == "threshold" else
+                                                " (inside the draft call, beside its last step)"
+                                                if fused_schedule and not args.confidence and args.head == "markov"
+                                                else "")
                    + (", z from the fused Markov-conditioned confidence head" if args.confidence else "")
                    + (", RNN sequential head" if args.head == "rnn" else ""),
                    "emitted_per_step": round(emitted / K, 2), "verified_per_step": round(n_adm, 2),

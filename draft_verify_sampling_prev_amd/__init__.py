@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     dspark_markov_draft,
     dspark_markov_draft_conf,
     dspark_markov_draft_noalloc,
+    dspark_markov_draft_sched,
     dspark_rnn_draft,
     dspark_rnn_verify,
     dspark_schedule,
@@ -28,6 +29,7 @@ __all__ = [
     "dspark_markov_draft",
     "dspark_markov_draft_conf",
     "dspark_markov_draft_noalloc",
+    "dspark_markov_draft_sched",
     "dspark_rnn_draft",
     "dspark_rnn_verify",
     "dspark_schedule",

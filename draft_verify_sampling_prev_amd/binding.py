@@ -62,6 +62,9 @@ def load_library():
     L.dspark_markov_draft_conf.restype = _I
     L.dspark_markov_draft_conf.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P,
                                            _P, _P, _P, ctypes.c_size_t, _P]
+    L.dspark_markov_draft_sched.restype = _I
+    L.dspark_markov_draft_sched.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P,
+                                            ctypes.c_int64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.dspark_rnn_draft.restype = _I
     L.dspark_rnn_draft.argtypes = [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_uint64, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P]
@@ -174,6 +177,44 @@ def dspark_markov_draft(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: 
                                             _ptr(lse), _ptr(ws), ws.numel(), _stream(dev, stream))
     _check(rc, "dspark_markov_draft")
     return tok, p, lse
+
+
+def dspark_markov_draft_sched(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor, seed,
+                              z: torch.Tensor, temps: torch.Tensor, budget: int, ws: Optional[torch.Tensor] = None,
+                              out: Optional[Tuple] = None, survival: Optional[torch.Tensor] = None,
+                              out_len: Optional[torch.Tensor] = None, stream=None):
+    """dspark_markov_draft then dspark_schedule(z, temps, budget) in one call (the schedule runs beside the last
+    draft step where it can).  Returns (draft_tok, draft_p, draft_lse, survival f32 [B][g], verify_len int32 [B])."""
+    dev = L.device
+    _dev(L, "L", None)
+    B, gamma, V = L.shape
+    r = A.shape[1]
+    _dev(A, "A", dev, L.dtype, (V, r))
+    _dev(Bm, "Bm", dev, L.dtype, (r, V))
+    _dev(x0, "x0", dev, torch.int32, (B,))
+    _dev(z, "z", dev, torch.float32, (B, gamma))
+    _dev(temps, "temps", dev, torch.float32, (gamma,))
+    if out is None:
+        tok = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+        p = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, gamma), dtype=torch.float64, device=dev)
+    else:
+        tok, p, lse = out
+    if survival is None:
+        survival = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    _dev(survival, "survival", dev, torch.float32, (B, gamma))
+    if out_len is None:
+        out_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    _dev(out_len, "verify_len", dev, torch.int32, (B,))
+    if ws is None:
+        ws = workspace(B, gamma, V, r, dev)
+    rc = load_library().dspark_markov_draft_sched(_dtype_code(L), _ptr(L), _ptr(A), _ptr(Bm), _ptr(x0), B, gamma, V,
+                                                  r, *_seed(seed, dev), _ptr(z), _ptr(temps),
+                                                  ctypes.c_int64(int(budget)), _ptr(tok), _ptr(p), _ptr(lse),
+                                                  _ptr(survival), _ptr(out_len), _ptr(ws), ws.numel(),
+                                                  _stream(dev, stream))
+    _check(rc, "dspark_markov_draft_sched")
+    return tok, p, lse, survival, out_len
 
 
 def dspark_markov_draft_noalloc(L: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, x0: torch.Tensor, seed,

@@ -187,7 +187,8 @@ size_t dspark_workspace_size(int B, int gamma, int V, int r)
 static int markov_draft_impl(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
                              int gamma, int V, int r, SeedArg seed, const float* z0, const void* wc,
                              int32_t* draft_tok, float* draft_p, double* draft_lse, float* z_out, const void* Wt,
-                             void* H, void* ws, size_t ws_bytes, void* stream, const WsLayout* layout = nullptr)
+                             void* H, void* ws, size_t ws_bytes, void* stream, const WsLayout* layout = nullptr,
+                             const SchedArg* sched = nullptr)
 {
     if (dtype != DSPARK_F32 && dtype != DSPARK_BF16) return fail(DSPARK_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
     int rc = check_common(B, gamma, V, r);
@@ -203,7 +204,7 @@ static int markov_draft_impl(int dtype, const void* L, const void* A, const void
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int k = 1; k <= gamma; ++k) {
         hipError_t e = launch_draft_step(dtype, L, A, Bm, x0, B, gamma, V, r, k, seed, draft_tok, draft_p, draft_lse,
-                                         z0, wc, z_out, Wt, H, ws, lay, s);
+                                         z0, wc, z_out, Wt, H, ws, lay, s, k == gamma ? sched : nullptr);
         if (e != hipSuccess) return hip_status(e, "draft launch");
     }
     return DSPARK_OK;
@@ -216,6 +217,29 @@ int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm,
     g_err[0] = 0;
     return markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, SeedArg{ seed, seed_dev }, nullptr, nullptr, draft_tok, draft_p,
                              draft_lse, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int dspark_markov_draft_sched(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
+                              int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, const float* z,
+                              const float* temps, int64_t budget, int32_t* draft_tok, float* draft_p,
+                              double* draft_lse, float* survival, int32_t* verify_len, void* ws, size_t ws_bytes,
+                              void* stream)
+{
+    g_err[0] = 0;
+    if (budget < 0) return fail(DSPARK_ERR_INVALID_ARG, "budget must be >= 0 (got %lld)", (long long)budget);
+    if (B > 0 && (!z || !temps || !survival || !verify_len)) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
+    const int64_t n = (int64_t)B * gamma;
+    const SchedArg sa{ z, temps, (long long)(budget < n ? budget : n), survival, verify_len };
+    // The schedule rides in the last locate launch where that launch can
+    // carry it; otherwise it is launched after the draft.
+    const bool fused = draft_step_can_schedule(dtype, B, gamma, V);
+    const int rc = markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, SeedArg{ seed, seed_dev }, nullptr, nullptr,
+                                     draft_tok, draft_p, draft_lse, nullptr, nullptr, nullptr, ws, ws_bytes, stream,
+                                     nullptr, fused ? &sa : nullptr);
+    if (rc || B == 0 || fused) return rc;
+    return hip_status(launch_schedule(z, temps, B, gamma, sa.admit, survival, verify_len,
+                                      static_cast<hipStream_t>(stream)),
+                      "schedule launch");
 }
 
 int dspark_markov_draft_noalloc(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,

@@ -29,6 +29,7 @@
 #include "dspark_internal.hpp"
 #include "dspark_locate.hpp"
 #include "dspark_markov.hpp"
+#include "dspark_select.hpp"
 #include "dspark_tile.hpp"
 
 namespace dspark {
@@ -461,8 +462,17 @@ __device__ __forceinline__ void prefetch_first_tile(const uint16_t* __restrict__
     wait_all_mem();
 }
 
-template <int KS, int PER, bool AG>
-__global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __restrict__ L,
+// The budget schedule carried by the last step's locate launch (SCHED): one
+// extra workgroup (index 0) of kSchedWgThreads threads, keys and scratch in
+// the locate's LDS tile buffer.  (Measured on MI355X: 512 threads were
+// slower than 256, and index 0 was 0.3-0.7 us per step faster than index B.)
+constexpr int kSchedWgThreads = 256;
+constexpr int kSchedKeysOffset = 2048;  // bytes; SelectScratch first
+constexpr int kSchedMaxKeys = (kBmTileBytes - kSchedKeysOffset) / 4;
+static_assert(sizeof(SelectScratch<kSchedWgThreads>) <= kSchedKeysOffset, "select scratch");
+
+template <int KS, int PER, bool AG, bool SCHED = false>
+__global__ __launch_bounds__(SCHED ? kSchedWgThreads : 128) void k_draft_locate_bf16(const uint16_t* __restrict__ L,
                                                           const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ Bm,
                                                           const int32_t* __restrict__ x0, int32_t* tok,
@@ -470,10 +480,21 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
                                                           const float2* __restrict__ part, uint16_t* __restrict__ ag,
                                                           const uint16_t* __restrict__ H, int B, int gamma, int V,
                                                           int r, int k, int nT, int nM_next, int S_next,
-                                                          SeedArg seed_arg, ConfOut co)
+                                                          SeedArg seed_arg, ConfOut co, SchedArg sa)
 {
-    const uint64_t seed = seed_of(seed_arg);
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
+    if constexpr (SCHED) {
+        // Workgroup 0 is the budget schedule (dispatched first: it takes longer
+        // than a request's locate); it shares nothing with the others, which
+        // take requests b = blockIdx.x - 1.
+        if (blockIdx.x == 0) {
+            budget_select<kSchedWgThreads>(sa.z, sa.temps, B, gamma, sa.admit, sa.surv, sa.len,
+                                           reinterpret_cast<uint32_t*>(lds + kSchedKeysOffset),
+                                           *reinterpret_cast<SelectScratch<kSchedWgThreads>*>(lds));
+            return;
+        }
+    }
+    const uint64_t seed = seed_of(seed_arg);
     // AG (not the last step): a second wave reads the next tile launch's
     // first tile ahead; it shares nothing with the first wave.
     if (threadIdx.x >= 64) {
@@ -488,7 +509,7 @@ __global__ __launch_bounds__(128) void k_draft_locate_bf16(const uint16_t* __res
     // that one row after the sample is faster than reading the chosen tile's
     // 64 candidate rows, 32 KB, alongside its Bm tile: 7.78 against 8.02 us
     // per launch, 8.4 MB less traffic.)
-    const int b = blockIdx.x;
+    const int b = blockIdx.x - (SCHED ? 1 : 0);
     const int lane = threadIdx.x & 63;
     // The partial loads go first: the A-operand loads wait for the token.
     const float2* pr = part + (size_t)b * nT;
@@ -643,7 +664,7 @@ __global__ __launch_bounds__(kMaxRank) void k_rnn_state(const typename DT::T* __
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
                              int gamma, int V, int r, int k, SeedArg seed, int32_t* tok, float* p, double* lse,
                              const float* z0, const void* wc, float* z_out, const void* Wt, void* H, void* ws,
-                             const WsLayout& lay, hipStream_t s)
+                             const WsLayout& lay, hipStream_t s, const SchedArg* sched)
 {
     const ConfOut co{ z0, wc, z_out };
     if (H) {  // RNN head: this step's operand rows
@@ -679,13 +700,18 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     }
     if (wave_locate) {
         const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32, wag = ag_path && k < gamma;
-        auto kern = small ? (k8 ? (wag ? k_draft_locate_bf16<8, 32, true> : k_draft_locate_bf16<8, 32, false>)
+        const bool sch = sched != nullptr && k == gamma;  // (wag is false at k = gamma)
+        auto kern = sch ? (small ? (k8 ? k_draft_locate_bf16<8, 32, false, true> : k_draft_locate_bf16<0, 32, false, true>)
+                                 : (k8 ? k_draft_locate_bf16<8, 64, false, true> : k_draft_locate_bf16<0, 64, false, true>))
+                  : small ? (k8 ? (wag ? k_draft_locate_bf16<8, 32, true> : k_draft_locate_bf16<8, 32, false>)
                                 : k_draft_locate_bf16<0, 32, false>)
                           : (k8 ? (wag ? k_draft_locate_bf16<8, 64, true> : k_draft_locate_bf16<8, 64, false>)
                                 : k_draft_locate_bf16<0, 64, false>);
-        launch_timed(K_DRAFT_LOCATE, kern, dim3(B), dim3(wag ? 128 : 64), s, static_cast<const uint16_t*>(L),
-                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
-                           ag, static_cast<const uint16_t*>(H), B, gamma, V, r, k, nT, nM, S, seed, co);
+        const SchedArg sa = sch ? *sched : SchedArg{ nullptr, nullptr, 0, nullptr, nullptr };
+        launch_timed(K_DRAFT_LOCATE, kern, dim3(B + (sch ? 1 : 0)), dim3(sch ? kSchedWgThreads : wag ? 128 : 64), s,
+                     static_cast<const uint16_t*>(L), static_cast<const uint16_t*>(A),
+                     static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part, ag, static_cast<const uint16_t*>(H), B,
+                     gamma, V, r, k, nT, nM, S, seed, co, sa);
     } else if (dtype == 1) {
         launch_timed(K_DRAFT_LOCATE, k_draft_locate<Bf16>, dim3(B), dim3(kThreads), s, static_cast<const uint16_t*>(L),
                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part,
@@ -695,6 +721,11 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
                            static_cast<const float*>(A), static_cast<const float*>(Bm), x0, tok, p, lse, part,
                            static_cast<const float*>(H), B, gamma, V, r, k, nT, seed, co);
     return hipGetLastError();
+}
+
+bool draft_step_can_schedule(int dtype, int B, int gamma, int V)
+{
+    return dtype == 1 && n_tiles(dtype, V) <= 64 * 64 && (long long)B * gamma <= kSchedMaxKeys;
 }
 
 }  // namespace dspark

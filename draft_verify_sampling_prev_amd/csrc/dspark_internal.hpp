@@ -104,10 +104,23 @@ inline void launch_timed(int id, F kernel, dim3 grid, dim3 block, hipStream_t s,
 // Wt/H (both null, or both set): the RNN head -- the step first writes the
 // state h_k = tanh(W h_{k-1} + A[x_{k-1}]) into row (b, k-1) of H, which
 // then replaces A[x_{k-1}] as the operand.
+// sched (non-null only at k = gamma, and only when draft_step_can_schedule):
+// the budget schedule of dspark_schedule runs as one extra workgroup of the
+// step's locate launch.
+struct SchedArg {
+    const float* z;      // [B][gamma] confidence logits
+    const float* temps;  // [gamma]
+    long long admit;     // min(budget, B*gamma)
+    float* surv;         // [B][gamma] out
+    int32_t* len;        // [B] out
+};
 hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0,
                              int B, int gamma, int V, int r, int k, SeedArg seed, int32_t* tok, float* p,
                              double* lse, const float* z0, const void* wc, float* z_out, const void* Wt, void* H,
-                             void* ws, const WsLayout& lay, hipStream_t s);
+                             void* ws, const WsLayout& lay, hipStream_t s, const SchedArg* sched = nullptr);
+// Whether the last draft step's locate launch can carry the budget schedule
+// (bf16, the one-wave locate, Markov head, B*gamma keys within its LDS).
+bool draft_step_can_schedule(int dtype, int B, int gamma, int V);
 
 hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,
                            int32_t* len, hipStream_t s);

@@ -161,6 +161,31 @@ int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dspark_markov_draft_sched -- dspark_markov_draft followed by
+ * dspark_schedule(z, temps, B, gamma, budget, survival, verify_len), in one
+ * call.  Given z as an input (not the Markov-conditioned z of
+ * dspark_markov_draft_conf, which depends on the sampled tokens: paperlayer.ai
+ * summary, Appendix A), the budget schedule needs nothing the draft steps
+ * produce, and it runs beside them, as the production scheduler runs
+ * asynchronously to drafting (paperlayer.ai summary, section 5.2): with bf16
+ * logits, V <= 262144 (at most 4096 tiles of 64 columns) and
+ * B*gamma <= 7680 it runs as one extra workgroup of the last draft step's
+ * locate launch, beside the per-request work; otherwise it is launched after
+ * the draft steps.  Outputs
+ * are bit-identical to the two separate calls in either case.
+ *
+ *   z, temps, budget, survival, verify_len  as in dspark_schedule, except that
+ *              z and temps must be non-null (no given-survival form)
+ * Other arguments, limits and errors as dspark_markov_draft and
+ * dspark_schedule; on an argument error nothing is enqueued.
+ */
+int dspark_markov_draft_sched(int dtype, const void* L, const void* A, const void* Bm, const int32_t* x0, int B,
+                              int gamma, int V, int r, uint64_t seed, const uint64_t* seed_dev, const float* z,
+                              const float* temps, int64_t budget, int32_t* draft_tok, float* draft_p,
+                              double* draft_lse, float* survival, int32_t* verify_len, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
  * dspark_rnn_draft -- the draft steps with the RNN sequential head instead of
  * the Markov head (menfem.com note, Key Contributions: the head variant that
  * keeps the whole in-block prefix history in a recurrent state).  Before

@@ -39,7 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_python_binding_has_the_same_names():
-    for n in ("dspark_markov_draft", "dspark_markov_draft_conf", "dspark_markov_draft_noalloc", "dspark_rnn_draft",
+    for n in ("dspark_markov_draft", "dspark_markov_draft_conf", "dspark_markov_draft_noalloc",
+              "dspark_markov_draft_sched", "dspark_rnn_draft",
               "dspark_rnn_verify",
               "dspark_schedule", "dspark_schedule_objective",
               "dspark_schedule_threshold",
