@@ -67,13 +67,16 @@ def vocab_passes(wl, kern: dict, adm: float, rej: float) -> dict:
     Algorithmic bytes (the method's minimum, s bytes per element): draft tiles, per launch the step's L rows,
     Bm and the A rows; target rows, s*V per verified draft (adm per step); residual tiles,
     Bm plus the target row and the draft-L row of each request with a rejection (rej per step); bonus rows,
-    s*V per request without one.  Flops: 2*r*V per draft row and per residual row.  Times are the per-kernel
+    s*V per request without one (counted under the accept launch, which computes them for every request).  Flops: 2*r*V per draft row and per residual row.  Times are the per-kernel
     averages of the timed pass (events bound to each kernel's own dispatch)."""
     s = 2 if wl.dtype == "bf16" else 4
     B, V, r, gamma = wl.B, wl.V, wl.r, wl.gamma
     tile_b, _, _ = draft_tiles_bytes_flops(wl)
     per_launch = {"draft_tiles": tile_b, "target_partials": s * V * adm,
                   "resid_tiles": s * (r * V + 2 * rej * V), "bonus_partials": s * V * (B - rej)}
+    if "bonus_partials" not in kern:
+        # The bonus rows ride in the accept launch (read there for all B requests; the method needs B - rej).
+        per_launch["accept"] = per_launch.pop("bonus_partials")
     out = {}
     tot_b = tot_us = 0.0
     for name, byts in per_launch.items():

@@ -13,15 +13,15 @@
 // device, so the sequence can be captured in a HIP graph):
 //   k_row_partials (target)  grid = chunks x (B*gamma): row (b,k) with
 //                            k <= ell_b -> chunk max and sum of exp (fp64).
-//   k_lse_accept             one wave per request: lse_t and p_t(x_k) of its
+//   k_accept_bonus           one wave per request: lse_t and p_t(x_k) of its
 //                            verified rows, accept draws, first rejection;
 //                            appends the requests with a rejection to the
-//                            residual list.
+//                            residual list.  In the same launch, chunks x B
+//                            workgroups: target row ell_b + 1 of every request
+//                            (the bonus row) -> chunk max and sum of exp.
 //   k_resid_tiles            Markov MFMA tiles of the rejected draft rows
 //                            fused with the target row: per tile sums of
 //                            max(0, p_t - p_d) and of p_t.
-//   k_row_partials (bonus)   grid = chunks x B: target row ell_b + 1 of
-//                            requests without a rejection.
 //   k_final                  one workgroup per request: locate and sample
 //                            the last token, write the emitted tokens.
 #include <limits.h>
@@ -70,28 +70,24 @@ __device__ __forceinline__ float resid_weight(float f, float t, float cd, float 
 // every element loaded once with 16-byte loads and kept in registers between
 // the max and the sum.
 // ---------------------------------------------------------------------------
+// Rows: kRowTarget, row = b*gamma + k-1 for k <= ell_b; kRowBonus, row = b,
+// target row ell_b of every request (the bonus row; it is used only when all
+// ell_b drafts are accepted, which is not known yet when it is computed).
+constexpr int kRowTarget = 0, kRowBonus = 1;
+
 template <class DT>
-__global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T* __restrict__ Tg,
-                                                           const int32_t* __restrict__ len,
-                                                           const int32_t* __restrict__ accepted, int B, int gamma,
-                                                           int V, int nC, int bonus, float* __restrict__ om,
-                                                           double* __restrict__ os, int32_t* __restrict__ clear_count)
+__device__ __forceinline__ void row_partials(const typename DT::T* __restrict__ Tg, const int32_t* __restrict__ len,
+                                             int gamma, int V, int nC, int mode, int c, int row,
+                                             float* __restrict__ om, double* __restrict__ os, BlockScratch& bs)
 {
-    __shared__ BlockScratch bs;
-    const int c = blockIdx.x;
-    const int row = blockIdx.y;
-    // The residual-list counter of the accept kernel, which runs next on the stream.
-    if (clear_count && c == 0 && row == 0 && threadIdx.x == 0) *clear_count = 0;
     int b, trow;
-    if (!bonus) {
+    if (mode == kRowTarget) {
         b = row / gamma;
         trow = row - b * gamma;
-        if (trow >= clamp_len(len[b], gamma)) return;
+        if (trow >= clamp_len(len[b], gamma)) return;  // uniform over the workgroup
     } else {
         b = row;
-        const int l = clamp_len(len[b], gamma);
-        if (accepted[b] < l) return;
-        trow = l;
+        trow = clamp_len(len[b], gamma);
     }
     const typename DT::T* x = Tg + ((size_t)b * (gamma + 1) + trow) * V;
     constexpr int PV = DT::kPerVec;
@@ -133,6 +129,18 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T*
     }
 }
 
+template <class DT>
+__global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T* __restrict__ Tg,
+                                                           const int32_t* __restrict__ len, int gamma, int V, int nC,
+                                                           float* __restrict__ om, double* __restrict__ os,
+                                                           int32_t* __restrict__ clear_count)
+{
+    __shared__ BlockScratch bs;
+    // The residual-list counter of the accept kernel, which runs next on the stream.
+    if (clear_count && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *clear_count = 0;
+    row_partials<DT>(Tg, len, gamma, V, nC, kRowTarget, blockIdx.x, blockIdx.y, om, os, bs);
+}
+
 // ---------------------------------------------------------------------------
 // Target log-normalisers, p_t(x_k) and the accept scan: one wave per request.
 //
@@ -146,18 +154,19 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T*
 // (every row's residual tile results depend only on the row).
 // ---------------------------------------------------------------------------
 constexpr int kAcceptWaves = 4;
+static_assert(64 * kAcceptWaves == kThreads, "the accept and row-pass workgroups share one launch");
 
 template <class DT>
-__global__ __launch_bounds__(64 * kAcceptWaves) void k_lse_accept(
+__device__ __forceinline__ void lse_accept(
     const typename DT::T* __restrict__ Tg, const float* __restrict__ pd, const int32_t* __restrict__ len,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const float* __restrict__ tgm,
     const double* __restrict__ tgs, int B, int gamma, int V, int nC, int rnn, SeedArg seed_arg,
     int32_t* __restrict__ accepted, int32_t* __restrict__ n_out, float* __restrict__ target_p,
     double* __restrict__ lse_t, int32_t* __restrict__ resid_idx, int4* __restrict__ resid_list,
-    int32_t* __restrict__ resid_count)
+    int32_t* __restrict__ resid_count, int wg)
 {
     const uint64_t seed = seed_of(seed_arg);
-    const int b = blockIdx.x * kAcceptWaves + (int)(threadIdx.x >> 6);
+    const int b = wg * kAcceptWaves + (int)(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (b >= B) return;
     const size_t row0 = (size_t)b * gamma;
@@ -246,8 +255,35 @@ __global__ __launch_bounds__(64 * kAcceptWaves) void k_lse_accept(
     }
 }
 
+// The accept scan (workgroups 0 .. nAcc-1, one wave per request) and, in the
+// same launch, the bonus row's chunk partials of every request (workgroup
+// nAcc + b*nC + c: chunk c of target row ell_b of request b).  The bonus row
+// is needed only where all ell_b drafts are accepted, but its index does not
+// depend on the accept scan, so it is computed for every request while the
+// scan's dependent loads are in flight, instead of by a launch of its own
+// after the scan.
+template <class DT>
+__global__ __launch_bounds__(kThreads) void k_accept_bonus(
+    const typename DT::T* __restrict__ Tg, const float* __restrict__ pd, const int32_t* __restrict__ len,
+    const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const float* __restrict__ tgm,
+    const double* __restrict__ tgs, int B, int gamma, int V, int nC, int rnn, SeedArg seed_arg,
+    int32_t* __restrict__ accepted, int32_t* __restrict__ n_out, float* __restrict__ target_p,
+    double* __restrict__ lse_t, int32_t* __restrict__ resid_idx, int4* __restrict__ resid_list,
+    int32_t* __restrict__ resid_count, int nAcc, float* __restrict__ bm, double* __restrict__ bsum)
+{
+    __shared__ BlockScratch bs;
+    const int wg = blockIdx.x;
+    if (wg < nAcc) {
+        lse_accept<DT>(Tg, pd, len, x0, tok, tgm, tgs, B, gamma, V, nC, rnn, seed_arg, accepted, n_out, target_p,
+                       lse_t, resid_idx, resid_list, resid_count, wg);
+        return;
+    }
+    const int q = wg - nAcc, b = q / nC;
+    row_partials<DT>(Tg, len, gamma, V, nC, kRowBonus, q - b * nC, b, bm, bsum, bs);
+}
+
 // Row m of the compacted residual list: request b at its first rejected
-// position ks, conditioned on token x (x_{ks-1}), as written by k_lse_accept.
+// position ks, conditioned on token x (x_{ks-1}), as written by the accept scan.
 // Every field is clamped into range, so a row read past the count (stale
 // workspace) still addresses valid memory; such rows are never reported.
 struct ResidRow {
@@ -872,11 +908,11 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     double* bsum = reinterpret_cast<double*>(w + lay.bon_s);
     const int nT = n_tiles(std::is_same<DT, Bf16>::value ? 1 : 0, V), nC = n_chunks(V);
 
-    launch_timed(K_TARGET_PARTIALS, k_row_partials<DT>, dim3(nC, B * gamma), dim3(kThreads), s, Tg, len, accepted, B, gamma, V,
-                       nC, 0, tgm, tgs, rcnt);
-    launch_timed(K_ACCEPT, k_lse_accept<DT>, dim3((B + kAcceptWaves - 1) / kAcceptWaves), dim3(64 * kAcceptWaves), s,
-                       Tg, pd, len, x0, tok, tgm, tgs, B, gamma, V, nC, rnn, seed, accepted, n_out, target_p, lse_t,
-                       ridx, rlist, rcnt);
+    launch_timed(K_TARGET_PARTIALS, k_row_partials<DT>, dim3(nC, B * gamma), dim3(kThreads), s, Tg, len, gamma, V, nC,
+                 tgm, tgs, rcnt);
+    const int nAcc = (B + kAcceptWaves - 1) / kAcceptWaves;
+    launch_timed(K_ACCEPT, k_accept_bonus<DT>, dim3(nAcc + nC * B), dim3(kThreads), s, Tg, pd, len, x0, tok, tgm, tgs,
+                 B, gamma, V, nC, rnn, seed, accepted, n_out, target_p, lse_t, ridx, rlist, rcnt, nAcc, bm, bsum);
     if (std::is_same<DT, Bf16>::value) {
         const int nM = (B + kTileRows - 1) / kTileRows;
         const int S = tile_slots(nT, nM, cu_count(), kResPartTiles);
@@ -892,8 +928,6 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
                            reinterpret_cast<const float*>(A), reinterpret_cast<const float*>(Bm), x0, tok, lse_d,
                            lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, nA, rpart);
     }
-    launch_timed(K_BONUS_PARTIALS, k_row_partials<DT>, dim3(nC, B), dim3(kThreads), s, Tg, len, accepted, B, gamma, V, nC, 1,
-                       bm, bsum, (int32_t*)nullptr);
     if (std::is_same<DT, Bf16>::value && nT <= 64 * 64 && nC <= 64 * 4) {
         const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32;
         auto kern = small ? (k8 ? k_final_bf16<8, 32> : k_final_bf16<0, 32>)
