@@ -16,12 +16,15 @@
 //   k_accept_bonus           one wave per request: lse_t and p_t(x_k) of its
 //                            verified rows, accept draws, first rejection;
 //                            appends the requests with a rejection to the
-//                            residual list.  In the same launch, chunks x B
-//                            workgroups: target row ell_b + 1 of every request
-//                            (the bonus row) -> chunk max and sum of exp.
+//                            residual list.  In the same launch, while
+//                            B*V*s <= 80 MB, chunks x B workgroups: target
+//                            row ell_b + 1 of every request (the bonus row)
+//                            -> chunk max and sum of exp.
 //   k_resid_tiles            Markov MFMA tiles of the rejected draft rows
 //                            fused with the target row: per tile sums of
 //                            max(0, p_t - p_d) and of p_t.
+//   k_row_partials (bonus)   otherwise: grid = chunks x B, the bonus rows of
+//                            the requests without a rejection.
 //   k_final                  one workgroup per request: locate and sample
 //                            the last token, write the emitted tokens.
 #include <limits.h>
@@ -70,15 +73,18 @@ __device__ __forceinline__ float resid_weight(float f, float t, float cd, float 
 // every element loaded once with 16-byte loads and kept in registers between
 // the max and the sum.
 // ---------------------------------------------------------------------------
-// Rows: kRowTarget, row = b*gamma + k-1 for k <= ell_b; kRowBonus, row = b,
-// target row ell_b of every request (the bonus row; it is used only when all
-// ell_b drafts are accepted, which is not known yet when it is computed).
-constexpr int kRowTarget = 0, kRowBonus = 1;
+// Rows: kRowTarget, row = b*gamma + k-1 for k <= ell_b; kRowBonusAll, row = b,
+// target row ell_b of every request (the bonus row, computed before it is
+// known whether all ell_b drafts are accepted, the only case that uses it);
+// kRowBonusAccepted, the same row of the requests whose drafts were all
+// accepted (after the accept scan).
+constexpr int kRowTarget = 0, kRowBonusAll = 1, kRowBonusAccepted = 2;
 
 template <class DT>
 __device__ __forceinline__ void row_partials(const typename DT::T* __restrict__ Tg, const int32_t* __restrict__ len,
-                                             int gamma, int V, int nC, int mode, int c, int row,
-                                             float* __restrict__ om, double* __restrict__ os, BlockScratch& bs)
+                                             const int32_t* __restrict__ accepted, int gamma, int V, int nC, int mode,
+                                             int c, int row, float* __restrict__ om, double* __restrict__ os,
+                                             BlockScratch& bs)
 {
     int b, trow;
     if (mode == kRowTarget) {
@@ -88,6 +94,7 @@ __device__ __forceinline__ void row_partials(const typename DT::T* __restrict__ 
     } else {
         b = row;
         trow = clamp_len(len[b], gamma);
+        if (mode == kRowBonusAccepted && accepted[b] < trow) return;
     }
     const typename DT::T* x = Tg + ((size_t)b * (gamma + 1) + trow) * V;
     constexpr int PV = DT::kPerVec;
@@ -129,16 +136,18 @@ __device__ __forceinline__ void row_partials(const typename DT::T* __restrict__ 
     }
 }
 
+// Grid chunks x rows (target: rows B*gamma; bonus: rows B).
 template <class DT>
 __global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T* __restrict__ Tg,
-                                                           const int32_t* __restrict__ len, int gamma, int V, int nC,
-                                                           float* __restrict__ om, double* __restrict__ os,
-                                                           int32_t* __restrict__ clear_count)
+                                                           const int32_t* __restrict__ len,
+                                                           const int32_t* __restrict__ accepted, int gamma, int V,
+                                                           int nC, int mode, float* __restrict__ om,
+                                                           double* __restrict__ os, int32_t* __restrict__ clear_count)
 {
     __shared__ BlockScratch bs;
     // The residual-list counter of the accept kernel, which runs next on the stream.
     if (clear_count && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *clear_count = 0;
-    row_partials<DT>(Tg, len, gamma, V, nC, kRowTarget, blockIdx.x, blockIdx.y, om, os, bs);
+    row_partials<DT>(Tg, len, accepted, gamma, V, nC, mode, blockIdx.x, blockIdx.y, om, os, bs);
 }
 
 // ---------------------------------------------------------------------------
@@ -154,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void k_row_partials(const typename DT::T*
 // (every row's residual tile results depend only on the row).
 // ---------------------------------------------------------------------------
 constexpr int kAcceptWaves = 4;
+constexpr double kBonusInAcceptBytes = 80.0 * 1024 * 1024;  // B * V * element size
 static_assert(64 * kAcceptWaves == kThreads, "the accept and row-pass workgroups share one launch");
 
 template <class DT>
@@ -255,13 +265,14 @@ __device__ __forceinline__ void lse_accept(
     }
 }
 
-// The accept scan (workgroups 0 .. nAcc-1, one wave per request) and, in the
-// same launch, the bonus row's chunk partials of every request (workgroup
-// nAcc + b*nC + c: chunk c of target row ell_b of request b).  The bonus row
-// is needed only where all ell_b drafts are accepted, but its index does not
-// depend on the accept scan, so it is computed for every request while the
-// scan's dependent loads are in flight, instead of by a launch of its own
-// after the scan.
+// The accept scan (workgroups 0 .. nAcc-1, one wave per request) and, when
+// the grid has more workgroups, in the same launch the bonus row's chunk
+// partials of every request (workgroup nAcc + b*nC + c: chunk c of target row
+// ell_b of request b).  The bonus row is needed only where all ell_b drafts
+// are accepted, but its index does not depend on the accept scan, so it can
+// be read while the scan's dependent loads are in flight instead of by a
+// launch of its own after the scan (the launcher does so while that read is
+// small; otherwise the rows that are needed are read after the scan).
 template <class DT>
 __global__ __launch_bounds__(kThreads) void k_accept_bonus(
     const typename DT::T* __restrict__ Tg, const float* __restrict__ pd, const int32_t* __restrict__ len,
@@ -279,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_accept_bonus(
         return;
     }
     const int q = wg - nAcc, b = q / nC;
-    row_partials<DT>(Tg, len, gamma, V, nC, kRowBonus, q - b * nC, b, bm, bsum, bs);
+    row_partials<DT>(Tg, len, accepted, gamma, V, nC, kRowBonusAll, q - b * nC, b, bm, bsum, bs);
 }
 
 // Row m of the compacted residual list: request b at its first rejected
@@ -908,11 +919,17 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     double* bsum = reinterpret_cast<double*>(w + lay.bon_s);
     const int nT = n_tiles(std::is_same<DT, Bf16>::value ? 1 : 0, V), nC = n_chunks(V);
 
-    launch_timed(K_TARGET_PARTIALS, k_row_partials<DT>, dim3(nC, B * gamma), dim3(kThreads), s, Tg, len, gamma, V, nC,
-                 tgm, tgs, rcnt);
+    launch_timed(K_TARGET_PARTIALS, k_row_partials<DT>, dim3(nC, B * gamma), dim3(kThreads), s, Tg, len, accepted,
+                 gamma, V, nC, kRowTarget, tgm, tgs, rcnt);
+    // Bonus rows inside the accept launch while reading them for every
+    // request stays small next to the launch it saves (measured on MI355X:
+    // B = 256, V = 129280 bf16, 66 MB: 2 us per step faster; B = 1024, 265 MB:
+    // 33-60 us slower).
+    const bool bonus_in_accept = (double)B * V * sizeof(T) <= kBonusInAcceptBytes;
     const int nAcc = (B + kAcceptWaves - 1) / kAcceptWaves;
-    launch_timed(K_ACCEPT, k_accept_bonus<DT>, dim3(nAcc + nC * B), dim3(kThreads), s, Tg, pd, len, x0, tok, tgm, tgs,
-                 B, gamma, V, nC, rnn, seed, accepted, n_out, target_p, lse_t, ridx, rlist, rcnt, nAcc, bm, bsum);
+    launch_timed(K_ACCEPT, k_accept_bonus<DT>, dim3(nAcc + (bonus_in_accept ? nC * B : 0)), dim3(kThreads), s, Tg, pd,
+                 len, x0, tok, tgm, tgs, B, gamma, V, nC, rnn, seed, accepted, n_out, target_p, lse_t, ridx, rlist, rcnt,
+                 nAcc, bm, bsum);
     if (std::is_same<DT, Bf16>::value) {
         const int nM = (B + kTileRows - 1) / kTileRows;
         const int S = tile_slots(nT, nM, cu_count(), kResPartTiles);
@@ -928,6 +945,9 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
                            reinterpret_cast<const float*>(A), reinterpret_cast<const float*>(Bm), x0, tok, lse_d,
                            lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, nA, rpart);
     }
+    if (!bonus_in_accept)
+        launch_timed(K_BONUS_PARTIALS, k_row_partials<DT>, dim3(nC, B), dim3(kThreads), s, Tg, len, accepted, gamma, V,
+                     nC, kRowBonusAccepted, bm, bsum, (int32_t*)nullptr);
     if (std::is_same<DT, Bf16>::value && nT <= 64 * 64 && nC <= 64 * 4) {
         const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32;
         auto kern = small ? (k8 ? k_final_bf16<8, 32> : k_final_bf16<0, 32>)
