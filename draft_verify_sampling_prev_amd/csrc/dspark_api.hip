@@ -204,7 +204,7 @@ static int markov_draft_impl(int dtype, const void* L, const void* A, const void
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int k = 1; k <= gamma; ++k) {
         hipError_t e = launch_draft_step(dtype, L, A, Bm, x0, B, gamma, V, r, k, seed, draft_tok, draft_p, draft_lse,
-                                         z0, wc, z_out, Wt, H, ws, lay, s, k == gamma ? sched : nullptr);
+                                         z0, wc, z_out, Wt, H, ws, lay, s, k == 1 || k == gamma ? sched : nullptr);
         if (e != hipSuccess) return hip_status(e, "draft launch");
     }
     return DSPARK_OK;
@@ -230,8 +230,9 @@ int dspark_markov_draft_sched(int dtype, const void* L, const void* A, const voi
     if (B > 0 && (!z || !temps || !survival || !verify_len)) return fail(DSPARK_ERR_INVALID_ARG, "null pointer argument");
     const int64_t n = (int64_t)B * gamma;
     const SchedArg sa{ z, temps, (long long)(budget < n ? budget : n), survival, verify_len };
-    // The schedule rides in the last locate launch where that launch can
-    // carry it; otherwise it is launched after the draft.
+    // The schedule rides in a draft launch where one can carry it (the first
+    // tile launch or the last locate launch); otherwise it is launched after
+    // the draft.
     const bool fused = draft_step_can_schedule(dtype, B, gamma, V);
     const int rc = markov_draft_impl(dtype, L, A, Bm, x0, B, gamma, V, r, SeedArg{ seed, seed_dev }, nullptr, nullptr,
                                      draft_tok, draft_p, draft_lse, nullptr, nullptr, nullptr, ws, ws_bytes, stream,

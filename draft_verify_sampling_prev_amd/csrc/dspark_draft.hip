@@ -155,12 +155,18 @@ constexpr int kPartTiles = 12;  // tiles per slot whose partials fit the LDS sta
 // so every wave has rows and the body has no branch.  Otherwise a wave whose
 // rows all lie past the batch skips the MFMAs and only issues its share of
 // the Bm DMA (the two paths then leave the compiler less exact waits).
+// The budget schedule in one workgroup of a draft launch (dspark_markov_draft_sched):
+// its scratch first, then the keys, in a 32 KB LDS tile buffer of that launch.
+constexpr int kSchedKeysOffset = 2048;  // bytes
+constexpr int kSchedMaxKeys = (kBmTileBytes - kSchedKeysOffset) / 4;
+static_assert(sizeof(SelectScratch<64 * kTileWaves>) <= kSchedKeysOffset, "select scratch");
+
 template <int KS, bool FULL>
 __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const uint16_t* __restrict__ ag,
     const uint16_t* __restrict__ H, int B, int gamma, int V, int r, int k, int nT, int nM, int S,
-    float2* __restrict__ part)
+    float2* __restrict__ part, SchedArg sa)
 {
     constexpr int NW = kTileWaves, R = kTileRows;
     __shared__ __attribute__((aligned(1024))) char s0[kBmTileBytes];
@@ -168,6 +174,15 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     __shared__ __attribute__((aligned(1024))) char s2[kBmTileBytes];
     __shared__ __attribute__((aligned(1024))) char s3[kBmTileBytes];
     __shared__ unsigned long long stage[kPartTiles][R];  // float2 pairs, stored as one 64-bit word each
+
+    // A workgroup past the S * nM tile workgroups (launched only with the
+    // schedule, see launch_draft_step) runs the budget schedule.
+    if (blockIdx.x == S * nM) {
+        budget_select<64 * NW>(sa.z, sa.temps, B, gamma, sa.admit, sa.surv, sa.len,
+                               reinterpret_cast<uint32_t*>(s0 + kSchedKeysOffset),
+                               *reinterpret_cast<SelectScratch<64 * NW>*>(s0));
+        return;
+    }
 
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int mblk = lid % nM, slot = lid / nM;
@@ -467,8 +482,6 @@ __device__ __forceinline__ void prefetch_first_tile(const uint16_t* __restrict__
 // the locate's LDS tile buffer.  (Measured on MI355X: 512 threads were
 // slower than 256, and index 0 was 0.3-0.7 us per step faster than index B.)
 constexpr int kSchedWgThreads = 256;
-constexpr int kSchedKeysOffset = 2048;  // bytes; SelectScratch first
-constexpr int kSchedMaxKeys = (kBmTileBytes - kSchedKeysOffset) / 4;
 static_assert(sizeof(SelectScratch<kSchedWgThreads>) <= kSchedKeysOffset, "select scratch");
 
 template <int KS, int PER, bool AG, bool SCHED = false>
@@ -685,13 +698,22 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     // bf16 tile grid: nM row blocks x S persistent slots.
     const int nM = (B + kTileRows - 1) / kTileRows;
     const int S = tile_slots(nT, nM, cu_count(), kPartTiles);
+    // The schedule rides in the first tile launch when one slot fewer leaves
+    // every slot's tile count as it is (the launch takes as long, and the
+    // freed CU runs the schedule), else in the last locate launch.
+    const bool first_tiles_sched = schedule_in_first_tiles(dtype, B, gamma, V);
+    const bool sch_tiles = sched != nullptr && k == 1 && first_tiles_sched;
+    const bool sch_locate = sched != nullptr && k == gamma && !first_tiles_sched;
+    const SchedArg none{ nullptr, nullptr, 0, nullptr, nullptr };
     if (dtype == 1) {
         auto kern = (r + 31) / 32 == 8 ? (B % kTileRows == 0 ? k_draft_tiles_bf16<8, true> : k_draft_tiles_bf16<8, false>)
                                        : k_draft_tiles_bf16<0, false>;
-        launch_timed(K_DRAFT_TILES, kern, dim3(S * nM), dim3(64 * kTileWaves), s, static_cast<const uint16_t*>(L),
-                           static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bm), x0, tok,
-                           static_cast<const uint16_t*>(ag_path && k >= 2 ? ag : nullptr),
-                           static_cast<const uint16_t*>(H), B, gamma, V, r, k, nT, nM, S, part);
+        const int St = sch_tiles ? S - 1 : S;
+        launch_timed(K_DRAFT_TILES, kern, dim3(St * nM + (sch_tiles ? 1 : 0)), dim3(64 * kTileWaves), s,
+                     static_cast<const uint16_t*>(L), static_cast<const uint16_t*>(A),
+                     static_cast<const uint16_t*>(Bm), x0, tok,
+                     static_cast<const uint16_t*>(ag_path && k >= 2 ? ag : nullptr), static_cast<const uint16_t*>(H),
+                     B, gamma, V, r, k, nT, nM, St, part, sch_tiles ? *sched : none);
     } else {
         const int nM32 = (B + 255) / 256;
         launch_timed(K_DRAFT_TILES, k_draft_tiles_f32, dim3(nT * nM32), dim3(kThreads), s, static_cast<const float*>(L),
@@ -700,14 +722,14 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     }
     if (wave_locate) {
         const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32, wag = ag_path && k < gamma;
-        const bool sch = sched != nullptr && k == gamma;  // (wag is false at k = gamma)
+        const bool sch = sch_locate;  // (wag is false at k = gamma)
         auto kern = sch ? (small ? (k8 ? k_draft_locate_bf16<8, 32, false, true> : k_draft_locate_bf16<0, 32, false, true>)
                                  : (k8 ? k_draft_locate_bf16<8, 64, false, true> : k_draft_locate_bf16<0, 64, false, true>))
                   : small ? (k8 ? (wag ? k_draft_locate_bf16<8, 32, true> : k_draft_locate_bf16<8, 32, false>)
                                 : k_draft_locate_bf16<0, 32, false>)
                           : (k8 ? (wag ? k_draft_locate_bf16<8, 64, true> : k_draft_locate_bf16<8, 64, false>)
                                 : k_draft_locate_bf16<0, 64, false>);
-        const SchedArg sa = sch ? *sched : SchedArg{ nullptr, nullptr, 0, nullptr, nullptr };
+        const SchedArg sa = sch ? *sched : none;
         launch_timed(K_DRAFT_LOCATE, kern, dim3(B + (sch ? 1 : 0)), dim3(sch ? kSchedWgThreads : wag ? 128 : 64), s,
                      static_cast<const uint16_t*>(L), static_cast<const uint16_t*>(A),
                      static_cast<const uint16_t*>(Bm), x0, tok, p, lse, part, ag, static_cast<const uint16_t*>(H), B,
@@ -723,9 +745,17 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     return hipGetLastError();
 }
 
+bool schedule_in_first_tiles(int dtype, int B, int gamma, int V)
+{
+    if (dtype != 1 || (long long)B * gamma > kSchedMaxKeys || B > kTileRows) return false;
+    const int nT = n_tiles(dtype, V), S = tile_slots(nT, 1, cu_count(), kPartTiles);
+    return S > 1 && (nT + S - 2) / (S - 1) == (nT + S - 1) / S;
+}
+
 bool draft_step_can_schedule(int dtype, int B, int gamma, int V)
 {
-    return dtype == 1 && n_tiles(dtype, V) <= 64 * 64 && (long long)B * gamma <= kSchedMaxKeys;
+    return dtype == 1 && (long long)B * gamma <= kSchedMaxKeys &&
+           (n_tiles(dtype, V) <= 64 * 64 || schedule_in_first_tiles(dtype, B, gamma, V));
 }
 
 }  // namespace dspark

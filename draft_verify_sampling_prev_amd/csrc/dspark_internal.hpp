@@ -104,9 +104,10 @@ inline void launch_timed(int id, F kernel, dim3 grid, dim3 block, hipStream_t s,
 // Wt/H (both null, or both set): the RNN head -- the step first writes the
 // state h_k = tanh(W h_{k-1} + A[x_{k-1}]) into row (b, k-1) of H, which
 // then replaces A[x_{k-1}] as the operand.
-// sched (non-null only at k = gamma, and only when draft_step_can_schedule):
+// sched (given at k = 1 and k = gamma, only when draft_step_can_schedule):
 // the budget schedule of dspark_schedule runs as one extra workgroup of the
-// step's locate launch.
+// first tile launch (schedule_in_first_tiles) or else of the last locate
+// launch.
 struct SchedArg {
     const float* z;      // [B][gamma] confidence logits
     const float* temps;  // [gamma]
@@ -118,8 +119,11 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
                              int B, int gamma, int V, int r, int k, SeedArg seed, int32_t* tok, float* p,
                              double* lse, const float* z0, const void* wc, float* z_out, const void* Wt, void* H,
                              void* ws, const WsLayout& lay, hipStream_t s, const SchedArg* sched = nullptr);
-// Whether the last draft step's locate launch can carry the budget schedule
-// (bf16, the one-wave locate, Markov head, B*gamma keys within its LDS).
+// Whether a draft launch can carry the budget schedule (bf16, Markov head,
+// B*gamma keys within a 32 KB LDS buffer): the first tile launch, when one
+// slot fewer leaves every slot's tile count unchanged (B <= 256), or the
+// last step's one-wave locate launch.
+bool schedule_in_first_tiles(int dtype, int B, int gamma, int V);
 bool draft_step_can_schedule(int dtype, int B, int gamma, int V);
 
 hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,

@@ -168,10 +168,11 @@ int dspark_markov_draft_conf(int dtype, const void* L, const void* A, const void
  * summary, Appendix A), the budget schedule needs nothing the draft steps
  * produce, and it runs beside them, as the production scheduler runs
  * asynchronously to drafting (paperlayer.ai summary, section 5.2): with bf16
- * logits, V <= 262144 (at most 4096 tiles of 64 columns) and
- * B*gamma <= 7680 it runs as one extra workgroup of the last draft step's
- * locate launch, beside the per-request work; otherwise it is launched after
- * the draft steps.  Outputs
+ * logits and B*gamma <= 7680 it runs as one extra workgroup of a draft
+ * launch -- of the first tile launch when B <= 256 and the tiles spread over
+ * one workgroup fewer need no more tiles per workgroup, else of the last
+ * step's locate launch when V <= 262144 (at most 4096 tiles of 64 columns);
+ * otherwise it is launched after the draft steps.  Outputs
  * are bit-identical to the two separate calls in either case.
  *
  *   z, temps, budget, survival, verify_len  as in dspark_schedule, except that

@@ -1,5 +1,8 @@
 """GPU parity of dspark_markov_draft_sched, the draft steps with the budget
-schedule carried by the last step's locate launch, through the C ABI.
+schedule carried by a draft launch, through the C ABI.  The schedule rides in
+the first tile launch when one slot fewer leaves every slot's tile count
+unchanged (B <= 256), else in the last locate launch, else (fp32, B*gamma
+above 7680) it is launched after the draft; cases cover all three.
 
 Every output is compared bit for bit with dspark_markov_draft followed by
 dspark_schedule on the same inputs (the two forms run the same selection code
@@ -23,7 +26,19 @@ from oracle import check
 
 pytestmark = pytest.mark.gpu
 
-FUSED_MAX_KEYS = 7680  # B*gamma the last locate launch can carry (its 32 KB LDS tile buffer)
+FUSED_MAX_KEYS = 7680  # B*gamma a draft launch can carry (a 32 KB LDS tile buffer)
+
+
+def _host(B, gamma, V, dtype="bf16"):
+    """Which launch carries the schedule, by the library's rule (slot count as bench.tile_slots)."""
+    import bench
+    if dtype != "bf16" or B * gamma > FUSED_MAX_KEYS:
+        return "separate"
+    nT = (V + 63) // 64
+    S = bench.tile_slots(nT, 1, torch.cuda.get_device_properties(0).multi_processor_count)
+    if B <= 256 and S > 1 and -(-nT // (S - 1)) == -(-nT // S):
+        return "first tiles"
+    return "last locate" if nT <= 64 * 64 else "separate"
 
 
 def _bits(a: np.ndarray) -> np.ndarray:
@@ -51,28 +66,33 @@ def _compare(fused, sep, z, temps, budget, what):
     assert np.array_equal(fused["ell"], oracle.select(fused["theta"], int(budget))), (what, budget)
 
 
-@pytest.mark.parametrize("B,gamma,V,r", [(64, 5, 8192, 256), (37, 4, 3000, 256), (300, 3, 1000, 24),
-                                         (1536, 5, 2048, 256)])
-def test_fused_schedule_matches_separate_calls(B, gamma, V, r):
+@pytest.mark.parametrize("B,gamma,V,r,where", [(64, 5, 8192, 256, "last locate"), (37, 4, 3000, 256, "last locate"),
+                                              (300, 3, 1000, 24, "last locate"),
+                                              (1536, 5, 2048, 256, "last locate"),
+                                              (64, 5, 40000, 256, "first tiles"), (200, 5, 40000, 24, "first tiles"),
+                                              (256, 1, 40000, 256, "first tiles")])
+def test_fused_schedule_matches_separate_calls(B, gamma, V, r, where):
     dev = torch.device("cuda:0")
     wl = synth.tiny(B=B, gamma=gamma, V=V, r=r, budget=1, dtype="bf16")
     inp = synth.make_inputs(wl)
     g = inp.to(dev)
     z, temps = inp.z.numpy(), inp.temps.numpy()
     N = B * gamma
-    assert N <= FUSED_MAX_KEYS
-    print(f"case B={B} gamma={gamma} V={V} r={r} N={N}", flush=True)
+    assert _host(B, gamma, V) == where
+    print(f"case B={B} gamma={gamma} V={V} r={r} N={N} ({where})", flush=True)
     for budget in sorted({0, 1, N // 3, N - 1, N, N + 5}):
         fused, sep = _both(g, budget, wl.philox_seed + budget)
         _compare(fused, sep, z, temps, budget, f"budget {budget}")
 
 
-def test_fused_schedule_ties_at_the_cut():
+@pytest.mark.parametrize("V,where", [(4096, "last locate"), (40000, "first tiles")])
+def test_fused_schedule_ties_at_the_cut(V, where):
     """Confidence logits quantised to four values, so whole groups of candidates share a survival and the cut
     falls inside a group: the tie is broken in (request, position) order on both paths."""
     dev = torch.device("cuda:0")
     B, gamma = 200, 5
-    wl = synth.tiny(B=B, gamma=gamma, V=4096, r=256, budget=1, dtype="bf16")
+    assert _host(B, gamma, V) == where
+    wl = synth.tiny(B=B, gamma=gamma, V=V, r=256, budget=1, dtype="bf16")
     inp = synth.make_inputs(wl)
     rng = np.random.default_rng(77)
     z = rng.choice(np.array([-1.0, 0.5, 2.0, 4.0], dtype=np.float32), size=(B, gamma))
@@ -102,7 +122,7 @@ def test_fallback_paths_match_separate_calls(case):
         wl = synth.tiny(B=96, gamma=5, V=2048, r=64, budget=1, dtype="f32")
     else:
         wl = synth.tiny(B=1600, gamma=5, V=1024, r=256, budget=1, dtype="bf16")
-        assert wl.B * wl.gamma > FUSED_MAX_KEYS
+    assert _host(wl.B, wl.gamma, wl.V, wl.dtype) == "separate"
     inp = synth.make_inputs(wl)
     g = inp.to(dev)
     N = wl.B * wl.gamma
@@ -115,7 +135,8 @@ def test_fused_step_against_the_oracle():
     """A whole step through the fused call and dspark_verify, every draft row and request checked against the
     oracle (teacher-forced), as the parity tests check the separate calls."""
     dev = torch.device("cuda:0")
-    wl = synth.tiny(B=48, gamma=5, V=3000, r=256, budget=150, dtype="bf16")
+    wl = synth.tiny(B=48, gamma=5, V=20000, r=256, budget=150, dtype="bf16")
+    assert _host(wl.B, wl.gamma, wl.V) == "first tiles"
     inp = synth.make_inputs(wl)
     g = inp.to(dev)
     seed = wl.philox_seed
@@ -135,6 +156,7 @@ def test_fused_schedule_at_the_headline_shape():
     """B = 256, gamma = 5, V = 129280, r = 256: the fused call against the separate calls, bit for bit."""
     dev = torch.device("cuda:0")
     wl = synth.dsv4()
+    assert _host(wl.B, wl.gamma, wl.V) == "first tiles"
     inp = synth.make_inputs(wl)
     g = inp.to(dev)
     for budget in (wl.budget, 1, wl.B * wl.gamma - 1):
