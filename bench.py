@@ -369,7 +369,7 @@ def main():
             dsp.dspark_markov_draft_conf(g.L, g.A, g.Bm, g.x0, seed, g.z, wc, ws=ws, out=(tok, p, lse, zc))
             schedule(budget)
         elif fused_schedule:
-            # The budget schedule needs only z: it runs inside the draft call, beside the last draft step.
+            # The budget schedule needs only z: it runs inside the draft call (in one of its launches).
             dsp.dspark_markov_draft_sched(g.L, g.A, g.Bm, g.x0, seed, g.z, g.temps, budget, ws=ws,
                                           out=(tok, p, lse), survival=theta, out_len=ell)
         else:
@@ -513,7 +513,7 @@ def main():
                    "schedule": args.schedule + (" (step time 1 ms + 1 us/token, capped at the budget)"
                                                 if args.schedule == "objective" else
                                                 f" (tau {args.tau})" if args.schedule == "threshold" else
-                                                " (inside the draft call, beside its last step)"
+                                                " (inside the draft call, dspark_markov_draft_sched)"
                                                 if fused_schedule and not args.confidence and args.head == "markov"
                                                 else "")
                    + (", z from the fused Markov-conditioned confidence head" if args.confidence else "")
