@@ -118,7 +118,8 @@ def kernel_source_digest() -> str:
 
 def tile_slots(nT: int, nM: int, cus: int, max_tiles: int = 12) -> int:
     """Persistent slots of the bf16 draft tile kernel (the library's rule): enough slots that each holds at most
-    max_tiles tiles, rounded up to whole rounds of one workgroup per compute unit per row block."""
+    max_tiles tiles (12; 36 for full-batch launches, B a multiple of 256, which write their staged partials out
+    every 12), rounded up to whole rounds of one workgroup per compute unit per row block."""
     per_round = max(cus // nM, 1)
     need = -(-nT // max_tiles)
     rounds = -(-need // per_round)
@@ -138,7 +139,7 @@ def pattern_ceiling(g, wl, dev, method_b: int, tile_us: float, reps: int = 8):
     lib.dspark_probe_time_tile_reads.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 6 + [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
     nT = (wl.V + 63) // 64
-    S = tile_slots(nT, 1, torch.cuda.get_device_properties(dev).multi_processor_count)
+    S = tile_slots(nT, 1, torch.cuda.get_device_properties(dev).multi_processor_count, 36 if wl.B == 256 else 12)
     sink = torch.empty(S * 512, dtype=torch.int32, device=dev)
     us = ctypes.c_double(0.0)
     rc = lib.dspark_probe_time_tile_reads(g.L.data_ptr(), g.Bm.data_ptr(), wl.B, wl.gamma, wl.V, wl.r, S, reps,

@@ -150,6 +150,9 @@ __global__ __launch_bounds__(kThreads) void k_draft_tiles_f32(const float* __res
 // waits on the register loads exact.
 // ---------------------------------------------------------------------------
 constexpr int kPartTiles = 12;  // tiles per slot whose partials fit the LDS staging
+// Full-batch launches (B a multiple of 256) may give a slot up to kManyTiles
+// tiles: the staging is then written out every kPartTiles tiles (MANY).
+constexpr int kManyTiles = 3 * kPartTiles;
 
 // FULL: every row block holds 256 rows of the batch (B a multiple of 256),
 // so every wave has rows and the body has no branch.  Otherwise a wave whose
@@ -161,7 +164,7 @@ constexpr int kSchedKeysOffset = 2048;  // bytes
 constexpr int kSchedMaxKeys = (kBmTileBytes - kSchedKeysOffset) / 4;
 static_assert(sizeof(SelectScratch<64 * kTileWaves>) <= kSchedKeysOffset, "select scratch");
 
-template <int KS, bool FULL>
+template <int KS, bool FULL, bool MANY = false>
 __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const uint16_t* __restrict__ ag,
@@ -227,8 +230,24 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
             for (int vb = 0; vb < 4; ++vb) v[vb] = fprev[vb][bb];
             float m, sum;
             row64_max_sum<decltype(tail)::value>(v, V - n0, &m, &sum);
-            stage[prev][32 * w + 16 * bb + c] = pack_f2(m, sum);
+            stage[MANY ? prev % kPartTiles : prev][32 * w + 16 * bb + c] = pack_f2(m, sum);
         }
+    };
+    // MANY (every wave active): the staged partials of tiles base .. base+11
+    // are made visible (LDS wait, barrier) and written out; then every memory
+    // operation of the wave is waited for, the loads in flight included, so
+    // the stage waits that follow see no extra operations in flight (the
+    // stores are complete) and keep their counts.  The staging rows are next
+    // written after the barrier that opens the following iteration, which
+    // every wave reaches only after its reads here.
+    auto flush = [&](int base) {
+        wait_lds();
+        barrier_lds();
+        for (int e = threadIdx.x; e < R * kPartTiles; e += 64 * NW) {
+            const int row = e / kPartTiles, j = e - row * kPartTiles;
+            part[(size_t)(m0 + row) * nT + t0 + (base + j) * ts] = unpack_f2(stage[j][row]);
+        }
+        wait_all_mem();
     };
     // L values of two tiles in flight: the four unrolled bodies alternate
     // between two register sets, so no copy waits on a load just issued.
@@ -263,6 +282,10 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
             if constexpr (decltype(has_prev)::value) {
                 epilogue(std::false_type{});
                 issue_fence();
+                if constexpr (MANY) {
+                    // Tile i-1 filled the staging: write tiles i-12 .. i-1 out.
+                    if (i % kPartTiles == 0) flush(i - kPartTiles);
+                }
             }
             floatx4 acc[4][2];
 #pragma unroll
@@ -360,10 +383,12 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     // the waves end.
     wait_lds();
     barrier_lds();
-    // Write the staged partials (consecutive threads take consecutive tiles of a row).
-    for (int e = threadIdx.x; e < R * cnt; e += 64 * NW) {
-        const int row = e / cnt, i = e - row * cnt;
-        if (m0 + row < B) part[(size_t)(m0 + row) * nT + t0 + i * ts] = unpack_f2(stage[i][row]);
+    // Write the staged partials (consecutive threads take consecutive tiles of
+    // a row): with MANY, those of the tiles since the last write-out.
+    const int base = MANY ? (cnt - 1) / kPartTiles * kPartTiles : 0, left = cnt - base;
+    for (int e = threadIdx.x; e < R * left; e += 64 * NW) {
+        const int row = e / left, i = e - row * left;
+        if (m0 + row < B) part[(size_t)(m0 + row) * nT + t0 + (base + i) * ts] = unpack_f2(stage[i][row]);
     }
     wait_all_mem();
 }
@@ -697,7 +722,8 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     const bool ag_path = wave_locate && r == kAgRank && !H;  // (RNN head: the next operand is the state, not A[x])
     // bf16 tile grid: nM row blocks x S persistent slots.
     const int nM = (B + kTileRows - 1) / kTileRows;
-    const int S = tile_slots(nT, nM, cu_count(), kPartTiles);
+    const int S = draft_tile_slots(B, nT);
+    const bool many = B % kTileRows == 0 && (nT + S - 1) / S > kPartTiles;
     // The schedule rides in the first tile launch when one slot fewer leaves
     // every slot's tile count as it is (the launch takes as long, and the
     // freed CU runs the schedule), else in the last locate launch.
@@ -706,8 +732,10 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     const bool sch_locate = sched != nullptr && k == gamma && !first_tiles_sched;
     const SchedArg none{ nullptr, nullptr, 0, nullptr, nullptr };
     if (dtype == 1) {
-        auto kern = (r + 31) / 32 == 8 ? (B % kTileRows == 0 ? k_draft_tiles_bf16<8, true> : k_draft_tiles_bf16<8, false>)
-                                       : k_draft_tiles_bf16<0, false>;
+        auto kern = (r + 31) / 32 == 8
+                        ? (many ? k_draft_tiles_bf16<8, true, true>
+                                : B % kTileRows == 0 ? k_draft_tiles_bf16<8, true> : k_draft_tiles_bf16<8, false>)
+                        : (many ? k_draft_tiles_bf16<0, true, true> : k_draft_tiles_bf16<0, false>);
         const int St = sch_tiles ? S - 1 : S;
         launch_timed(K_DRAFT_TILES, kern, dim3(St * nM + (sch_tiles ? 1 : 0)), dim3(64 * kTileWaves), s,
                      static_cast<const uint16_t*>(L), static_cast<const uint16_t*>(A),
@@ -745,10 +773,16 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     return hipGetLastError();
 }
 
+int draft_tile_slots(int B, int nT)
+{
+    const int nM = (B + kTileRows - 1) / kTileRows;
+    return tile_slots(nT, nM, cu_count(), B % kTileRows == 0 ? kManyTiles : kPartTiles);
+}
+
 bool schedule_in_first_tiles(int dtype, int B, int gamma, int V)
 {
     if (dtype != 1 || (long long)B * gamma > kSchedMaxKeys || B > kTileRows) return false;
-    const int nT = n_tiles(dtype, V), S = tile_slots(nT, 1, cu_count(), kPartTiles);
+    const int nT = n_tiles(dtype, V), S = draft_tile_slots(B, nT);
     return S > 1 && (nT + S - 2) / (S - 1) == (nT + S - 1) / S;
 }
 

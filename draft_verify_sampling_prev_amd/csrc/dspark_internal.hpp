@@ -124,6 +124,10 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
 // slot fewer leaves every slot's tile count unchanged (B <= 256), or the
 // last step's one-wave locate launch.
 bool schedule_in_first_tiles(int dtype, int B, int gamma, int V);
+// Persistent slots of the bf16 draft tile launch for B rows and nT tiles:
+// tile_slots with at most 12 tiles per slot, or 36 for full-batch launches
+// (B a multiple of 256), which write their staged partials out every 12.
+int draft_tile_slots(int B, int nT);
 bool draft_step_can_schedule(int dtype, int B, int gamma, int V);
 
 hipError_t launch_schedule(const float* z, const float* temps, int B, int gamma, int64_t admit, float* survival,

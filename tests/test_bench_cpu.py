@@ -81,7 +81,9 @@ def test_tile_slots_match_the_library_rule():
     """The bench's copy of the slot rule (used to split the load-only ceiling kernel as the tile kernel splits its
     tiles): at most 12 tiles per slot, whole rounds of one workgroup per compute unit and row block."""
     assert bench.tile_slots(2020, 1, 256) == 256       # V = 129280, B <= 256: one round
-    assert bench.tile_slots(2020, 4, 256) == 192       # B = 1024: 169 needed, three rounds of 64
+    assert bench.tile_slots(2020, 4, 256) == 192       # 169 needed at 12 tiles per slot: three rounds of 64
+    assert bench.tile_slots(2020, 4, 256, 36) == 64    # B = 1024 (full batch, up to 36 tiles): one round
+    assert bench.tile_slots(1719, 2, 256, 36) == 128   # B = 512, V = 110000: 13-14 tiles per slot
     assert bench.tile_slots(16, 1, 256) == 16          # fewer tiles than compute units
     assert bench.tile_slots(3200, 1, 256) == 512       # 267 needed: two rounds
 

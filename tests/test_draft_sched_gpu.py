@@ -35,7 +35,7 @@ def _host(B, gamma, V, dtype="bf16"):
     if dtype != "bf16" or B * gamma > FUSED_MAX_KEYS:
         return "separate"
     nT = (V + 63) // 64
-    S = bench.tile_slots(nT, 1, torch.cuda.get_device_properties(0).multi_processor_count)
+    S = bench.tile_slots(nT, 1, torch.cuda.get_device_properties(0).multi_processor_count, 36 if B == 256 else 12)
     if B <= 256 and S > 1 and -(-nT // (S - 1)) == -(-nT // S):
         return "first tiles"
     return "last locate" if nT <= 64 * 64 else "separate"

@@ -185,10 +185,24 @@ def test_load_sweep_sampled(mult):
     print("  ", rep.summary(), flush=True)
     assert rep.ok(), rep.summary()
     assert check.flips_ok(rep), rep.summary()
-    if mult == 8:  # run to run, bitwise, at the B = 1024 shape (four row blocks, three rounds of tile slots)
+    if mult == 8:  # run to run, bitwise, at the B = 1024 shape (four row blocks, ~32 tiles per slot)
         again = run_step(inp, wl.budget, wl.philox_seed)
         for k in out:
             assert np.array_equal(out[k].view(np.uint8), again[k].view(np.uint8)), k
+
+
+def test_full_batch_slots_past_the_staging():
+    """B = 512, V = 110000 (1719 tiles): a full-batch launch gives each of 128 slots per row block 13-14 tiles,
+    more than the 12 whose partials the LDS staging holds, so the staging is written out mid-launch.  Every draft
+    row's sample depends on all of its tiles' partials, so sampled rows check every write-out; plus bitwise run
+    to run."""
+    wl = synth.tiny(B=512, gamma=2, V=110000, r=256, budget=700, dtype="bf16")
+    inp = synth.make_inputs(wl)
+    rows, reqs = _sample(wl, 321, n=96)
+    out, _ = _run_and_check(wl, draft_rows=rows, requests=reqs, inp=inp)
+    again = run_step(inp, wl.budget, wl.philox_seed)
+    for k in out:
+        assert np.array_equal(out[k].view(np.uint8), again[k].view(np.uint8)), k
 
 
 def test_run_to_run_determinism():
