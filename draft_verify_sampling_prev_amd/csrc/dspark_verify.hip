@@ -396,13 +396,31 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
 // ---------------------------------------------------------------------------
 constexpr int kResPartTiles = 12;
 
+// Rank of workgroup b among the G workgroups of a launch in the order the
+// hardware starts them when every CU takes one at a time: workgroups go to
+// the 8 XCDs round-robin (b mod 8), and within an XCD the q-th one (q = b/8)
+// lands on CU q mod cpx, behind the ones before it on that CU (measured on
+// MI355X: with one workgroup per CU, a workgroup that exits at once does not
+// let a later one past an earlier one still running on its CU).  Rank
+// p*8*cpx + x*n_p + (q mod cpx) for position p = q / cpx (n_p workgroups of
+// the XCD at that position): position 0 of every CU first, consecutive
+// ranks on one XCD.  A bijection of [0, G) when G is a multiple of 8; the
+// XCD-grouped order of xcd_logical_id otherwise.
+__device__ __forceinline__ int resid_item(int b, int G, int cpx)
+{
+    if ((G & 7) || cpx <= 0) return xcd_logical_id(b, G);
+    const int x = b & 7, q = b >> 3, Qx = G >> 3;
+    const int p = q / cpx, n = min(cpx, Qx - p * cpx);
+    return p * 8 * cpx + x * n + (q - p * cpx);
+}
+
 template <int KS>
 __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     const uint16_t* __restrict__ Tg, const uint16_t* __restrict__ L, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ accepted,
     const int4* __restrict__ resid_list, const int32_t* __restrict__ resid_count, int B, int gamma, int V, int r, int nT,
-    int nM, int S, int nA, float2* __restrict__ rpart)
+    int nM, int S, int nA, int cpx, float2* __restrict__ rpart)
 {
     constexpr int NW = kTileWaves, R = kTileRows;
     __shared__ __attribute__((aligned(1024))) char s0[kBmTileBytes];
@@ -411,13 +429,20 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     __shared__ __attribute__((aligned(1024))) char s3[kBmTileBytes];
     __shared__ unsigned long long stage[kResPartTiles][R];  // float2 pairs, stored as one 64-bit word each
 
-    const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int mblk = lid % nM, slot = lid / nM;
+    // Work items (slot, row block) of the row blocks that hold rejected rows,
+    // slot-major, so the row blocks of a slot are consecutive items; items
+    // past them exit at once.  Items go to workgroups in dispatch order
+    // (resid_item), so whatever the rejected count, the active items take
+    // the first workgroup of every CU and a slot's row blocks share an XCD.
     const int cntr = *resid_count;
+    const int nMa = min(nM, (cntr + R - 1) / R);
+    const int item = resid_item(blockIdx.x, gridDim.x, cpx);
+    if (item >= S * nMa) return;  // uniform
+    const int mblk = item % nMa, slot = item / nMa;
     const int m0 = mblk * R;
     int t0, ts, cnt;
     slot_tiles(slot, S, nT, &t0, &ts, &cnt);
-    if (m0 >= cntr || cnt <= 0) return;  // uniform
+    if (cnt <= 0) return;  // uniform
     const int w = wave_id(), lane = threadIdx.x & 63, G = lane >> 4, c = lane & 15;
     // Batch block bb of wave w holds the workgroup's rows 128bb + 16w .. +15,
     // so the first rejected rows spread over all waves (and SIMDs) and a
@@ -937,7 +962,8 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
         launch_timed(K_RESID_TILES, kern, dim3(S * nM), dim3(64 * kTileWaves), s,
                            reinterpret_cast<const uint16_t*>(Tg), reinterpret_cast<const uint16_t*>(L),
                            reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(Bm), x0, tok,
-                           lse_d, lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, S, nA, rpart);
+                           lse_d, lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, S, nA, cu_count() / 8,
+                           rpart);
     } else {
         const int nM = (B + 255) / 256;
         launch_timed(K_RESID_TILES, k_resid_tiles_f32, dim3(nT * nM), dim3(kThreads), s,
