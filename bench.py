@@ -430,6 +430,24 @@ def main():
     ms_step_instr = e0.elapsed_time(e1) / K
     tiles_ms, tiles_n = binding.profile_query("draft_tiles")
 
+    # The same K steps as the three separate calls of the boundary
+    # (dspark_markov_draft, dspark_schedule, dspark_verify), for comparison
+    # with the fused draft+schedule call the timed region uses.
+    separate = None
+    if fused_schedule and not args.confidence and args.head == "markov":
+        fused_schedule = False
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(K):
+            step(i, base_seed + i)
+        e1.record()
+        torch.cuda.synchronize()
+        fused_schedule = True
+        ms_sep = e0.elapsed_time(e1) / K
+        separate = {"ms_per_step": round(ms_sep, 4),
+                    "tokens_per_s": round(emitted / K / (ms_sep / 1000.0), 1),
+                    "calls": "dspark_markov_draft + dspark_schedule + dspark_verify, the same K steps"}
+
     # Per-kernel averages (separate pass, every kernel timed) for context, and
     # the verify lengths / accepted counts of those steps.
     kern = {}
@@ -552,6 +570,8 @@ def main():
     }
     if graph:
         result["graph_replay"] = graph
+    if separate:
+        result["separate_schedule_call"] = separate
     if not args.no_cpu_baseline and args.schedule == "budget" and not args.confidence and args.head == "markov":
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, wl, base_seed, min(args.cpu_requests, B),
