@@ -41,7 +41,6 @@ WsLayout ws_layout(int B, int gamma, int V)
     l.tgt_m = take(Bz * G * nC * 4);
     l.tgt_s = take(Bz * G * nC * 8);
     l.lse_t = take(Bz * G * 8);
-    l.resid_idx = take(Bz * 4);
     l.resid_list = take(Bz * 16);
     l.resid_count = take(4);
     l.res_part = take(Bz * nT * 8);

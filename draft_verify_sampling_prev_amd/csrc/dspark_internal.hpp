@@ -28,10 +28,9 @@ struct WsLayout {
     size_t draft_part;            // [B][nT] float2 : draft tile max and sum of exp(f - max)
     size_t tgt_m, tgt_s;          // [B*gamma][nC] f32 / f64 : target chunk max and sum of exp
     size_t lse_t;                 // [B][gamma] f64 : target log-normalisers of verified rows
-    size_t resid_idx;             // [B] i32 : compact residual index of request b, or -1
     size_t resid_list;            // [B] int4 : (request, first rejected position, its conditioning token), in no fixed order
     size_t resid_count;           // [1] i32
-    size_t res_part;              // [B][nT] float2 : per tile sum of max(0, p_t - p_d) and of p_t
+    size_t res_part;              // [B][nT] float2 : per tile sum of max(0, p_t - p_d) and of p_t, row b for request b
     size_t bon_m, bon_s;          // [B][nC] f32 / f64 : bonus-row chunk max and sum of exp
     size_t ag;                    // [ceil(B/16)*16][256] bf16 : the next draft step's A rows, MFMA order (rank 256)
     size_t total;

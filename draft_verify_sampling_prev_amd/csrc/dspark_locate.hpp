@@ -315,8 +315,9 @@ __device__ __forceinline__ int scan_row_tile_lanes(int n0, double scale, double 
 }
 
 // Wave 0: inverse-CDF scan of a 64-column tile held as by row_tile_vm.  The
-// row sits in MFMA batch column pos & 15 (the column it occupied in the tile
-// pass), i.e. lanes 16G + (pos & 15), G = 0..3.  wfn(vb, i, col) gives the
+// row is read from MFMA batch column pos & 15, i.e. lanes 16G + (pos & 15),
+// G = 0..3 (every column holds the same row, so any pos gives the same
+// bits).  wfn(vb, i, col) gives the
 // weight of the lane's element i of block vb, which is column col (the
 // function returns 0 for col >= V).  Returns the tile column where
 // cprev + scale * (running weight in column order) first exceeds tau, else

@@ -22,7 +22,8 @@
 //                            -> chunk max and sum of exp.
 //   k_resid_tiles            Markov MFMA tiles of the rejected draft rows
 //                            fused with the target row: per tile sums of
-//                            max(0, p_t - p_d) and of p_t.
+//                            max(0, p_t - p_d) and of p_t, stored in the
+//                            request's row of the residual partials.
 //   k_row_partials (bonus)   otherwise: grid = chunks x B, the bonus rows of
 //                            the requests without a rejection.
 //   k_final                  one workgroup per request: locate and sample
@@ -172,7 +173,7 @@ __device__ __forceinline__ void lse_accept(
     const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const float* __restrict__ tgm,
     const double* __restrict__ tgs, int B, int gamma, int V, int nC, int rnn, SeedArg seed_arg,
     int32_t* __restrict__ accepted, int32_t* __restrict__ n_out, float* __restrict__ target_p,
-    double* __restrict__ lse_t, int32_t* __restrict__ resid_idx, int4* __restrict__ resid_list,
+    double* __restrict__ lse_t, int4* __restrict__ resid_list,
     int32_t* __restrict__ resid_count, int wg)
 {
     const uint64_t seed = seed_of(seed_arg);
@@ -257,10 +258,7 @@ __device__ __forceinline__ void lse_accept(
             // or with the RNN head the state row (b, ks-1)
             const int xprev = rnn ? b * gamma + ks - 1 : ks == 1 ? x0[b] : tok[row0 + ks - 2];
             const int idx = atomicAdd(resid_count, 1);
-            resid_idx[b] = idx;
             resid_list[idx] = make_int4(b, ks, xprev, 0);
-        } else {
-            resid_idx[b] = -1;
         }
     }
 }
@@ -279,14 +277,14 @@ __global__ __launch_bounds__(kThreads) void k_accept_bonus(
     const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const float* __restrict__ tgm,
     const double* __restrict__ tgs, int B, int gamma, int V, int nC, int rnn, SeedArg seed_arg,
     int32_t* __restrict__ accepted, int32_t* __restrict__ n_out, float* __restrict__ target_p,
-    double* __restrict__ lse_t, int32_t* __restrict__ resid_idx, int4* __restrict__ resid_list,
+    double* __restrict__ lse_t, int4* __restrict__ resid_list,
     int32_t* __restrict__ resid_count, int nAcc, float* __restrict__ bm, double* __restrict__ bsum)
 {
     __shared__ BlockScratch bs;
     const int wg = blockIdx.x;
     if (wg < nAcc) {
         lse_accept<DT>(Tg, pd, len, x0, tok, tgm, tgs, B, gamma, V, nC, rnn, seed_arg, accepted, n_out, target_p,
-                       lse_t, resid_idx, resid_list, resid_count, wg);
+                       lse_t, resid_list, resid_count, wg);
         return;
     }
     const int q = wg - nAcc, b = q / nC;
@@ -379,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void k_resid_tiles_f32(
             }
             sw = sum16(sw);
             sp = sum16(sp);
-            if ((lane & 15) == 0 && row < cnt) rpart[(size_t)row * nT + tile] = make_float2((float)sw, (float)sp);
+            if ((lane & 15) == 0 && row < cnt) rpart[(size_t)rr.b * nT + tile] = make_float2((float)sw, (float)sp);
         }
     }
 }
@@ -454,6 +452,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     const uint16_t* lrow[2];
     const uint16_t* trow[2];
     int lrow_idx[2];
+    int rowb[2] = { 0, 0 };  // request of this lane's row in each active block (its partials' row)
     float ld[2], lt[2];
     int4 rec[2];  // the rows' records (decoded after the first Bm tile is issued)
 #pragma unroll
@@ -581,6 +580,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
                 lrow[bb] = L + ((size_t)rr.b * gamma + (rr.ks - 1)) * V;
                 trow[bb] = Tg + ((size_t)rr.b * (gamma + 1) + (rr.ks - 1)) * V;
                 lrow_idx[bb] = rr.b * gamma + rr.ks - 1;
+                rowb[bb] = rr.b;
             }
             load_lt(nbb, 0, l0, t0r);
             issue_fence();
@@ -625,12 +625,15 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     else if (act0) run(std::integral_constant<int, 1>{});
     else run(std::integral_constant<int, 0>{});
     // As in the draft tile kernel: LDS wait and barrier for the staging, the
-    // dummy loads drain while the sums are written.
-    wait_lds();
-    barrier_lds();
-    for (int e = threadIdx.x; e < R * cnt; e += 64 * NW) {
-        const int row = e / cnt, i = e - row * cnt;
-        if (m0 + row < cntr) rpart[(size_t)(m0 + row) * nT + t0 + i * ts] = unpack_f2(stage[i][row]);
+    // dummy loads drain while the sums are written.  The partials go to the
+    // row of the request (rpart is indexed by request, so the final kernel
+    // can read them before it knows whether the request was rejected); each
+    // wave writes its own rows, lane group G taking tiles G, G+4, ...
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        const int row = row_of(bb) + c;
+        if (m0 + row < cntr)
+            for (int i = G; i < cnt; i += 4) rpart[(size_t)rowb[bb] * nT + t0 + i * ts] = unpack_f2(stage[i][row]);
     }
     wait_all_mem();
 }
@@ -643,9 +646,9 @@ __global__ __launch_bounds__(kThreads) void k_final(
     const typename DT::T* __restrict__ Tg, const typename DT::T* __restrict__ L, const typename DT::T* __restrict__ A,
     const typename DT::T* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ len,
-    const int32_t* __restrict__ accepted, const int32_t* __restrict__ resid_idx, const float2* __restrict__ rpart,
-    const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rnn,
-    SeedArg seed_arg, int32_t* __restrict__ out_tok)
+    const int32_t* __restrict__ accepted, const float2* __restrict__ rpart, const float* __restrict__ bm,
+    const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rnn, SeedArg seed_arg,
+    int32_t* __restrict__ out_tok)
 {
     const uint64_t seed = seed_of(seed_arg);
     typedef typename DT::T T;
@@ -663,8 +666,7 @@ __global__ __launch_bounds__(kThreads) void k_final(
     if (a < l) {
         // ---- residual at the first rejected position ks -------------------
         const int ks = a + 1;
-        const int m = resid_idx[b];
-        const float2* rq = rpart + (size_t)m * nT;
+        const float2* rq = rpart + (size_t)b * nT;
         // Total residual mass decides between the residual and its p_t fallback.
         double sloc = 0.0;
         {
@@ -699,7 +701,7 @@ __global__ __launch_bounds__(kThreads) void k_final(
                 for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(row16_block(tv, vb));
                 double wsel;
                 const int j = scan_vm_tile(
-                    n0, m, 1.0, loc.cprev, loc.tau,
+                    n0, 0, 1.0, loc.cprev, loc.tau,
                     [&](int vb, int i, int col) { return col < V ? weight(f[vb][i], tf[vb][i]) : 0.0; }, &wsel);
                 if (lane == 0) sh_tok = clamp_tok(n0 + j, V);
             }
@@ -777,35 +779,85 @@ __global__ __launch_bounds__(kThreads) void k_final(
 // column the row had in the residual pass.  Bonus: the target chunk is
 // located from the chunk partials; each lane sums the weights of 128
 // contiguous elements of the chunk, the lane slice holding the crossing is
-// found by a wave scan, and that slice is rescanned two elements per lane.
+// found by a wave scan, and that slice (handed over through LDS by the lane
+// that loaded it) is rescanned two elements per lane.
+//
+// The small loads that do not depend on the accept count go out with the
+// length and the accept count: the request's bonus chunk partials (stale and
+// ignored when the request has a rejection) and per position k = lane + 1
+// its conditioning token, draft token and both log-normalisers.  The
+// residual tile sums (the request's row of the residual partials) are read
+// in the residual branch only: issued in every workgroup they cost more than
+// the round trip they save (measured on MI355X, B = 256, V = 129280: 9.7
+// against 8.4 us per launch).
 // ---------------------------------------------------------------------------
+
+// Holds v in a register at this point, so the load that produced it is not
+// moved into the one branch that uses it (behind the accept count).
+template <class X>
+__device__ __forceinline__ void pin_reg(X& v)
+{
+    asm volatile("" : "+v"(v));
+}
+
 template <int KS, int PER>
 __global__ __launch_bounds__(64) void k_final_bf16(
     const uint16_t* __restrict__ Tg, const uint16_t* __restrict__ L, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ len,
-    const int32_t* __restrict__ accepted, const int32_t* __restrict__ resid_idx, const float2* __restrict__ rpart,
-    const float* __restrict__ bm, const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rnn,
-    SeedArg seed_arg, int32_t* __restrict__ out_tok)
+    const int32_t* __restrict__ accepted, const float2* __restrict__ rpart, const float* __restrict__ bm,
+    const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rnn, SeedArg seed_arg,
+    int32_t* __restrict__ out_tok)
 {
     const uint64_t seed = seed_of(seed_arg);
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
+    const size_t row0 = (size_t)b * gamma;
+
     const int l = clamp_len(len[b], gamma);
     const int a = accepted[b];
+    int xc = 0, tk = 0;       // position lane+1: conditioning token x_lane, draft token x_{lane+1}
+    double lsd = 0.0, lst = 0.0;  // and the draft / target log-normalisers of its row
+    if (lane < gamma) {
+        if (!rnn) xc = lane == 0 ? x0[b] : tok[row0 + lane - 1];  // the RNN head has no x0 (null)
+        tk = tok[row0 + lane];
+        lsd = lse_d[row0 + lane];
+        lst = lse_t[row0 + lane];
+    }
+    // nC <= 64 * 4 chunks (lengths up to 2^21), slices of at most 4 per lane.
+    const float* pm = bm + (size_t)b * nC;
+    const double* ps = bsum + (size_t)b * nC;
+    const int cper = (nC + 63) / 64, c0l = lane * cper;
+    float cm[4];
+    double cs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int ci = min(c0l + j, nC - 1);
+        const bool ok = j < cper && c0l + j < nC;
+        cm[j] = ok ? pm[ci] : -INFINITY;
+        cs[j] = ok ? ps[ci] : 0.0;
+    }
+    pin_reg(xc);
+    pin_reg(lsd);
+    pin_reg(lst);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        pin_reg(cm[j]);
+        pin_reg(cs[j]);
+    }
     int token;
 
     if (a < l) {
-        // ---- residual at the first rejected position ks -------------------
+        // ---- residual at the first rejected position ks = a + 1 -----------
         const int ks = a + 1;
-        const int m = resid_idx[b];
         float2 q[PER];
         int i0;
-        load_slices<PER>(rpart + (size_t)m * nT, nT, make_float2(0.0f, 0.0f), q, &i0);
+        load_slices<PER>(rpart + (size_t)b * nT, nT, make_float2(0.0f, 0.0f), q, &i0);
         uint4 af[1][8];
         {
-            const uint16_t* arow[1] = { A + (size_t)(rnn ? b * gamma + ks - 1 : cond_token_v(x0, tok, b, gamma, ks, V)) * r };
+            const int xr = rnn ? (int)row0 + a : clamp_tok(__shfl(xc, a, 64), V);
+            const uint16_t* arow[1] = { A + (size_t)xr * r };
             load_a_frags<1>(arow, r, af);
         }
         float sw = 0.0f;
@@ -821,9 +873,9 @@ __global__ __launch_bounds__(64) void k_final_bf16(
         uint4 tv[2];
         load_row16(trow, n0, V, false, tv);
         floatx4 f[4];
-        row_tile_vm_wave<KS>(L + ((size_t)b * gamma + (ks - 1)) * V, af, Bm, V, r, n0, lds, f);
-        const float ld = lse_log2(lse_d[(size_t)b * gamma + ks - 1]);
-        const float lt = lse_log2(lse_t[(size_t)b * gamma + ks - 1]);
+        row_tile_vm_wave<KS>(L + (row0 + (ks - 1)) * V, af, Bm, V, r, n0, lds, f);
+        const float ld = lse_log2(__shfl(lsd, a, 64));
+        const float lt = lse_log2(__shfl(lst, a, 64));
         floatx4 tf[4];
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb) tf[vb] = bf16x4_to_f32(row16_block(tv, vb));
@@ -840,27 +892,18 @@ __global__ __launch_bounds__(64) void k_final_bf16(
         token = clamp_tok(n0 + j, V);
     } else {
         // ---- bonus token from target row l (position l + 1) ----------------
-        const float* pm = bm + (size_t)b * nC;
-        const double* ps = bsum + (size_t)b * nC;
-        float mloc = -INFINITY;
-        for (int c = lane; c < nC; c += 64) mloc = fmaxf(mloc, pm[c]);
-        const float M = wave_max(mloc);
+        const float M = wave_max(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])));
         const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)(l + 1), 3u);
-        // nC <= 64 * 4 chunks (lengths up to 2^21), slices of at most 4 per lane.
-        const int cper = (nC + 63) / 64, c0l = lane * cper;
-        float cm[4];
-        double cs[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ci = min(c0l + j, nC - 1);
-            const bool ok = j < cper && c0l + j < nC;
-            cm[j] = ok ? pm[ci] : -INFINITY;
-            cs[j] = ok ? ps[ci] : 0.0;
-        }
         const Located loc = wave_locate_slices<4>(c0l, [&](int j) { return tile_mass(cm[j], cs[j], M); }, u,
                                                   reinterpret_cast<double*>(lds));
 
-        const float mc = pm[loc.idx];
+        // The chosen chunk's maximum, from the lane whose slice holds it.
+        const int own = loc.idx / cper, jo = loc.idx - lane * cper;
+        float mine = cm[0];
+#pragma unroll
+        for (int j = 1; j < 4; ++j)
+            if (j == jo) mine = cm[j];
+        const float mc = __shfl(mine, own, 64);
         const float mcl = row_mlog2(mc);
         const double scale = tile_mass(mc, 1.0, M);
         const uint16_t* x = Tg + ((size_t)b * (gamma + 1) + l) * V;
@@ -868,7 +911,8 @@ __global__ __launch_bounds__(64) void k_final_bf16(
         const int c0 = loc.idx * kChunkElems;
         auto w_of = [&](int e, float xv) { return e < V && mc != -INFINITY ? (double)softmax_w(xv, mcl) : 0.0; };
         // Pass 1: lane totals over contiguous 128-element slices (16-byte
-        // loads, all in flight at once).
+        // loads, all in flight at once; V is a multiple of 8, so a group
+        // that starts below V is loaded unclamped).
         const int e0 = c0 + lane * EPL;
         uint4 xv[EPL / 8];
 #pragma unroll
@@ -889,11 +933,21 @@ __global__ __launch_bounds__(64) void k_final_bf16(
         if (mh) src = __builtin_ctzll(mh);
         else if (mp) src = 63 - __builtin_clzll(mp);
         else src = 0;
-        // Pass 2: the chosen slice, two elements per lane, scanned in index order.
+        // Pass 2: the chosen slice, two elements per lane, scanned in index
+        // order.  Lane src hands its 128 values over through LDS (past the
+        // locate scratch): lane L takes the 32-bit word L, elements 2L, 2L+1.
+        uint4* xs = reinterpret_cast<uint4*>(lds + 1024);
+        if (lane == src) {
+#pragma unroll
+            for (int qv = 0; qv < EPL / 8; ++qv) xs[qv] = xv[qv];
+        }
+        __builtin_amdgcn_wave_barrier();  // one wave: its LDS accesses complete in order
+        const uint32_t pair = reinterpret_cast<const uint32_t*>(xs)[lane];
+        __builtin_amdgcn_wave_barrier();
         const double base = __shfl(off, src, 64);
         const int s0 = c0 + src * EPL + 2 * lane;
-        const double w0 = s0 < V ? w_of(s0, Bf16::to_f32(x[s0])) : 0.0;
-        const double w1 = s0 + 1 < V ? w_of(s0 + 1, Bf16::to_f32(x[s0 + 1])) : 0.0;
+        const double w0 = s0 < V ? w_of(s0, __uint_as_float(pair << 16)) : 0.0;
+        const double w1 = s0 + 1 < V ? w_of(s0 + 1, __uint_as_float(pair & 0xFFFF0000u)) : 0.0;
         const double pin = wave_incl_scan(w0 + w1);
         const double pex = pin - (w0 + w1);
         const double r0 = base + pex + w0, r1 = base + pex + w0 + w1;
@@ -914,8 +968,8 @@ __global__ __launch_bounds__(64) void k_final_bf16(
         }
         token = clamp_tok(e, V);
     }
-    for (int kk = lane; kk <= gamma; kk += 64)
-        out_tok[(size_t)b * (gamma + 1) + kk] = kk < a ? tok[(size_t)b * gamma + kk] : (kk == a ? token : -1);
+    // gamma <= 16: one lane per output slot.
+    if (lane <= gamma) out_tok[(size_t)b * (gamma + 1) + lane] = lane < a ? tk : (lane == a ? token : -1);
 }
 
 template <class DT>
@@ -936,7 +990,6 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     float* tgm = reinterpret_cast<float*>(w + lay.tgt_m);
     double* tgs = reinterpret_cast<double*>(w + lay.tgt_s);
     double* lse_t = reinterpret_cast<double*>(w + lay.lse_t);
-    int32_t* ridx = reinterpret_cast<int32_t*>(w + lay.resid_idx);
     int4* rlist = reinterpret_cast<int4*>(w + lay.resid_list);
     int32_t* rcnt = reinterpret_cast<int32_t*>(w + lay.resid_count);
     float2* rpart = reinterpret_cast<float2*>(w + lay.res_part);
@@ -953,7 +1006,7 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     const bool bonus_in_accept = (double)B * V * sizeof(T) <= kBonusInAcceptBytes;
     const int nAcc = (B + kAcceptWaves - 1) / kAcceptWaves;
     launch_timed(K_ACCEPT, k_accept_bonus<DT>, dim3(nAcc + (bonus_in_accept ? nC * B : 0)), dim3(kThreads), s, Tg, pd,
-                 len, x0, tok, tgm, tgs, B, gamma, V, nC, rnn, seed, accepted, n_out, target_p, lse_t, ridx, rlist, rcnt,
+                 len, x0, tok, tgm, tgs, B, gamma, V, nC, rnn, seed, accepted, n_out, target_p, lse_t, rlist, rcnt,
                  nAcc, bm, bsum);
     if (std::is_same<DT, Bf16>::value) {
         const int nM = (B + kTileRows - 1) / kTileRows;
@@ -980,11 +1033,11 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
                           : (k8 ? k_final_bf16<8, 64> : k_final_bf16<0, 64>);
         launch_timed(K_FINAL, kern, dim3(B), dim3(64), s, reinterpret_cast<const uint16_t*>(Tg),
                            reinterpret_cast<const uint16_t*>(L), reinterpret_cast<const uint16_t*>(A),
-                           reinterpret_cast<const uint16_t*>(Bm), x0, tok, lse_d, lse_t, len, accepted, ridx, rpart, bm,
+                           reinterpret_cast<const uint16_t*>(Bm), x0, tok, lse_d, lse_t, len, accepted, rpart, bm,
                            bsum, gamma, V, r, nT, nC, rnn, seed, out_tok);
     } else {
         launch_timed(K_FINAL, k_final<DT>, dim3(B), dim3(kThreads), s, Tg, L, A, Bm, x0, tok, lse_d, lse_t, len,
-                           accepted, ridx, rpart, bm, bsum, gamma, V, r, nT, nC, rnn, seed, out_tok);
+                           accepted, rpart, bm, bsum, gamma, V, r, nT, nC, rnn, seed, out_tok);
     }
     return hipGetLastError();
 }
