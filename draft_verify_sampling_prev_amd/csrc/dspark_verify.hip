@@ -783,8 +783,8 @@ __global__ __launch_bounds__(kThreads) void k_final(
 // that loaded it) is rescanned two elements per lane.
 //
 // The small loads that do not depend on the accept count go out with the
-// length and the accept count: the request's bonus chunk partials (stale and
-// ignored when the request has a rejection) and per position k = lane + 1
+// length and the accept count: the request's bonus chunk partials (unused,
+// and possibly stale, when the request has a rejection) and per position k = lane + 1
 // its conditioning token, draft token and both log-normalisers.  The
 // residual tile sums (the request's row of the residual partials) are read
 // in the residual branch only: issued in every workgroup they cost more than
