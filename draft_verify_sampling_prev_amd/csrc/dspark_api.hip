@@ -46,7 +46,8 @@ WsLayout ws_layout(int B, int gamma, int V)
     l.res_part = take(Bz * nT * 8);
     l.bon_m = take(Bz * nC * 4);
     l.bon_s = take(Bz * nC * 8);
-    l.ag = take(((Bz + 15) / 16) * 16 * (size_t)kAgRank * 2);
+    l.ag = take(ag_bytes(B));
+    l.slot_agg = take(slot_agg_bytes(B));  // = ag + slot_agg_offset(B)
     l.total = o;
     return l;
 }
@@ -99,15 +100,17 @@ static void* scratch_address(hipError_t* err)
     return g_scratch_ptr[dev];
 }
 
-// The draft's share of a workspace (the tile partials, then the A rows in
-// MFMA order); the other offsets are unused by the draft kernels.
+// The draft's share of a workspace (the tile partials, the A rows in MFMA
+// order, then the tile partials' slot aggregates); the other offsets are
+// unused by the draft kernels.
 static WsLayout draft_layout(int B, int V)
 {
     WsLayout l = {};
     const size_t Bz = (size_t)(B > 0 ? B : 0);
     l.draft_part = 0;
     l.ag = align256(Bz * (size_t)n_tiles(1, V) * 8);
-    l.total = align256(l.ag + ((Bz + 15) / 16) * 16 * (size_t)kAgRank * 2);
+    l.slot_agg = l.ag + slot_agg_offset(B);
+    l.total = align256(l.slot_agg + slot_agg_bytes(B));
     return l;
 }
 

@@ -160,16 +160,17 @@ constexpr int kManyTiles = 3 * kPartTiles;
 // the Bm DMA (the two paths then leave the compiler less exact waits).
 // The budget schedule in one workgroup of a draft launch (dspark_markov_draft_sched):
 // its scratch first, then the keys, in a 32 KB LDS tile buffer of that launch.
+static_assert(kTileRows == 256, "slot_agg_bytes sizes the slot aggregates for batches above one 256-row block");
 constexpr int kSchedKeysOffset = 2048;  // bytes
 constexpr int kSchedMaxKeys = (kBmTileBytes - kSchedKeysOffset) / 4;
 static_assert(sizeof(SelectScratch<64 * kTileWaves>) <= kSchedKeysOffset, "select scratch");
 
-template <int KS, bool FULL, bool MANY = false>
+template <int KS, bool FULL, bool MANY = false, bool SLOTS = false>
 __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     const uint16_t* __restrict__ L, const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ tok, const uint16_t* __restrict__ ag,
     const uint16_t* __restrict__ H, int B, int gamma, int V, int r, int k, int nT, int nM, int S,
-    float2* __restrict__ part, SchedArg sa)
+    float2* __restrict__ part, float2* __restrict__ sagg, SchedArg sa)
 {
     constexpr int NW = kTileWaves, R = kTileRows;
     __shared__ __attribute__((aligned(1024))) char s0[kBmTileBytes];
@@ -177,6 +178,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     __shared__ __attribute__((aligned(1024))) char s2[kBmTileBytes];
     __shared__ __attribute__((aligned(1024))) char s3[kBmTileBytes];
     __shared__ unsigned long long stage[kPartTiles][R];  // float2 pairs, stored as one 64-bit word each
+    // MANY with slot aggregates: row t's running (max, sum) over the tiles
+    // already written out, touched by thread t only.
+    __shared__ float2 run_agg[MANY && SLOTS ? R : 1];
 
     // A workgroup past the S * nM tile workgroups (launched only with the
     // schedule, see launch_draft_step) runs the budget schedule.
@@ -192,6 +196,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     int t0, ts, cnt;
     slot_tiles(slot, S, nT, &t0, &ts, &cnt);
     if (cnt <= 0) return;  // uniform
+    if constexpr (MANY && SLOTS) {
+        if (threadIdx.x < R) run_agg[threadIdx.x] = make_float2(-INFINITY, 0.0f);
+    }
     const int w = wave_id(), lane = threadIdx.x & 63, c = lane & 15;
     const int m0 = mblk * R;
     const int mw = m0 + 32 * w;  // first row of this wave
@@ -246,6 +253,11 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
         for (int e = threadIdx.x; e < R * kPartTiles; e += 64 * NW) {
             const int row = e / kPartTiles, j = e - row * kPartTiles;
             part[(size_t)(m0 + row) * nT + t0 + (base + j) * ts] = unpack_f2(stage[j][row]);
+        }
+        if (SLOTS && threadIdx.x < R) {  // fold these tiles into the row's running slot aggregate
+            float2 ra = run_agg[threadIdx.x];
+            fold_partials(&ra.x, &ra.y, kPartTiles, [&](int j) { return unpack_f2(stage[j][threadIdx.x]); });
+            run_agg[threadIdx.x] = ra;
         }
         wait_all_mem();
     };
@@ -390,6 +402,15 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
         const int row = e / left, i = e - row * left;
         if (m0 + row < B) part[(size_t)(m0 + row) * nT + t0 + (base + i) * ts] = unpack_f2(stage[i][row]);
     }
+    // The slot aggregate of each row: its max and sum of exp over the slot's
+    // tiles (t0 .. t0+cnt-1), for the locate's first level.
+    if (SLOTS && threadIdx.x < R && m0 + (int)threadIdx.x < B) {
+        const int row = threadIdx.x;
+        float2 ra = make_float2(-INFINITY, 0.0f);
+        if constexpr (MANY && SLOTS) ra = run_agg[row];
+        fold_partials(&ra.x, &ra.y, left, [&](int i) { return unpack_f2(stage[i][row]); });
+        sagg[(size_t)(m0 + row) * kSlotAggMax + slot] = ra;
+    }
     wait_all_mem();
 }
 
@@ -509,7 +530,7 @@ __device__ __forceinline__ void prefetch_first_tile(const uint16_t* __restrict__
 constexpr int kSchedWgThreads = 256;
 static_assert(sizeof(SelectScratch<kSchedWgThreads>) <= kSchedKeysOffset, "select scratch");
 
-template <int KS, int PER, bool AG, bool SCHED = false>
+template <int KS, int PER, bool AG, bool SCHED = false, bool SLOTS = false>
 __global__ __launch_bounds__(SCHED ? kSchedWgThreads : 128) void k_draft_locate_bf16(const uint16_t* __restrict__ L,
                                                           const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ Bm,
@@ -550,10 +571,24 @@ __global__ __launch_bounds__(SCHED ? kSchedWgThreads : 128) void k_draft_locate_
     const int b = blockIdx.x - (SCHED ? 1 : 0);
     const int lane = threadIdx.x & 63;
     // The partial loads go first: the A-operand loads wait for the token.
+    // SLOTS: the tile launch wrote slot aggregates (its S_next = Sp slots,
+    // at most kSlotAggMax; such launches never carry the schedule, so every
+    // tile launch of the call has the same slots).  Only those are read now,
+    // 2 KB per row instead of the row's 8 bytes per tile (at 2020 tiles a
+    // wave's full slices take 3-4 us to arrive, a 2 KB read 1.3 us), and the
+    // chosen slot's tiles after them.  (A compile-time choice: loads pending
+    // on one side of a run-time branch would make the compiler wait for every
+    // load where the paths join.  The aggregates' address comes from ag: an
+    // extra kernel argument measured 0.2 us slower per launch.)
+    const int Sp = S_next;
+    const float2* sagg = reinterpret_cast<const float2*>(reinterpret_cast<const char*>(ag) + slot_agg_offset(B));
     const float2* pr = part + (size_t)b * nT;
-    float2 q[PER];
-    int i0;
-    load_slices<PER>(pr, nT, make_float2(-INFINITY, 0.0f), q, &i0);
+    float2 q[SLOTS ? 1 : PER];
+    int i0 = 0;
+    float2 qs[4];
+    int i0s = 0;
+    if constexpr (SLOTS) load_slices<4>(sagg + (size_t)b * kSlotAggMax, Sp, make_float2(-INFINITY, 0.0f), qs, &i0s);
+    else load_slices<PER>(pr, nT, make_float2(-INFINITY, 0.0f), q, &i0);
     const int prev = cond_token(x0, tok, b, gamma, k, V);
     uint4 a[1][8];
     {
@@ -569,32 +604,60 @@ __global__ __launch_bounds__(SCHED ? kSchedWgThreads : 128) void k_draft_locate_
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) wcf[ks] = ld16(wc + min(32 * ks + kq8, r - 8));
     }
-    float mloc = -INFINITY;
+    float M, mt = 0.0f;
+    Located loc;
+    if constexpr (SLOTS) {
+        // First level: the slots in index order (each a contiguous tile range),
+        // masses from their aggregates; the row max is the max of the slot maxima.
+        M = wave_max(fmaxf(fmaxf(qs[0].x, qs[1].x), fmaxf(qs[2].x, qs[3].x)));
+        const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)k, 0u);
+        const Located ls = wave_locate_slices<4>(
+            i0s, [&](int j) { return tile_mass(qs[j].x, (double)qs[j].y, M); }, u, reinterpret_cast<double*>(lds));
+        // Second level: the chosen slot's tiles (at most kManyTiles), one per
+        // lane, scanned from the mass before the slot.  Where rounding leaves
+        // every running sum in the slot at or below tau, its last tile of
+        // positive mass is taken (as wave_locate_slices does within a slice).
+        int t0, ts, cnt;
+        slot_tiles(ls.idx, Sp, nT, &t0, &ts, &cnt);
+        const float2 qt = pr[t0 + min(lane, cnt - 1) * ts];
+        const double mm = lane < cnt ? tile_mass(qt.x, (double)qt.y, M) : 0.0;
+        const double inc = wave_incl_scan(mm);
+        const uint64_t hit = __ballot(mm > 0.0 && ls.cprev + inc > ls.tau);
+        const uint64_t pos = __ballot(mm > 0.0);
+        const int sel = hit ? __builtin_ctzll(hit) : pos ? 63 - __builtin_clzll(pos) : 0;
+        loc.S = ls.S;
+        loc.tau = ls.tau;
+        loc.idx = t0 + sel * ts;
+        loc.cprev = ls.cprev + __shfl(inc - mm, sel, 64);
+        mt = __shfl(qt.x, sel, 64);
+    } else {
+        float mloc = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) mloc = fmaxf(mloc, q[j].x);
-    const float M = wave_max(mloc);
-    const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)k, 0u);
-    // Tile masses relative to the row max, kept when the registers allow.
-    constexpr bool kCache = PER <= 32;
-    double ms[kCache ? PER : 1];
-    if constexpr (kCache) {
+        for (int j = 0; j < PER; ++j) mloc = fmaxf(mloc, q[j].x);
+        M = wave_max(mloc);
+        const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)k, 0u);
+        // Tile masses relative to the row max, kept when the registers allow.
+        constexpr bool kCache = PER <= 32;
+        double ms[kCache ? PER : 1];
+        if constexpr (kCache) {
 #pragma unroll
-        for (int j = 0; j < PER; ++j) ms[j] = tile_mass(q[j].x, (double)q[j].y, M);
+            for (int j = 0; j < PER; ++j) ms[j] = tile_mass(q[j].x, (double)q[j].y, M);
+        }
+        loc = wave_locate_slices<PER>(
+            i0,
+            [&](int j) {
+                if constexpr (kCache) return ms[j];
+                else return tile_mass(q[j].x, (double)q[j].y, M);
+            },
+            u, reinterpret_cast<double*>(lds));
     }
-    const Located loc = wave_locate_slices<PER>(
-        i0,
-        [&](int j) {
-            if constexpr (kCache) return ms[j];
-            else return tile_mass(q[j].x, (double)q[j].y, M);
-        },
-        u, reinterpret_cast<double*>(lds));
     const int idx = loc.idx;
     const double cprev = loc.cprev, tau = loc.tau, S = loc.S;
 
     const int n0 = idx * kTcols;
-    // Max of the chosen tile (reloaded: the partials are cached; its latency
-    // hides behind the tile's own loads).
-    const float mt = pr[idx].x;
+    // Max of the chosen tile (one level: reloaded, the partials are cached;
+    // its latency hides behind the tile's own loads).
+    if constexpr (!SLOTS) mt = pr[idx].x;
     floatx4 f[4];
     row_tile_vm_wave<KS>(L + ((size_t)b * gamma + (k - 1)) * V, a, Bm, V, r, n0, lds, f);
     if (co.z) {
@@ -731,17 +794,33 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     const bool sch_tiles = sched != nullptr && k == 1 && first_tiles_sched;
     const bool sch_locate = sched != nullptr && k == gamma && !first_tiles_sched;
     const SchedArg none{ nullptr, nullptr, 0, nullptr, nullptr };
+    const int St = sch_tiles ? S - 1 : S;  // slots of this step's tile launch
+    // Slot aggregates for the one-wave locate, where its workgroups share CUs
+    // (B > 256): each then reads 2 KB of aggregates and one slot's tiles
+    // instead of its row's 8 bytes per tile.  (Measured on MI355X at
+    // V = 129280: B = 1024, the locate 14.1 -> 11.5 us per launch; B = 256, one
+    // workgroup per CU, its waves end earlier but the launch, held by its
+    // slowest workgroups, does not, and the tile launch grows by 0.1-0.2 us.)
+    // Such shapes never carry the schedule in a tile launch, so every tile
+    // launch of a call has the same slots and the aggregates the same ranges.
+    float2* sagg = wave_locate && B > kTileRows && St <= kSlotAggMax
+                       ? reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.slot_agg)
+                       : nullptr;
     if (dtype == 1) {
-        auto kern = (r + 31) / 32 == 8
-                        ? (many ? k_draft_tiles_bf16<8, true, true>
-                                : B % kTileRows == 0 ? k_draft_tiles_bf16<8, true> : k_draft_tiles_bf16<8, false>)
-                        : (many ? k_draft_tiles_bf16<0, true, true> : k_draft_tiles_bf16<0, false>);
-        const int St = sch_tiles ? S - 1 : S;
+        const bool k8 = (r + 31) / 32 == 8, full = B % kTileRows == 0;
+        auto kern = sagg ? (k8 ? (many ? k_draft_tiles_bf16<8, true, true, true>
+                                       : full ? k_draft_tiles_bf16<8, true, false, true>
+                                              : k_draft_tiles_bf16<8, false, false, true>)
+                               : (many ? k_draft_tiles_bf16<0, true, true, true>
+                                       : k_draft_tiles_bf16<0, false, false, true>))
+                         : (k8 ? (many ? k_draft_tiles_bf16<8, true, true>
+                                       : full ? k_draft_tiles_bf16<8, true> : k_draft_tiles_bf16<8, false>)
+                               : (many ? k_draft_tiles_bf16<0, true, true> : k_draft_tiles_bf16<0, false>));
         launch_timed(K_DRAFT_TILES, kern, dim3(St * nM + (sch_tiles ? 1 : 0)), dim3(64 * kTileWaves), s,
                      static_cast<const uint16_t*>(L), static_cast<const uint16_t*>(A),
                      static_cast<const uint16_t*>(Bm), x0, tok,
                      static_cast<const uint16_t*>(ag_path && k >= 2 ? ag : nullptr), static_cast<const uint16_t*>(H),
-                     B, gamma, V, r, k, nT, nM, St, part, sch_tiles ? *sched : none);
+                     B, gamma, V, r, k, nT, nM, St, part, sagg, sch_tiles ? *sched : none);
     } else {
         const int nM32 = (B + 255) / 256;
         launch_timed(K_DRAFT_TILES, k_draft_tiles_f32, dim3(nT * nM32), dim3(kThreads), s, static_cast<const float*>(L),
@@ -751,7 +830,12 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     if (wave_locate) {
         const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32, wag = ag_path && k < gamma;
         const bool sch = sch_locate;  // (wag is false at k = gamma)
-        auto kern = sch ? (small ? (k8 ? k_draft_locate_bf16<8, 32, false, true> : k_draft_locate_bf16<0, 32, false, true>)
+        auto kern = sagg ? (sch ? (k8 ? k_draft_locate_bf16<8, 4, false, true, true>
+                                      : k_draft_locate_bf16<0, 4, false, true, true>)
+                                : k8 ? (wag ? k_draft_locate_bf16<8, 4, true, false, true>
+                                            : k_draft_locate_bf16<8, 4, false, false, true>)
+                                     : k_draft_locate_bf16<0, 4, false, false, true>)
+                  : sch ? (small ? (k8 ? k_draft_locate_bf16<8, 32, false, true> : k_draft_locate_bf16<0, 32, false, true>)
                                  : (k8 ? k_draft_locate_bf16<8, 64, false, true> : k_draft_locate_bf16<0, 64, false, true>))
                   : small ? (k8 ? (wag ? k_draft_locate_bf16<8, 32, true> : k_draft_locate_bf16<8, 32, false>)
                                 : k_draft_locate_bf16<0, 32, false>)

@@ -23,9 +23,23 @@ inline int n_chunks(int V) { return (V + kChunkElems - 1) / kChunkElems; }
 // in MFMA order (the "ag" workspace region, see dspark_tile.hpp).
 constexpr int kAgRank = 256;
 
+// Slot aggregates of the draft tile partials: a bf16 draft tile launch of at
+// most this many slots also writes, per row and slot, the max and sum of exp
+// of the slot's contiguous tile range, and the locate reads those first.
+// Every workspace layout puts them right after the A-row hand-over, at
+// ag + slot_agg_offset(B) (so the locate finds them without an argument).
+constexpr int kSlotAggMax = 256;
+__host__ __device__ inline size_t ag_bytes(int B) { return ((size_t)(B > 0 ? B : 0) + 15) / 16 * 16 * kAgRank * 2; }
+__host__ __device__ inline size_t slot_agg_offset(int B) { return (ag_bytes(B) + 255) & ~(size_t)255; }
+// Their size: only batches above one row block (kTileRows) use them (there
+// the locate workgroups share CUs); smaller batches keep the workspace as it
+// is without them.
+inline size_t slot_agg_bytes(int B) { return B > 256 ? (size_t)B * kSlotAggMax * 8 : 0; }
+
 // Byte offsets into the caller's workspace (each 256-byte aligned).
 struct WsLayout {
     size_t draft_part;            // [B][nT] float2 : draft tile max and sum of exp(f - max)
+    size_t slot_agg;              // [B][kSlotAggMax] float2 : the same per tile slot (contiguous tile range)
     size_t tgt_m, tgt_s;          // [B*gamma][nC] f32 / f64 : target chunk max and sum of exp
     size_t lse_t;                 // [B][gamma] f64 : target log-normalisers of verified rows
     size_t resid_list;            // [B] int4 : (request, first rejected position, its conditioning token), in no fixed order

@@ -422,6 +422,31 @@ __device__ __forceinline__ float2 unpack_f2(unsigned long long v)
     return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
+// Folds the (max, sum of exp relative to it) partials get(0 .. n-1) of
+// consecutive tiles into the running pair (*m, *s) of the range before them:
+// the range max, then every sum rescaled to it and added in tile order, in
+// fp32.  Each factor is 2^((x - max) log2 e), the difference taken first (as
+// tile_mass does), so a sum already relative to the max is multiplied by
+// exactly 1 (a factor formed as x log2 e - max log2 e would carry the
+// rounding of max log2 e, ~1e-6 at logits near 20, with the same sign into
+// every rescale).  Partials without a finite value add nothing.
+template <class Get>
+__device__ __forceinline__ void fold_partials(float* m, float* s, int n, Get get)
+{
+    float mx = *m;
+    for (int j = 0; j < n; ++j) mx = fmaxf(mx, get(j).x);
+    float acc = 0.0f;
+    if (mx != -INFINITY) {
+        if (*m != -INFINITY) acc = *s * __builtin_amdgcn_exp2f((*m - mx) * kLog2e);
+        for (int j = 0; j < n; ++j) {
+            const float2 p = get(j);
+            if (p.x != -INFINITY) acc += p.y * __builtin_amdgcn_exp2f((p.x - mx) * kLog2e);
+        }
+    }
+    *m = mx;
+    *s = acc;
+}
+
 // Tiles of persistent slot s of S over nT tiles: t0, t0 + ts, ... (cnt of
 // them), a contiguous range per slot (ts = 1).  (Measured on MI355X at the
 // 129280-column shape, contiguous ranges stream faster than slots

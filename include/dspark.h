@@ -122,10 +122,11 @@ int dspark_markov_draft(int dtype, const void* L, const void* A, const void* Bm,
  * allocate or pass device memory for a workspace (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
  * arguments, outputs, limits and errors as dspark_markov_draft, without
- * ws/ws_bytes: the draft's per-tile softmax partials and its A-row hand-over
- * live in a static device array of the library (32 MiB per device, held until
- * the process ends), enough for B * ceil(V/64) * 8 + ceil(B/16) * 8192 bytes
- * (e.g. B = 256 at V up to ~2M, B = 1024 at V = 129280).  Larger sizes return
+ * ws/ws_bytes: the draft's per-tile softmax partials, its A-row hand-over
+ * and (B > 256) the partials' per-slot aggregates live in a static device
+ * array of the library (32 MiB per device, held until the process ends),
+ * enough for B * ceil(V/64) * 8 + ceil(B/16) * 8192 (+ B * 2048 when
+ * B > 256) bytes (e.g. B = 256 at V up to ~1M, B = 1024 at V = 129280).  Larger sizes return
  * DSPARK_ERR_WORKSPACE with nothing enqueued.  The call allocates nothing
  * (no hipMalloc/hipFree, no allocating library call); its first call on a
  * device looks up that device's copy of the array.  All calls on one device

@@ -1,6 +1,6 @@
 """dspark_markov_draft_noalloc (the allocation-free draft entry point, whose
-tile partials and A-row hand-over live in the library's static device
-scratch) against dspark_markov_draft with a caller workspace: bit-identical
+tile partials, A-row hand-over and slot aggregates live in the library's
+static device scratch) against dspark_markov_draft with a caller workspace: bit-identical
 outputs on two calls in a row, the second with a smaller input, and the
 shape-ragged and headline cases; the first call on a fresh device looks the
 scratch up."""
@@ -38,6 +38,13 @@ def test_noalloc_two_calls_second_smaller():
 def test_noalloc_small_then_fp32_and_ragged_rank():
     _pair(synth.tiny(B=300, gamma=3, V=1000, r=24, budget=450, dtype="bf16"), 11)
     _pair(synth.tiny(B=5, gamma=3, V=777 * 8, r=16, budget=9, dtype="f32"), 12)
+
+
+def test_noalloc_two_row_blocks_rank256():
+    # B above one 256-row block at rank 256: the locate reads the tile launch's slot aggregates, which the
+    # static scratch holds after the A-row hand-over
+    _pair(synth.tiny(B=512, gamma=3, V=20000, r=256, budget=700, dtype="bf16"), 13)
+    _pair(synth.tiny(B=300, gamma=2, V=9000, r=256, budget=300, dtype="bf16"), 14)
 
 
 def test_noalloc_rejects_sizes_beyond_the_scratch():
