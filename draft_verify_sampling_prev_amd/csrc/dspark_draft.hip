@@ -798,9 +798,9 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     // Slot aggregates for the one-wave locate, where its workgroups share CUs
     // (B > 256): each then reads 2 KB of aggregates and one slot's tiles
     // instead of its row's 8 bytes per tile.  (Measured on MI355X at
-    // V = 129280: B = 1024, the locate 14.1 -> 11.5 us per launch; B = 256, one
-    // workgroup per CU, its waves end earlier but the launch, held by its
-    // slowest workgroups, does not, and the tile launch grows by 0.1-0.2 us.)
+    // V = 129280: B = 1024, the locate 14.3 -> 10.8 us per launch and the step
+    // 0.4-1.3% shorter; B = 256, one workgroup per CU, its waves end earlier
+    // but the launch, held by its slowest workgroups, does not.)
     // Such shapes never carry the schedule in a tile launch, so every tile
     // launch of a call has the same slots and the aggregates the same ranges.
     float2* sagg = wave_locate && B > kTileRows && St <= kSlotAggMax
