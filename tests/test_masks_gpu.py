@@ -9,8 +9,11 @@ verified draft is accepted), or no mask.  Masked tiles carry the partial
 (-inf, 0) and weigh nothing in the draft's two-level and one-level locates,
 the target normalisers, the residual and the bonus samples.  Every draft row
 and every request is checked, teacher-forced, as the other parity tests do.
-Cases: B = 300 (two 256-row blocks: the locate reads slot aggregates) and
-B = 64 at rank 256 (one row block, the one-level locate, the A-row hand-over).
+Cases: B = 300 (two 256-row blocks: the locate reads slot aggregates),
+B = 64 at rank 256 (one row block, the one-level locate, the A-row hand-over)
+and B = 512 at V = 129280 (full-batch launches that write their staged
+partials out every 12 tiles and fold the slot aggregates there; sampled rows
+and requests, every mask kind among them).
 """
 import numpy as np
 import pytest
@@ -59,6 +62,25 @@ def test_vocabulary_masks_match_the_oracle(B, gamma, V, r):
     assert np.allclose(out["p"][one], 1.0, rtol=0.0, atol=1e-6), out["p"][one]
     assert (out["acc"][one] == out["ell"][one]).mean() > 0.99
     rep = check_step(inp, out, wl.budget, wl.philox_seed, threads=check.default_threads())
+    print("  ", rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert check.flips_ok(rep), rep.summary()
+
+
+def test_vocabulary_masks_full_batch_sampled():
+    B, gamma, V, r = 512, 2, 129280, 256
+    wl = synth.tiny(B=B, gamma=gamma, V=V, r=r, budget=B * gamma // 2, dtype="bf16")
+    inp = synth.make_inputs(wl)
+    kinds = _mask(inp, V, seed=17)
+    print(f"case masks B={B} gamma={gamma} V={V} r={r} (sampled)", flush=True)
+    out = run_step(inp, wl.budget, wl.philox_seed)
+    structural_checks(out, gamma)
+    g = np.random.default_rng(23)
+    reqs = sorted(set(int(b) for b in g.integers(0, B, 24)) | {0, 1, 2, 3, B - 1})
+    rows = [(b, k) for b in reqs for k in range(1, gamma + 1)]
+    assert set(kinds[reqs]) == {0, 1, 2, 3}
+    rep = check_step(inp, out, wl.budget, wl.philox_seed, draft_rows=rows, requests=reqs,
+                     threads=check.default_threads())
     print("  ", rep.summary(), flush=True)
     assert rep.ok(), rep.summary()
     assert check.flips_ok(rep), rep.summary()
