@@ -10,8 +10,9 @@ verified draft is accepted), or no mask.  Masked tiles carry the partial
 the target normalisers, the residual and the bonus samples.  Every draft row
 and every request is checked, teacher-forced, as the other parity tests do.
 Cases: B = 300 (two 256-row blocks: the locate reads slot aggregates),
-B = 64 at rank 256 (one row block, the one-level locate, the A-row hand-over)
-and B = 512 at V = 129280 (full-batch launches that write their staged
+B = 64 at rank 256 (one row block, the one-level locate, the A-row hand-over),
+fp32 logits, a 270000-token vocabulary (more than 4096 tiles: the generic
+locate and final kernels) and B = 512 at V = 129280 (full-batch launches that write their staged
 partials out every 12 tiles and fold the slot aggregates there; sampled rows
 and requests, every mask kind among them).
 """
@@ -48,12 +49,13 @@ def _mask(inp, V: int, seed: int):
     return np.array(kinds)
 
 
-@pytest.mark.parametrize("B,gamma,V,r", [(300, 3, 24000, 64), (64, 4, 24000, 256)])
-def test_vocabulary_masks_match_the_oracle(B, gamma, V, r):
-    wl = synth.tiny(B=B, gamma=gamma, V=V, r=r, budget=B * gamma // 2, dtype="bf16")
+@pytest.mark.parametrize("B,gamma,V,r,dtype", [(300, 3, 24000, 64, "bf16"), (64, 4, 24000, 256, "bf16"),
+                                                (48, 3, 3000, 32, "f32"), (8, 2, 270000, 64, "bf16")])
+def test_vocabulary_masks_match_the_oracle(B, gamma, V, r, dtype):
+    wl = synth.tiny(B=B, gamma=gamma, V=V, r=r, budget=B * gamma // 2, dtype=dtype)
     inp = synth.make_inputs(wl)
     kinds = _mask(inp, V, seed=5 + B)
-    print(f"case masks B={B} gamma={gamma} V={V} r={r}", flush=True)
+    print(f"case masks B={B} gamma={gamma} V={V} r={r} {dtype}", flush=True)
     out = run_step(inp, wl.budget, wl.philox_seed)
     structural_checks(out, gamma)
     # the single-token requests draft that token with probability 1 (up to the rounding of the normaliser)
