@@ -182,16 +182,19 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_draft_tiles_bf16(
     // already written out, touched by thread t only.
     __shared__ float2 run_agg[MANY && SLOTS ? R : 1];
 
-    // A workgroup past the S * nM tile workgroups (launched only with the
-    // schedule, see launch_draft_step) runs the budget schedule.
-    if (blockIdx.x == S * nM) {
+    // With the schedule (one workgroup more than the S * nM tile workgroups,
+    // see launch_draft_step) workgroup 0 runs it: dispatched first, it ends
+    // early beside the tile workgroups, which take indices 1 .. S * nM.
+    // (Measured on MI355X: 1.0 us per step faster than the last index.)
+    const bool sched_wg = (int)gridDim.x > S * nM;  // uniform
+    if (sched_wg && blockIdx.x == 0) {
         budget_select<64 * NW>(sa.z, sa.temps, B, gamma, sa.admit, sa.surv, sa.len,
                                reinterpret_cast<uint32_t*>(s0 + kSchedKeysOffset),
                                *reinterpret_cast<SelectScratch<64 * NW>*>(s0));
         return;
     }
 
-    const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+    const int lid = xcd_logical_id(blockIdx.x - (sched_wg ? 1 : 0), gridDim.x - (sched_wg ? 1 : 0));
     const int mblk = lid % nM, slot = lid / nM;
     int t0, ts, cnt;
     slot_tiles(slot, S, nT, &t0, &ts, &cnt);
