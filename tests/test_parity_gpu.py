@@ -78,7 +78,8 @@ def test_full_row_blocks_all_residual_paths(B, budget, rej_lo, rej_hi):
     assert rej_lo <= n_rej <= rej_hi
 
 
-@pytest.mark.parametrize("B,gamma,budget", [(1, 1, 1), (1, 16, 7), (3, 16, 48), (17, 2, 0), (9, 4, 10**9)])
+@pytest.mark.parametrize("B,gamma,budget", [(1, 1, 1), (1, 16, 7), (3, 16, 48), (17, 2, 0), (9, 4, 10**9),
+                                            (257, 3, 400)])  # 257: a second row block of one row
 def test_edge_shapes_and_budgets(B, gamma, budget):
     wl = synth.tiny(B=B, gamma=gamma, V=256, r=8, budget=budget, dtype="bf16")
     out, _ = _run_and_check(wl)
