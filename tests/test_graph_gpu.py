@@ -11,8 +11,15 @@ from draft_verify_sampling_prev_amd import binding, synth
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager():
-    wl = synth.tiny(B=48, gamma=5, V=4096, r=64, budget=100, dtype="bf16")
+@pytest.mark.parametrize("shape,fused", [(dict(B=48, gamma=5, V=4096, r=64, budget=100), False),
+                                         (dict(B=48, gamma=5, V=4096, r=64, budget=100), True),
+                                         (dict(B=300, gamma=3, V=9000, r=256, budget=450), False)],
+                         ids=["B48", "B48-fused-schedule", "B300-two-level"])
+def test_graph_replays_match_eager(shape, fused):
+    """B = 300 at rank 256: the locate reads slot aggregates and hands over A rows; fused: the schedule runs
+    inside the draft call (dspark_markov_draft_sched)."""
+    wl = synth.tiny(**shape, dtype="bf16")
+    print(f"case graph {wl.describe()} fused={fused}", flush=True)
     inp = synth.make_inputs(wl)
     dev = torch.device("cuda:0")
     g = inp.to(dev)
@@ -29,8 +36,12 @@ def test_graph_replays_match_eager():
     tp = torch.empty((B, gamma), dtype=torch.float32, device=dev)
 
     def step(seed):
-        dsp.dspark_markov_draft(g.L, g.A, g.Bm, g.x0, seed, ws=ws, out=(tok, p, lse))
-        dsp.dspark_schedule(g.z, g.temps, wl.budget, survival=theta, out_len=ell)
+        if fused:
+            dsp.dspark_markov_draft_sched(g.L, g.A, g.Bm, g.x0, seed, g.z, g.temps, wl.budget, ws=ws,
+                                          out=(tok, p, lse), survival=theta, out_len=ell)
+        else:
+            dsp.dspark_markov_draft(g.L, g.A, g.Bm, g.x0, seed, ws=ws, out=(tok, p, lse))
+            dsp.dspark_schedule(g.z, g.temps, wl.budget, survival=theta, out_len=ell)
         dsp.dspark_verify(g.T, g.L, g.A, g.Bm, g.x0, tok, p, lse, ell, seed, ws=ws, out=(acc, out_tok, n_out, tp))
 
     def snap():
