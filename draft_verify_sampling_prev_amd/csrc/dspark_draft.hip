@@ -809,6 +809,8 @@ hipError_t launch_draft_step(int dtype, const void* L, const void* A, const void
     float2* sagg = wave_locate && B > kTileRows && St <= kSlotAggMax
                        ? reinterpret_cast<float2*>(static_cast<char*>(ws) + lay.slot_agg)
                        : nullptr;
+    // The locate finds the aggregates at ag + slot_agg_offset(B): every layout keeps them there.
+    if (sagg && lay.slot_agg != lay.ag + slot_agg_offset(B)) return hipErrorInvalidValue;
     if (dtype == 1) {
         const bool k8 = (r + 31) / 32 == 8, full = B % kTileRows == 0;
         auto kern = sagg ? (k8 ? (many ? k_draft_tiles_bf16<8, true, true, true>
