@@ -412,7 +412,19 @@ __device__ __forceinline__ int resid_item(int b, int G, int cpx)
     return p * 8 * cpx + x * n + (q - p * cpx);
 }
 
-template <int KS>
+// Byte offset of the draft's slot-aggregate rows from the residual tile sums
+// in the verify workspace (residual tile sums, bonus chunk maxima and sums,
+// the A-row hand-over, each rounded up to 256 bytes): B > 256 kernels reach
+// the per-slot residual sums there without a kernel argument (the launcher
+// checks the layout agrees).
+__host__ __device__ inline size_t rslot_offset(int B, int V)
+{
+    const size_t nT = (size_t)(V + kTcols - 1) / kTcols, nC = (size_t)(V + kChunkElems - 1) / kChunkElems;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return up((size_t)B * nT * 8) + up((size_t)B * nC * 4) + up((size_t)B * nC * 8) + up(ag_bytes(B));
+}
+
+template <int KS, bool SLOTS = false>
 __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
     const uint16_t* __restrict__ Tg, const uint16_t* __restrict__ L, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
@@ -635,6 +647,24 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_resid_tiles_bf16(
         if (m0 + row < cntr)
             for (int i = G; i < cnt; i += 4) rpart[(size_t)rowb[bb] * nT + t0 + i * ts] = unpack_f2(stage[i][row]);
     }
+    // SLOTS (B > 256): the request's sums over this slot's tiles, in tile
+    // order, for the final kernel's first level.
+    if (SLOTS && G == 0) {
+        float2* rslot = reinterpret_cast<float2*>(reinterpret_cast<char*>(rpart) + rslot_offset(B, V));
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int row = row_of(bb) + c;
+            if (m0 + row < cntr) {
+                float2 sum = make_float2(0.0f, 0.0f);
+                for (int i = 0; i < cnt; ++i) {
+                    const float2 v = unpack_f2(stage[i][row]);
+                    sum.x += v.x;
+                    sum.y += v.y;
+                }
+                rslot[(size_t)rowb[bb] * kSlotAggMax + slot] = sum;
+            }
+        }
+    }
     wait_all_mem();
 }
 
@@ -789,7 +819,10 @@ __global__ __launch_bounds__(kThreads) void k_final(
 // residual tile sums (the request's row of the residual partials) are read
 // in the residual branch only: issued in every workgroup they cost more than
 // the round trip they save (measured on MI355X, B = 256, V = 129280: 9.7
-// against 8.4 us per launch).
+// against 8.4 us per launch).  SLOTS (B > 256, at most 256 residual slots):
+// the request's per-slot sums are read instead (2 KB), then the chosen
+// slot's tile sums (measured on MI355X, B = 1024, V = 129280: 10.2-11.2
+// against 11.7-15.0 us per launch).
 // ---------------------------------------------------------------------------
 
 // Holds v in a register at this point, so the load that produced it is not
@@ -800,15 +833,19 @@ __device__ __forceinline__ void pin_reg(X& v)
     asm volatile("" : "+v"(v));
 }
 
-template <int KS, int PER>
+template <int KS, int PER, bool SLOTS = false>
 __global__ __launch_bounds__(64) void k_final_bf16(
     const uint16_t* __restrict__ Tg, const uint16_t* __restrict__ L, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ Bm, const int32_t* __restrict__ x0, const int32_t* __restrict__ tok,
     const double* __restrict__ lse_d, const double* __restrict__ lse_t, const int32_t* __restrict__ len,
     const int32_t* __restrict__ accepted, const float2* __restrict__ rpart, const float* __restrict__ bm,
-    const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rnn, SeedArg seed_arg,
+    const double* __restrict__ bsum, int gamma, int V, int r, int nT, int nC, int rmode, SeedArg seed_arg,
     int32_t* __restrict__ out_tok)
 {
+    // rmode: the RNN head flag; with SLOTS also the residual slot count
+    // (bits 1-9) and the batch size (bits 10 and up), which locate the
+    // per-slot residual sums without more kernel arguments.
+    const int rnn = SLOTS ? (rmode & 1) : rmode;
     const uint64_t seed = seed_of(seed_arg);
     __shared__ __attribute__((aligned(1024))) char lds[kBmTileBytes];
     const int b = blockIdx.x;
@@ -851,9 +888,20 @@ __global__ __launch_bounds__(64) void k_final_bf16(
     if (a < l) {
         // ---- residual at the first rejected position ks = a + 1 -----------
         const int ks = a + 1;
-        float2 q[PER];
-        int i0;
-        load_slices<PER>(rpart + (size_t)b * nT, nT, make_float2(0.0f, 0.0f), q, &i0);
+        // SLOTS (B > 256): the request's per-slot sums first (2 KB, Sr <= 256
+        // slots of contiguous tiles), then the chosen slot's tile sums, as the
+        // draft locate reads its slot aggregates; else the row's tile sums.
+        float2 q[SLOTS ? 1 : PER];
+        float2 qs[4];
+        int i0 = 0, i0s = 0;
+        const int Sr = (rmode >> 1) & 511;
+        if constexpr (SLOTS) {
+            const float2* rslot =
+                reinterpret_cast<const float2*>(reinterpret_cast<const char*>(rpart) + rslot_offset(rmode >> 10, V));
+            load_slices<4>(rslot + (size_t)b * kSlotAggMax, Sr, make_float2(0.0f, 0.0f), qs, &i0s);
+        } else {
+            load_slices<PER>(rpart + (size_t)b * nT, nT, make_float2(0.0f, 0.0f), q, &i0);
+        }
         uint4 af[1][8];
         {
             const int xr = rnn ? (int)row0 + a : clamp_tok(__shfl(xc, a, 64), V);
@@ -861,12 +909,37 @@ __global__ __launch_bounds__(64) void k_final_bf16(
             load_a_frags<1>(arow, r, af);
         }
         float sw = 0.0f;
+        if constexpr (SLOTS) {
 #pragma unroll
-        for (int j = 0; j < PER; ++j) sw += q[j].x;
+            for (int j = 0; j < 4; ++j) sw += qs[j].x;
+        } else {
+#pragma unroll
+            for (int j = 0; j < PER; ++j) sw += q[j].x;
+        }
         const bool degen = !(wave_last(wave_incl_scan((double)sw)) > 0.0);  // no residual mass: sample p_t
         const float u = philox_uniform(seed, (uint32_t)b, (uint32_t)ks, 2u);
-        const Located loc = wave_locate_slices<PER>(
-            i0, [&](int j) { return (double)(degen ? q[j].y : q[j].x); }, u, reinterpret_cast<double*>(lds));
+        Located loc;
+        if constexpr (SLOTS) {
+            const Located ls = wave_locate_slices<4>(
+                i0s, [&](int j) { return (double)(degen ? qs[j].y : qs[j].x); }, u, reinterpret_cast<double*>(lds));
+            // the chosen slot's tiles (at most 12), one per lane, from the mass
+            // before the slot; without a crossing, its last tile of positive mass
+            int t0, ts, cnt;
+            slot_tiles(ls.idx, Sr, nT, &t0, &ts, &cnt);
+            const float2 qt = rpart[(size_t)b * nT + t0 + min(lane, cnt - 1) * ts];
+            const double mm = lane < cnt ? (double)(degen ? qt.y : qt.x) : 0.0;
+            const double inc = wave_incl_scan(mm);
+            const uint64_t hit = __ballot(mm > 0.0 && ls.cprev + inc > ls.tau);
+            const uint64_t pos = __ballot(mm > 0.0);
+            const int sel = hit ? __builtin_ctzll(hit) : pos ? 63 - __builtin_clzll(pos) : 0;
+            loc.S = ls.S;
+            loc.tau = ls.tau;
+            loc.idx = t0 + sel * ts;
+            loc.cprev = ls.cprev + __shfl(inc - mm, sel, 64);
+        } else {
+            loc = wave_locate_slices<PER>(
+                i0, [&](int j) { return (double)(degen ? q[j].y : q[j].x); }, u, reinterpret_cast<double*>(lds));
+        }
 
         const int n0 = loc.idx * kTcols;
         const uint16_t* trow = Tg + ((size_t)b * (gamma + 1) + (ks - 1)) * V;
@@ -996,6 +1069,14 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     float* bm = reinterpret_cast<float*>(w + lay.bon_m);
     double* bsum = reinterpret_cast<double*>(w + lay.bon_s);
     const int nT = n_tiles(std::is_same<DT, Bf16>::value ? 1 : 0, V), nC = n_chunks(V);
+    // bf16: the residual pass's tile slots, and whether it also writes
+    // per-(request, slot) residual sums for the final kernel's two-level
+    // locate (B > 256, at most kSlotAggMax slots).  They go to the draft's
+    // slot-aggregate rows, which the draft call has finished reading, and
+    // both kernels find them at rslot_offset past the residual tile sums.
+    const int Sr = tile_slots(nT, (B + kTileRows - 1) / kTileRows, cu_count(), kResPartTiles);
+    const bool rslot = std::is_same<DT, Bf16>::value && B > kTileRows && B < (1 << 21) && Sr <= kSlotAggMax;
+    if (rslot && lay.slot_agg != lay.res_part + rslot_offset(B, V)) return hipErrorInvalidValue;
 
     launch_timed(K_TARGET_PARTIALS, k_row_partials<DT>, dim3(nC, B * gamma), dim3(kThreads), s, Tg, len, accepted,
                  gamma, V, nC, kRowTarget, tgm, tgs, rcnt);
@@ -1008,11 +1089,23 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
     launch_timed(K_ACCEPT, k_accept_bonus<DT>, dim3(nAcc + (bonus_in_accept ? nC * B : 0)), dim3(kThreads), s, Tg, pd,
                  len, x0, tok, tgm, tgs, B, gamma, V, nC, rnn, seed, accepted, n_out, target_p, lse_t, rlist, rcnt,
                  nAcc, bm, bsum);
+    // The bf16 residual-pass and final-token kernels.  The variants without
+    // per-slot sums are named first: the code object holds kernels in the
+    // order they are first named, and with the slot variants ahead of them
+    // the same machine code ran slower (measured on MI355X, B = 256, V =
+    // 129280: residual pass 30.9 against 30.4 us, final 8.3 against 8.2 us).
+    const bool k8 = (r + 31) / 32 == 8;
+    auto resid_kern = k8 ? k_resid_tiles_bf16<8> : k_resid_tiles_bf16<0>;
+    auto final_kern = nT <= 64 * 32 ? (k8 ? k_final_bf16<8, 32> : k_final_bf16<0, 32>)
+                                    : (k8 ? k_final_bf16<8, 64> : k_final_bf16<0, 64>);
+    if (rslot) {
+        resid_kern = k8 ? k_resid_tiles_bf16<8, true> : k_resid_tiles_bf16<0, true>;
+        final_kern = k8 ? k_final_bf16<8, 32, true> : k_final_bf16<0, 32, true>;
+    }
     if (std::is_same<DT, Bf16>::value) {
         const int nM = (B + kTileRows - 1) / kTileRows;
-        const int S = tile_slots(nT, nM, cu_count(), kResPartTiles);
-        auto kern = (r + 31) / 32 == 8 ? k_resid_tiles_bf16<8> : k_resid_tiles_bf16<0>;
-        launch_timed(K_RESID_TILES, kern, dim3(S * nM), dim3(64 * kTileWaves), s,
+        const int S = Sr;
+        launch_timed(K_RESID_TILES, resid_kern, dim3(S * nM), dim3(64 * kTileWaves), s,
                            reinterpret_cast<const uint16_t*>(Tg), reinterpret_cast<const uint16_t*>(L),
                            reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(Bm), x0, tok,
                            lse_d, lse_t, accepted, rlist, rcnt, B, gamma, V, r, nT, nM, S, nA, cu_count() / 8,
@@ -1028,13 +1121,10 @@ static hipError_t verify_t(const void* Tg_, const void* L_, const void* A_, cons
         launch_timed(K_BONUS_PARTIALS, k_row_partials<DT>, dim3(nC, B), dim3(kThreads), s, Tg, len, accepted, gamma, V,
                      nC, kRowBonusAccepted, bm, bsum, (int32_t*)nullptr);
     if (std::is_same<DT, Bf16>::value && nT <= 64 * 64 && nC <= 64 * 4) {
-        const bool k8 = (r + 31) / 32 == 8, small = nT <= 64 * 32;
-        auto kern = small ? (k8 ? k_final_bf16<8, 32> : k_final_bf16<0, 32>)
-                          : (k8 ? k_final_bf16<8, 64> : k_final_bf16<0, 64>);
-        launch_timed(K_FINAL, kern, dim3(B), dim3(64), s, reinterpret_cast<const uint16_t*>(Tg),
+        launch_timed(K_FINAL, final_kern, dim3(B), dim3(64), s, reinterpret_cast<const uint16_t*>(Tg),
                            reinterpret_cast<const uint16_t*>(L), reinterpret_cast<const uint16_t*>(A),
                            reinterpret_cast<const uint16_t*>(Bm), x0, tok, lse_d, lse_t, len, accepted, rpart, bm,
-                           bsum, gamma, V, r, nT, nC, rnn, seed, out_tok);
+                           bsum, gamma, V, r, nT, nC, rslot ? rnn | Sr << 1 | B << 10 : rnn, seed, out_tok);
     } else {
         launch_timed(K_FINAL, k_final<DT>, dim3(B), dim3(kThreads), s, Tg, L, A, Bm, x0, tok, lse_d, lse_t, len,
                            accepted, rpart, bm, bsum, gamma, V, r, nT, nC, rnn, seed, out_tok);

@@ -96,6 +96,20 @@ def test_many_vocab_chunks_and_row_blocks():
     _run_and_check(wl, draft_rows=rows, requests=range(0, 600, 7))
 
 
+def test_two_row_blocks_more_slots_than_slot_sums():
+    """B = 300, V = 240000 (3750 tiles): two row blocks with more than 256 tile slots each, so the draft locate
+    and the final kernel scan the tile sums in one level, as below B = 257 (with at most 256 slots they first
+    pick a slot from per-slot sums; the load-sweep, mask and B = 300 cases cover that)."""
+    import bench
+    wl = synth.tiny(B=300, gamma=3, V=240000, r=64, budget=450, dtype="bf16")
+    nT = (wl.V + 63) // 64
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert bench.tile_slots(nT, 2, cus, 12) > 256
+    rows = [(b, k) for b in range(0, 300, 13) for k in (1, 2, 3)]
+    out, _ = _run_and_check(wl, draft_rows=rows, requests=range(0, 300, 3))
+    assert (out["acc"] < out["ell"]).sum() > 50  # many residual samples
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_long_vocabulary_generic_paths(dtype):
     # V = 600000: 74 target chunks (> 64, the accept kernel's per-lane chunk loop)

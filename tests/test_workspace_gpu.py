@@ -2,8 +2,9 @@
 held before the call, through the C ABI.
 
 The verify's final kernel reads rows of the workspace that only one of its
-two branches fills (the residual tile sums of a request with a rejection, the
-bonus-row chunk partials of a request without one), and the draft's tile
+two branches fills (the residual tile sums of a request with a rejection, and
+at B = 300 its per-slot sums in the rows the draft's slot aggregates used;
+the bonus-row chunk partials of a request without one), and the draft's tile
 launches write and read the A-row hand-over and the tile partials there.  Each
 case runs the same step on workspaces filled with all-ones bytes (NaN and -1
 patterns), with zeros and with random bytes, and requires every output to be
